@@ -1,0 +1,254 @@
+"""Pins for the CPU oracle, against things other than the oracle itself.
+
+Each test fixes the oracle to an independent fact: a library routine
+(numpy fp64 matmul, Python's math.fsum, torch's bf16 decode), exact rational
+brute force, integer arithmetic, closed forms (identity, one-hot), the
+invariants that the pages' "exact algorithm" implies (any chunk order, chunked
+equals unchunked, the ring decomposition equals the collective), and hand
+worked values in tests/golden/.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import brute, ring
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+# ---- bf16 decode / encode -------------------------------------------------
+
+def test_bf16_decode_known_patterns(orc):
+    cases = {0x3F80: 1.0, 0xC000: -2.0, 0x0000: 0.0, 0x4049: 3.140625,
+             0x0080: 2.0 ** -126, 0x0001: 2.0 ** -133, 0x7F7F: (2 - 2 ** -7) * 2.0 ** 127,
+             0xBF40: -0.75, 0x3C00: 2.0 ** -7}
+    bits = np.array(list(cases), dtype=np.uint16)
+    got = orc.bf16_to_f64(bits)
+    assert list(got) == list(cases.values())
+
+
+def test_bf16_decode_all_finite_patterns_vs_torch_and_fraction(orc):
+    import torch
+    allb = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = allb[((allb >> 7) & 0xFF) != 0xFF]
+    t = torch.from_numpy(finite.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    sample = finite[:: 97]
+    got = orc.bf16_to_f64(sample)
+    assert np.array_equal(got, t[:: 97])
+    for b, g in zip(sample[:: 7], got[:: 7]):
+        assert brute.bf16_fraction(int(b)) == g
+
+
+def test_f64_to_bf16_rne_ties_and_library(orc):
+    # closed-form ties: 1 + 2^-8 lies half way between 1 and 1 + 2^-7
+    tie_cases = [(1.0 + 2 ** -8, 0x3F80),            # tie -> even (1.0)
+                 (1.0 + 3 * 2 ** -8, 0x3F82),        # tie -> even (1 + 2^-6)
+                 (1.0 + 2 ** -8 + 2 ** -40, 0x3F81),  # just above tie -> up
+                 (-(1.0 + 2 ** -8), 0xBF80),
+                 (2.0 ** -134, 0x0000),              # half the smallest subnormal -> 0
+                 (3 * 2.0 ** -134, 0x0002),          # 1.5 quanta -> 2
+                 (0.0, 0x0000), (-0.0, 0x8000)]
+    vals = np.array([v for v, _ in tie_cases], dtype=np.float64)
+    got = orc.f64_to_bf16(vals)
+    assert [int(g) for g in got] == [b for _, b in tie_cases]
+    # a value whose float32 rounding would create a false tie: one rounding only
+    v = 1.0 + 2 ** -8 + 2 ** -30     # rounds to 1+2^-8 in fp32, then to 1.0
+    assert int(orc.f64_to_bf16(np.array([v]))[0]) == 0x3F81
+    # against torch for values exactly representable in fp32 (single rounding)
+    import torch
+    x = rng(5).standard_normal(20000).astype(np.float32).astype(np.float64) * 37.0
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(orc.f64_to_bf16(x), ref)
+
+
+# ---- exact summation --------------------------------------------------------
+
+def _hard_sums(n_cases=400, seed=11):
+    g = rng(seed)
+    out = []
+    for _ in range(n_cases):
+        R = int(g.integers(1, 17))
+        e = g.integers(-60, 60, size=R)
+        v = g.standard_normal(R) * np.exp2(e)
+        if R > 2 and g.random() < 0.5:         # add catastrophic cancellation
+            v[-1] = -np.sum(v[:-1])
+        out.append(v)
+    # half-way cases for the final rounding
+    out.append(np.array([1.0, 2.0 ** -53, 2.0 ** -106]))
+    out.append(np.array([1.0, 2.0 ** -53, -(2.0 ** -106)]))
+    out.append(np.array([1.0, -(2.0 ** -54), 2.0 ** -107, 1e-300]))
+    out.append(np.array([1e308, 1e308 * 0.5, -1e308]))
+    return out
+
+
+def test_sum_exact_matches_math_fsum(orc):
+    for v in _hard_sums():
+        assert orc.sum_exact(v) == math.fsum(v)
+
+
+def test_sum_exact_matches_fraction(orc):
+    for v in _hard_sums(120, seed=12):
+        assert orc.sum_exact(v) == float(brute.sum_exact(v))
+
+
+def test_reduce_order_invariant_and_exact(orc):
+    g = rng(13)
+    for R in (1, 2, 3, 4):
+        srcs = [(g.standard_normal(257) * np.exp2(g.integers(-20, 20, 257))).astype(np.float32)
+                for _ in range(R)]
+        ref = orc.reduce(srcs)
+        for perm in itertools.permutations(range(R)):
+            assert np.array_equal(orc.reduce([srcs[p] for p in perm]), ref)
+        fs = np.array([math.fsum(float(s[e]) for s in srcs) for e in range(257)])
+        assert np.array_equal(ref, fs)
+
+
+def test_reduce_integer_equals_int64(orc):
+    c = wl.CFG4
+    srcs = wl.reduce_sources(c, "int", n=4096)
+    ref = np.sum(np.stack([s.astype(np.int64) for s in srcs]), axis=0)
+    assert np.array_equal(orc.reduce(srcs), ref.astype(np.float64))
+
+
+# ---- GEMM -------------------------------------------------------------------
+
+@pytest.mark.parametrize("m,n,k", [(37, 23, 19), (64, 48, 128), (5, 130, 33)])
+def test_gemm_vs_numpy(orc, m, n, k):
+    x = wl.bf16_operand((m, k), "gauss", 1.0, 101)
+    w = wl.bf16_operand((n, k), "gauss", 0.02, 102)
+    xf = orc.bf16_to_f64(x)
+    wf = orc.bf16_to_f64(w)
+    y = orc.gemm(x, w)
+    ref = xf @ wf.T
+    scale = np.abs(xf) @ np.abs(wf).T
+    assert np.all(np.abs(y - ref) <= 1e-12 * scale + 1e-300)
+    # a transposed operand would not even have this shape, and a wrong index
+    # would break the comparison
+    assert y.shape == (m, n)
+
+
+@pytest.mark.parametrize("mode", ["int", "gauss"])
+def test_gemm_vs_fraction_bruteforce(orc, mode):
+    for (m, n, k), seed in zip([(3, 4, 5), (7, 5, 16), (16, 9, 13)], (1, 2, 3)):
+        x = wl.bf16_operand((m, k), mode, 1.0, 200 + seed)
+        w = wl.bf16_operand((n, k), mode, 0.5, 300 + seed)
+        exact = brute.gemm(x, w)
+        y = orc.gemm(x, w)
+        if mode == "int":
+            assert np.array_equal(y, brute.to_float(exact))
+        else:
+            ex = brute.to_float(exact)
+            absx = np.abs(orc.bf16_to_f64(x)) @ np.abs(orc.bf16_to_f64(w)).T
+            assert np.all(np.abs(y - ex) <= k * 2.0 ** -53 * absx)
+
+
+def test_gemm_integer_equals_int64_cfg1(orc):
+    c = wl.CFG1
+    x, w = wl.gemm_inputs(c, "int")
+    xi = orc.bf16_to_f64(x).astype(np.int64)
+    wi = orc.bf16_to_f64(w).astype(np.int64)
+    ref = xi @ wi.T
+    assert np.array_equal(orc.gemm(x, w), ref.astype(np.float64))
+    assert np.abs(ref).max() <= 9 * c.k
+
+
+def test_gemm_identity_and_one_hot(orc):
+    k = 24
+    x = wl.bf16_operand((10, k), "gauss", 1.0, 401)
+    eye = wl.f32_to_bf16_bits(np.eye(k, dtype=np.float32))
+    assert np.array_equal(orc.gemm(x, eye), orc.bf16_to_f64(x))
+    w = wl.bf16_operand((7, k), "gauss", 1.0, 402)          # stored [n, k]
+    idx = [3, 0, 23, 11]
+    onehot = np.zeros((len(idx), k), dtype=np.float32)
+    onehot[np.arange(len(idx)), idx] = 1.0
+    y = orc.gemm(wl.f32_to_bf16_bits(onehot), w)
+    assert np.array_equal(y, orc.bf16_to_f64(w)[:, idx].T)
+
+
+def test_chunked_equals_unchunked_every_order(orc):
+    m, n, k = 48, 20, 36
+    x = wl.bf16_operand((m, k), "gauss", 1.0, 501)
+    w = wl.bf16_operand((n, k), "gauss", 0.02, 502)
+    full = orc.gemm(x, w)
+    for R in (1, 2, 3, 4):
+        for order in itertools.permutations(range(R)):
+            assert np.array_equal(orc.ag_gemm(x, w, R, list(order)), full)
+    g = rng(503)
+    for R in (8, 16):
+        for _ in range(8):
+            o = list(g.permutation(R))
+            assert np.array_equal(orc.ag_gemm(x, w, R, o), full)
+
+
+def test_gemm_rs_shard_vs_fraction_and_int64(orc):
+    m, n, k, R = 16, 6, 10, 4
+    for mode in ("int", "gauss"):
+        x = wl.bf16_operand((m, k), mode, 1.0, 601)
+        w = wl.bf16_operand((n, k), mode, 0.3, 602)
+        inc = [None if q == 1 else wl.f32_operand((m // R, n), mode, 0.7, 610 + q, 4096)
+               for q in range(R)]
+        s = orc.gemm_rs_shard(x, w, R, 1, inc)
+        P = brute.gemm(x, w)
+        mc = m // R
+        ex = [[P[mc + i][j] + sum((brute.f32_fraction(inc[q][i, j]) for q in range(R) if q != 1), 0)
+               for j in range(n)] for i in range(mc)]
+        assert np.array_equal(s, brute.to_float(ex))
+
+
+def test_ring_ag_equals_collective(orc):
+    R, mc, n, k = 4, 8, 12, 20
+    chunks = [wl.bf16_operand((mc, k), "int", 1.0, 700 + r) for r in range(R)]
+    ws = [wl.bf16_operand((n + r, k), "int", 1.0, 710 + r) for r in range(R)]
+    ys, done = ring.ring_ag(chunks, ws)
+    X = np.concatenate(chunks)
+    for r in range(R):
+        assert np.array_equal(ys[r], orc.gemm(X, ws[r]))
+        # local slice first, then received slices from predecessors
+        assert done[r] == [(r - s) % R for s in range(R)]
+
+
+@pytest.mark.parametrize("mode", ["int", "gauss"])
+def test_ring_rs_equals_collective(orc, mode):
+    R, m, n = 4, 16, 10
+    ks = [6, 9, 5, 12]
+    xs = [wl.bf16_operand((m, ks[r]), mode, 1.0, 800 + r) for r in range(R)]
+    ws = [wl.bf16_operand((n, ks[r]), mode, 0.5, 810 + r) for r in range(R)]
+    shards, done = ring.ring_rs(xs, ws)
+    mc = m // R
+    for r in range(R):
+        exact = [[sum((brute.gemm(xs[q][r * mc:(r + 1) * mc], ws[q])[i][j] for q in range(R)), 0)
+                  for j in range(n)] for i in range(mc)]
+        ex = brute.to_float(exact)
+        if mode == "int":
+            assert np.array_equal(shards[r], ex)
+        else:
+            assert np.allclose(shards[r], ex, rtol=1e-13, atol=1e-13)
+        assert done[r][-1] == r       # the local chunk is computed last
+
+
+def test_golden_worked_example(orc):
+    """Hand-worked 4x2 example (tests/golden/worked_example.txt)."""
+    vals = {}
+    with open(os.path.join(GOLDEN, "worked_example.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                key, rest = line.split("=")
+                vals[key.strip()] = np.array(eval(rest, {"__builtins__": {}}), dtype=np.float64)
+    x = wl.f32_to_bf16_bits(vals["X"].astype(np.float32))
+    w = wl.f32_to_bf16_bits(vals["W_stored"].astype(np.float32))
+    assert np.array_equal(orc.gemm(x, w), vals["Y"])
+    assert np.array_equal(orc.ag_gemm(x, w, 2, [1, 0]), vals["Y"])
+    inc = [None, vals["IN1"].astype(np.float32)]
+    assert np.array_equal(orc.gemm_rs_shard(x, w, 2, 0, inc), vals["SHARD0"])
+    srcs = [vals["SRC0"].astype(np.float32), vals["SRC1"].astype(np.float32),
+            vals["SRC2"].astype(np.float32)]
+    assert np.array_equal(orc.reduce(srcs), vals["SUM"])
