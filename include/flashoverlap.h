@@ -1,0 +1,194 @@
+/*
+ * flashoverlap.h - C ABI of the one-GPU FlashOverlap hot path for gfx950.
+ *
+ * FlashOverlap (arXiv 2604.24013) replaces the all-gather and reduce-scatter
+ * collectives of tensor/data parallel training with decomposed peer-to-peer
+ * pieces and schedules partitioned computation on those pieces so that no
+ * compute waits for the last piece (abstract; gist.science technical summary
+ * §2 "Methodology", Flash-AG and Flash-RS; euno.news "Methodology" steps 1-3).
+ * This library is one rank's share of that work on one MI355X:
+ *
+ *   fo_ag_gemm       Y = AllGather(X) * W, computed chunk by chunk as peer
+ *                    row-chunks of X land (Flash-AG).
+ *   fo_gemm_rs       the partial outputs P_c = X[rows of c] * W for every
+ *                    chunk c, peer-destined chunks first and the chunk that
+ *                    stays local last (Flash-RS, rank-adaptive partial output
+ *                    scheduling).
+ *   fo_chunk_reduce  dst = sum of R partial chunks, each peer chunk added once
+ *                    it has landed (the reduction inside reduce-scatter; DP
+ *                    needs reduce-scatter, technical summary §1).
+ *   fo_emulate_arrivals  enqueues the arrivals of emulated peers: SDMA copies
+ *                    from a staging region of the same HBM, each released at
+ *                    a programmable time and then flagged (the receive side of
+ *                    the decomposed collective).
+ *
+ * Conventions shared by every call
+ *  - Pointers named "device" are HIP device pointers on the current device;
+ *    "host" pointers are read during the call only.  The caller owns every
+ *    buffer, flag array, workspace and stream; the library keeps no pointer
+ *    after the enqueued work completes and allocates no device memory.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream);
+ *    calls return without synchronising.  Buffers must stay alive until the
+ *    stream work completes.
+ *  - Argument errors are reported synchronously and enqueue nothing.  Errors
+ *    found on the device (a flag wait that exceeds its bound) are written to
+ *    the optional device status word and the kernel exits cleanly.
+ *  - Matrices are row-major.  bf16 operands are IEEE binary32's upper halves.
+ *    W is the K x N weight stored as [n][k] (K contiguous, nn.Linear layout).
+ *  - Chunk c of an m-row operand is rows [c*m/R, (c+1)*m/R); m % R == 0.
+ *  - Epoch flags: chunk c counts as landed once (int32)(flag[c] - epoch) >= 0.
+ *    The caller passes a new, larger epoch on every call and never resets
+ *    flags.  Calls that share a workspace or flag array must not overlap.
+ */
+#ifndef FLASHOVERLAP_H
+#define FLASHOVERLAP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t fo_status;
+enum {
+  FO_OK = 0,
+  FO_ERR_NULL = 1,       /* a required pointer is NULL                        */
+  FO_ERR_SHAPE = 2,      /* non-positive size, m % R != 0, R out of range     */
+  FO_ERR_ALIGN = 3,      /* pointer not 16-byte aligned, or k % 8 != 0        */
+  FO_ERR_DTYPE = 4,      /* unknown dtype, or a dtype the call cannot store   */
+  FO_ERR_ORDER = 5,      /* order is not a permutation of 0..R-1              */
+  FO_ERR_SCHEDULE = 6,   /* local out of range, epoch == 0, bad mode/split    */
+  FO_ERR_WORKSPACE = 7,  /* workspace NULL or smaller than fo_workspace_bytes */
+  FO_ERR_HIP = 8,        /* a HIP runtime call failed (see fo_last_hip_error) */
+  FO_ERR_TIMEOUT = 9,    /* device-side: a flag wait exceeded timeout_ns      */
+  FO_ERR_ALIAS = 10      /* buffers overlap in a way the call does not allow  */
+};
+
+typedef int32_t fo_dtype;
+enum { FO_F32 = 0, FO_BF16 = 1 };
+
+/* Chunk claim policy (euno.news "Methodology" step 3: no sub-task waits for
+ * the last piece; technical summary §2: chunks that depend on incoming data
+ * first, the slice that stays local last). */
+enum {
+  FO_SCHED_READY_FIRST = 0, /* claim work from the first chunk in `order` that
+                               has landed and has work left                    */
+  FO_SCHED_STRICT = 1       /* take chunks exactly in `order`, waiting for each */
+};
+
+/* Largest supported number of chunks (emulated ranks). */
+#define FO_MAX_CHUNKS 64
+
+/* The chunk-order / arrival-schedule argument taken by every call. */
+typedef struct fo_schedule {
+  int32_t         nchunks;     /* R, 1 <= R <= FO_MAX_CHUNKS                    */
+  int32_t         local;       /* this rank's chunk, 0 <= local < R             */
+  const int32_t  *order;       /* host [R]: permutation of 0..R-1, the compute
+                                  priority.  NULL = default: peers in ring
+                                  arrival order local-1, local-2, ..., local+1,
+                                  then local last                               */
+  const uint32_t *arrived;     /* device [R] epoch flags; NULL = every chunk is
+                                  present.  arrived[local] is never read.  Used
+                                  by fo_ag_gemm and fo_chunk_reduce only.       */
+  uint32_t        epoch;       /* > 0; new and larger on every call             */
+  uint32_t        mode;        /* FO_SCHED_READY_FIRST or FO_SCHED_STRICT       */
+  uint64_t        timeout_ns;  /* bound on one flag wait; 0 = 10 s              */
+  int32_t        *status;      /* device [1], optional: receives FO_ERR_TIMEOUT */
+  uint64_t       *stamps;      /* device, optional wall-clock timeline (ticks of
+                                  the device wall clock, fo_wall_clock_hz):
+                                  GEMM calls: [2R+2] = per-chunk first claim,
+                                  per-chunk completion, kernel start, last
+                                  output written.  fo_chunk_reduce: [2] = first
+                                  workgroup start, completion (the caller zeroes
+                                  [1] before the call; it receives a maximum).  */
+  const int32_t  *split;       /* host [R], optional split-K factor per chunk
+                                  (1..8).  NULL = auto: 1 everywhere when
+                                  arrived == NULL, otherwise the last peer in
+                                  `order` (the chunk expected to land last) is
+                                  split so its tiles fill the GPU.             */
+  int32_t         max_workgroups; /* 0 = auto                                  */
+  int32_t         reserved;
+} fo_schedule;
+
+/* Workspace bytes that fo_ag_gemm / fo_gemm_rs need for an m x n x k problem
+ * in R chunks with the automatic split policy (or any split vector whose split
+ * chunks fit; the call checks).  The workspace must be zero-filled once before
+ * its first use; every call leaves it zeroed again when it completes. */
+size_t fo_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t nchunks);
+
+/* Chunked AG-GEMM (technical summary §2, Flash-AG; row/column-parallel
+ * projections for MLP and QKV).
+ *   x  device bf16 [m][k]: all R row-chunks.  Peer chunks are written by
+ *      the caller (or fo_emulate_arrivals) and flagged in s->arrived.
+ *   w  device bf16 [n][k] (the K x N weight, K contiguous).
+ *   y  device [m][n], y_dtype FO_F32 or FO_BF16 (round to nearest even);
+ *      y = x * W for every row, whatever the order or arrival times.
+ *   ws device workspace of ws_bytes >= fo_workspace_bytes(m, n, k, R).
+ * Each output tile is computed from bf16 MFMA products with fp32 accumulation
+ * in a fixed k order, so a given shape, split vector and input give the same
+ * bits on every run.  Errors: NULL, SHAPE, ALIGN, DTYPE, ORDER, SCHEDULE,
+ * WORKSPACE, ALIAS (y overlapping x or w), HIP. */
+fo_status fo_ag_gemm(const void *x, const void *w, void *y, fo_dtype y_dtype,
+                     int64_t m, int64_t n, int64_t k,
+                     const fo_schedule *s, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/* Chunked GEMM-RS (technical summary §2, Flash-RS).
+ *   x        device bf16 [m][k]; w device bf16 [n][k].
+ *   partial  device fp32 [m][n]: partial[rows of c] = x[rows of c] * W.
+ *   done     device [R] epoch flags, optional: done[c] = epoch is stored with
+ *            release semantics once chunk c is complete, so a copy engine or
+ *            a peer may send it on.
+ * Default order: peers in send order local-1, ..., local+1, then the local
+ * chunk last.  s->arrived must be NULL (the input rows are local).
+ * Errors as fo_ag_gemm. */
+fo_status fo_gemm_rs(const void *x, const void *w, float *partial, uint32_t *done,
+                     int64_t m, int64_t n, int64_t k,
+                     const fo_schedule *s, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/* Chunk reduce-add (technical summary §1 DP reduce-scatter, §2 Flash-RS).
+ *   srcs  host [R] array of device fp32 pointers, n elements each.
+ *   dst   device, n elements of dst_dtype (FO_F32 or FO_BF16).
+ * dst = srcs[local] + srcs[order'[0]] + srcs[order'[1]] + ... in fp32, added
+ * left to right, where order' is `order` without `local`.  With s->arrived,
+ * a source is read only after its flag shows the epoch; each pass adds the
+ * longest run of pending sources (in that order) that have all landed, so the
+ * bits never depend on arrival timing.
+ * Intermediate fp32 sums of a multi-pass reduce are kept in dst when dst is
+ * fp32 (dst may equal srcs[local]: in place) and in srcs[local] when dst is
+ * bf16 (srcs[local] is then overwritten).  n % 4 == 0 and 16-byte aligned
+ * pointers are required.  Errors: NULL, SHAPE, ALIGN, DTYPE, ORDER, SCHEDULE,
+ * ALIAS, HIP. */
+fo_status fo_chunk_reduce(void *dst, fo_dtype dst_dtype, const float *const *srcs,
+                          int64_t n, const fo_schedule *s, void *stream);
+
+/* Emulated peer arrivals on `stream` (a side stream, normally).  For each i in
+ * 0..count-1 in array order: wait until issue_ns[i] after the call's start
+ * t0, copy bytes[i] from src[i] to dst[i] on a DMA (SDMA) engine, wait until
+ * release_ns[i] after t0 and after the copy, then record the device wall clock
+ * in stamps[1 + chunk_id[i]] and store arrived[chunk_id[i]] = epoch with
+ * release semantics.  stamps[0] receives t0.
+ *   dst, src, bytes, issue_ns, release_ns, chunk_id: host arrays [count];
+ *   issue_ns may be NULL (each copy is issued at its release time).
+ *   arrived: device [R]; stamps: device [1 + max chunk id + 1], optional. */
+fo_status fo_emulate_arrivals(void *const *dst, const void *const *src,
+                              const size_t *bytes, const int64_t *issue_ns,
+                              const int64_t *release_ns, const int32_t *chunk_id,
+                              int32_t count, uint32_t *arrived, uint32_t epoch,
+                              uint64_t *stamps, void *stream);
+
+/* Device facts used to interpret stamps and size launches. */
+fo_status fo_device_info(int32_t *num_cus, int32_t *lds_bytes_per_cu,
+                         uint64_t *wall_clock_hz);
+
+const char *fo_status_string(fo_status st);
+
+/* Text of the last HIP error seen by the calling thread ("" if none). */
+const char *fo_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FLASHOVERLAP_H */

@@ -1,0 +1,382 @@
+// C ABI of the one-GPU FlashOverlap hot path: argument validation, schedule
+// expansion (default rank-adaptive order, split policy), launch sizing.
+// Declarations, argument meaning and error behaviour: include/flashoverlap.h.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <string.h>
+
+#include "fo_internal.hpp"
+
+namespace fo {
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr uint64_t kDefaultTimeoutNs = 10ull * 1000 * 1000 * 1000;
+constexpr int kMaxSplit = 8;
+
+struct DevInfo {
+  int cus = 0;
+  int lds = 0;
+  uint64_t wall_hz = 0;
+  hipError_t err = hipSuccess;
+};
+
+DevInfo g_dev[kMaxDevices];
+std::once_flag g_once[kMaxDevices];
+thread_local char g_hip_err[256] = "";
+
+void record(hipError_t e) {
+  const char *s = hipGetErrorString(e);
+  strncpy(g_hip_err, s ? s : "unknown HIP error", sizeof(g_hip_err) - 1);
+  g_hip_err[sizeof(g_hip_err) - 1] = 0;
+}
+
+const DevInfo *dev_info() {
+  int d = 0;
+  hipError_t e = hipGetDevice(&d);
+  if (e != hipSuccess) { record(e); return nullptr; }
+  if (d < 0 || d >= kMaxDevices) return nullptr;
+  std::call_once(g_once[d], [d]() {
+    DevInfo &I = g_dev[d];
+    int khz = 0;
+    I.err = hipDeviceGetAttribute(&I.cus, hipDeviceAttributeMultiprocessorCount, d);
+    if (I.err == hipSuccess)
+      I.err = hipDeviceGetAttribute(&I.lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, d);
+    if (I.err == hipSuccess) I.err = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, d);
+    I.wall_hz = (uint64_t)khz * 1000ull;
+  });
+  if (g_dev[d].err != hipSuccess) { record(g_dev[d].err); return nullptr; }
+  return &g_dev[d];
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+fo_status check_schedule(const fo_schedule *s) {
+  if (!s) return FO_ERR_NULL;
+  if (s->nchunks < 1 || s->nchunks > FO_MAX_CHUNKS) return FO_ERR_SHAPE;
+  if (s->local < 0 || s->local >= s->nchunks) return FO_ERR_SCHEDULE;
+  if (s->epoch == 0) return FO_ERR_SCHEDULE;
+  if (s->mode != FO_SCHED_READY_FIRST && s->mode != FO_SCHED_STRICT) return FO_ERR_SCHEDULE;
+  if (s->max_workgroups < 0) return FO_ERR_SCHEDULE;
+  if (s->order) {
+    uint64_t seen = 0;
+    for (int i = 0; i < s->nchunks; ++i) {
+      const int c = s->order[i];
+      if (c < 0 || c >= s->nchunks || (seen >> c) & 1ull) return FO_ERR_ORDER;
+      seen |= 1ull << c;
+    }
+  }
+  if (s->split)
+    for (int i = 0; i < s->nchunks; ++i)
+      if (s->split[i] < 1 || s->split[i] > kMaxSplit) return FO_ERR_SCHEDULE;
+  return FO_OK;
+}
+
+// Default priority: peers in ring arrival order local-1, local-2, ..., then local.
+void expand_order(const fo_schedule *s, int32_t *order) {
+  const int R = s->nchunks;
+  if (s->order) {
+    for (int i = 0; i < R; ++i) order[i] = s->order[i];
+    return;
+  }
+  for (int i = 1; i < R; ++i) order[i - 1] = ((s->local - i) % R + R) % R;
+  order[R - 1] = s->local;
+}
+
+uint64_t ns_to_ticks(uint64_t ns, uint64_t hz) {
+  const long double t = (long double)ns * (long double)hz / 1e9L;
+  return t > 1.8e19L ? ~0ull : (uint64_t)t;
+}
+
+struct GemmPlan {
+  TileCfg tile;
+  int64_t mc;
+  int tiles_m, tiles_n, tiles;
+  int kt_total;
+  size_t counter_bytes, partial_offset, partial_capacity_tiles, total_bytes;
+};
+
+GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, int R) {
+  GemmPlan p{};
+  p.mc = m / R;
+  p.tile = choose_tile(p.mc, n, k);
+  p.tiles_m = (int)((p.mc + p.tile.bm - 1) / p.tile.bm);
+  p.tiles_n = (int)((n + p.tile.bn - 1) / p.tile.bn);
+  p.tiles = p.tiles_m * p.tiles_n;
+  p.kt_total = (int)((k + 63) / 64);
+  p.counter_bytes = WS_HEADER_BYTES + (size_t)R * p.tiles * sizeof(uint32_t);
+  p.partial_offset = (p.counter_bytes + 255) & ~(size_t)255;
+  p.partial_capacity_tiles = (size_t)p.tiles * kMaxSplit;
+  p.total_bytes = p.partial_offset + p.partial_capacity_tiles * partial_slot_bytes(p.tile);
+  return p;
+}
+
+fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t *done,
+                   bool rs_mode, int64_t m, int64_t n, int64_t k, const fo_schedule *s,
+                   void *ws, size_t ws_bytes, void *stream) {
+  if (!x || !w || !y || !s) return FO_ERR_NULL;
+  fo_status st = check_schedule(s);
+  if (st != FO_OK) return st;
+  const int R = s->nchunks;
+  if (m <= 0 || n <= 0 || k <= 0 || m % R != 0) return FO_ERR_SHAPE;
+  if (m / R > (int64_t)1 << 30 || n > (int64_t)1 << 30) return FO_ERR_SHAPE;
+  if (k % 8 != 0 || !aligned16(x) || !aligned16(w)) return FO_ERR_ALIGN;
+  if (!aligned16(y) && !y_bf16) return FO_ERR_ALIGN;
+  if (rs_mode && s->arrived) return FO_ERR_SCHEDULE;
+  const size_t ybytes = (size_t)m * n * (y_bf16 ? 2 : 4);
+  if (overlaps(y, ybytes, x, (size_t)m * k * 2) || overlaps(y, ybytes, w, (size_t)n * k * 2))
+    return FO_ERR_ALIAS;
+  const GemmPlan p = plan_gemm(m, n, k, R);
+  if (!ws) return FO_ERR_WORKSPACE;
+  if (ws_bytes < p.counter_bytes || !aligned16(ws)) return FO_ERR_WORKSPACE;
+
+  const DevInfo *I = dev_info();
+  if (!I) return FO_ERR_HIP;
+
+  GemmArgs a{};
+  a.x = static_cast<const uint16_t *>(x);
+  a.w = static_cast<const uint16_t *>(w);
+  a.y = y;
+  a.y_bf16 = y_bf16 ? 1 : 0;
+  a.rs_mode = rs_mode ? 1 : 0;
+  a.m = m; a.n = n; a.k = k;
+  a.R = R;
+  a.mc = (int32_t)p.mc;
+  a.tiles_m = p.tiles_m;
+  a.tiles_n = p.tiles_n;
+  a.local = s->local;
+  a.strict = s->mode == FO_SCHED_STRICT ? 1 : 0;
+  a.arrived = s->arrived;
+  a.done_flags = done;
+  a.epoch = s->epoch;
+  a.timeout_ticks = ns_to_ticks(s->timeout_ns ? s->timeout_ns : kDefaultTimeoutNs, I->wall_hz);
+  a.status = s->status;
+  a.stamps = s->stamps;
+  a.ws32 = static_cast<uint32_t *>(ws);
+  a.partials = reinterpret_cast<float *>(static_cast<char *>(ws) + p.partial_offset);
+  expand_order(s, a.order);
+
+  // Workgroups: one per CU; with arrival flags leave one CU per XCD free for
+  // the emulator's timer and flag kernels on the side stream.
+  int occ = 1;
+  const int full = I->cus * occ;
+  int grid_cap = s->max_workgroups > 0 ? s->max_workgroups : full;
+  if (s->arrived && s->max_workgroups == 0) grid_cap = full > 16 ? full - 8 : full;
+
+  // Split policy.
+  int split[FO_MAX_CHUNKS];
+  for (int c = 0; c < R; ++c) split[c] = 1;
+  if (s->split) {
+    for (int c = 0; c < R; ++c) split[c] = s->split[c];
+  } else if (s->arrived && R > 1) {
+    // the last peer in priority order is the chunk expected to land last
+    int tail = -1;
+    for (int i = R - 1; i >= 0; --i)
+      if (a.order[i] != s->local) { tail = a.order[i]; break; }
+    int sk = (grid_cap + p.tiles - 1) / p.tiles;
+    if (sk > kMaxSplit) sk = kMaxSplit;
+    if (sk > p.kt_total) sk = p.kt_total;
+    if (sk < 1) sk = 1;
+    if (tail >= 0) split[tail] = sk;
+  }
+  int64_t total_units = 0;
+  size_t ctr_used = 0, part_used = 0;
+  for (int c = 0; c < R; ++c) {
+    int sk = split[c];
+    if (sk > p.kt_total) sk = p.kt_total;
+    int kt_per = (p.kt_total + sk - 1) / sk;
+    // every split must own at least one k stage
+    while (sk > 1 && (int64_t)(sk - 1) * kt_per >= p.kt_total) {
+      --sk;
+      kt_per = (p.kt_total + sk - 1) / sk;
+    }
+    a.split[c] = sk;
+    a.kslice[c] = kt_per * 64;
+    a.units[c] = p.tiles * sk;
+    if (sk > 1) {
+      a.ctr_base[c] = (int32_t)ctr_used;
+      a.part_base[c] = (int32_t)part_used;
+      ctr_used += (size_t)p.tiles;
+      part_used += (size_t)p.tiles * sk;
+    } else {
+      a.ctr_base[c] = -1;
+      a.part_base[c] = -1;
+    }
+    total_units += a.units[c];
+  }
+  if (part_used > 0 && ws_bytes < p.partial_offset + part_used * partial_slot_bytes(p.tile))
+    return FO_ERR_WORKSPACE;
+  if (total_units > (int64_t)1 << 30) return FO_ERR_SHAPE;
+  a.total_units = (int32_t)total_units;
+  a.grid = (int32_t)(total_units < grid_cap ? total_units : grid_cap);
+  if (a.grid < 1) a.grid = 1;
+
+  hipError_t e = launch_gemm(a, p.tile, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) { record(e); return FO_ERR_HIP; }
+  return FO_OK;
+}
+
+}  // namespace
+
+int device_num_cus() {
+  const DevInfo *I = dev_info();
+  return I ? I->cus : 0;
+}
+
+uint64_t device_wall_hz() {
+  const DevInfo *I = dev_info();
+  return I ? I->wall_hz : 0;
+}
+
+}  // namespace fo
+
+using namespace fo;
+
+extern "C" {
+
+size_t fo_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t nchunks) {
+  if (m <= 0 || n <= 0 || k <= 0 || nchunks < 1 || nchunks > FO_MAX_CHUNKS || m % nchunks) return 0;
+  return plan_gemm(m, n, k, nchunks).total_bytes;
+}
+
+fo_status fo_ag_gemm(const void *x, const void *w, void *y, fo_dtype y_dtype, int64_t m, int64_t n,
+                     int64_t k, const fo_schedule *s, void *ws, size_t ws_bytes, void *stream) {
+  if (y_dtype != FO_F32 && y_dtype != FO_BF16) return FO_ERR_DTYPE;
+  return run_gemm(x, w, y, y_dtype == FO_BF16, nullptr, false, m, n, k, s, ws, ws_bytes, stream);
+}
+
+fo_status fo_gemm_rs(const void *x, const void *w, float *partial, uint32_t *done, int64_t m,
+                     int64_t n, int64_t k, const fo_schedule *s, void *ws, size_t ws_bytes,
+                     void *stream) {
+  return run_gemm(x, w, partial, false, done, true, m, n, k, s, ws, ws_bytes, stream);
+}
+
+fo_status fo_chunk_reduce(void *dst, fo_dtype dst_dtype, const float *const *srcs, int64_t n,
+                          const fo_schedule *s, void *stream) {
+  if (!dst || !srcs || !s) return FO_ERR_NULL;
+  fo_status st = check_schedule(s);
+  if (st != FO_OK) return st;
+  if (dst_dtype != FO_F32 && dst_dtype != FO_BF16) return FO_ERR_DTYPE;
+  const int R = s->nchunks;
+  if (n <= 0) return FO_ERR_SHAPE;
+  if (n % 4 != 0) return FO_ERR_ALIGN;
+  for (int i = 0; i < R; ++i) {
+    if (!srcs[i]) return FO_ERR_NULL;
+    if (!aligned16(srcs[i])) return FO_ERR_ALIGN;
+  }
+  if (!aligned16(dst)) return FO_ERR_ALIGN;
+  const size_t nb = (size_t)n * 4, db = (size_t)n * (dst_dtype == FO_BF16 ? 2 : 4);
+  // dst may equal srcs[local] exactly (fp32, in place); any other overlap is refused
+  for (int i = 0; i < R; ++i) {
+    if (dst_dtype == FO_F32 && i == s->local && dst == (const void *)srcs[i]) continue;
+    if (overlaps(dst, db, srcs[i], nb)) return FO_ERR_ALIAS;
+  }
+  for (int i = 0; i < R; ++i)
+    for (int j = i + 1; j < R; ++j)
+      if (overlaps(srcs[i], nb, srcs[j], nb)) return FO_ERR_ALIAS;
+
+  const DevInfo *I = dev_info();
+  if (!I) return FO_ERR_HIP;
+
+  int32_t order[FO_MAX_CHUNKS];
+  expand_order(s, order);
+  ReduceArgs a{};
+  int q = 0;
+  a.src[q] = srcs[s->local];
+  a.chunk_of[q++] = s->local;
+  for (int i = 0; i < R; ++i) {
+    if (order[i] == s->local) continue;
+    a.src[q] = srcs[order[i]];
+    a.chunk_of[q++] = order[i];
+  }
+  a.dst = dst;
+  a.dst_bf16 = dst_dtype == FO_BF16 ? 1 : 0;
+  a.acc = dst_dtype == FO_F32 ? static_cast<float *>(dst) : const_cast<float *>(srcs[s->local]);
+  a.R = R;
+  a.n4 = n / 4;
+  a.arrived = s->arrived;
+  a.epoch = s->epoch;
+  a.timeout_ticks = ns_to_ticks(s->timeout_ns ? s->timeout_ns : kDefaultTimeoutNs, I->wall_hz);
+  a.status = s->status;
+  a.stamps = s->stamps;
+
+  // 4 workgroups of 256 threads per CU keeps enough bytes in flight; with
+  // arrival flags, wave slots stay free for the emulator's one-wave kernels.
+  int grid = s->max_workgroups > 0 ? s->max_workgroups : I->cus * 4;
+  const int64_t min_per = 256 * 4;   // one full step of the workgroup
+  int64_t per = (a.n4 + grid - 1) / grid;
+  if (per < min_per) per = min_per;
+  per = (per + 255) / 256 * 256;
+  a.per_wg4 = per;
+  grid = (int)((a.n4 + per - 1) / per);
+  hipError_t e = launch_reduce(a, grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) { record(e); return FO_ERR_HIP; }
+  return FO_OK;
+}
+
+fo_status fo_emulate_arrivals(void *const *dst, const void *const *src, const size_t *bytes,
+                              const int64_t *issue_ns, const int64_t *release_ns,
+                              const int32_t *chunk_id, int32_t count, uint32_t *arrived,
+                              uint32_t epoch, uint64_t *stamps, void *stream) {
+  if (count < 0) return FO_ERR_SHAPE;
+  if (count == 0) return FO_OK;
+  if (!dst || !src || !bytes || !release_ns || !chunk_id || !arrived || !stamps) return FO_ERR_NULL;
+  if (epoch == 0) return FO_ERR_SCHEDULE;
+  for (int i = 0; i < count; ++i) {
+    if (chunk_id[i] < 0 || chunk_id[i] >= FO_MAX_CHUNKS) return FO_ERR_SCHEDULE;
+    if (release_ns[i] < 0 || (issue_ns && (issue_ns[i] < 0 || issue_ns[i] > release_ns[i])))
+      return FO_ERR_SCHEDULE;
+    if (bytes[i] && (!dst[i] || !src[i])) return FO_ERR_NULL;
+  }
+  const DevInfo *I = dev_info();
+  if (!I) return FO_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  auto issue_at = [&](int i) -> uint64_t { return (uint64_t)(issue_ns ? issue_ns[i] : release_ns[i]); };
+  hipError_t e = launch_emu_start(stamps, ns_to_ticks(issue_at(0), I->wall_hz), st);
+  for (int i = 0; i < count && e == hipSuccess; ++i) {
+    if (bytes[i]) e = hipMemcpyAsync(dst[i], src[i], bytes[i], hipMemcpyDeviceToDeviceNoCU, st);
+    if (e != hipSuccess) break;
+    const uint64_t next = (i + 1 < count) ? ns_to_ticks(issue_at(i + 1), I->wall_hz) : 0;
+    e = launch_emu_flag(stamps, ns_to_ticks((uint64_t)release_ns[i], I->wall_hz), next,
+                        arrived + chunk_id[i], epoch, stamps + 1 + chunk_id[i], st);
+  }
+  if (e != hipSuccess) { record(e); return FO_ERR_HIP; }
+  return FO_OK;
+}
+
+fo_status fo_device_info(int32_t *num_cus, int32_t *lds_bytes_per_cu, uint64_t *wall_clock_hz) {
+  const DevInfo *I = dev_info();
+  if (!I) return FO_ERR_HIP;
+  if (num_cus) *num_cus = I->cus;
+  if (lds_bytes_per_cu) *lds_bytes_per_cu = I->lds;
+  if (wall_clock_hz) *wall_clock_hz = I->wall_hz;
+  return FO_OK;
+}
+
+const char *fo_status_string(fo_status st) {
+  switch (st) {
+    case FO_OK: return "ok";
+    case FO_ERR_NULL: return "a required pointer is NULL";
+    case FO_ERR_SHAPE: return "invalid shape (non-positive size, m % R != 0 or R out of range)";
+    case FO_ERR_ALIGN: return "pointer not 16-byte aligned or k/n not a multiple of the vector width";
+    case FO_ERR_DTYPE: return "unsupported dtype";
+    case FO_ERR_ORDER: return "order is not a permutation of 0..R-1";
+    case FO_ERR_SCHEDULE: return "invalid schedule (local, epoch, mode, split or arrival times)";
+    case FO_ERR_WORKSPACE: return "workspace missing or too small";
+    case FO_ERR_HIP: return "HIP runtime error";
+    case FO_ERR_TIMEOUT: return "a flag wait exceeded the timeout";
+    case FO_ERR_ALIAS: return "buffers overlap";
+    default: return "unknown status";
+  }
+}
+
+const char *fo_last_hip_error(void) { return g_hip_err; }
+
+}  // extern "C"

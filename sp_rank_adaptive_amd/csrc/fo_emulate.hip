@@ -1,0 +1,50 @@
+// Peer emulator kernels: one-wave timers that release emulated peer chunks.
+//
+// The decomposed collective's receive side (FlashOverlap abstract and
+// euno.news "Methodology" step 1: the collective becomes directed
+// peer-to-peer messages) is emulated on one GPU: each peer chunk is a copy
+// from a staging region of the same HBM on a DMA engine, enqueued between these
+// kernels on a side stream.  A timer kernel holds the stream until the copy's
+// issue time; a flag kernel waits for the chunk's release time, records the
+// device wall clock and stores the chunk's epoch flag with release semantics.
+// Each kernel is a single wave that sleeps between clock reads.
+#include "fo_device.hpp"
+#include "fo_internal.hpp"
+
+namespace fo {
+
+__device__ __forceinline__ void sleep_until(uint64_t t0, uint64_t offset) {
+  while (now_ticks() - t0 < offset) __builtin_amdgcn_s_sleep(16);
+}
+
+__global__ void __launch_bounds__(64) emu_start_kernel(uint64_t *t0_slot, uint64_t wait_ticks) {
+  if (threadIdx.x != 0) return;
+  const uint64_t t0 = now_ticks();
+  store_u64_relaxed(t0_slot, t0);
+  sleep_until(t0, wait_ticks);
+}
+
+__global__ void __launch_bounds__(64) emu_flag_kernel(const uint64_t *t0_slot, uint64_t release_ticks,
+                                                      uint64_t next_issue_ticks, uint32_t *flag,
+                                                      uint32_t epoch, uint64_t *stamp_slot) {
+  if (threadIdx.x != 0) return;
+  const uint64_t t0 = __hip_atomic_load(t0_slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  sleep_until(t0, release_ticks);
+  if (stamp_slot) store_u64_relaxed(stamp_slot, now_ticks());
+  store_release(flag, epoch);
+  sleep_until(t0, next_issue_ticks);
+}
+
+hipError_t launch_emu_start(uint64_t *t0_slot, uint64_t wait_ticks, hipStream_t s) {
+  hipLaunchKernelGGL(emu_start_kernel, dim3(1), dim3(64), 0, s, t0_slot, wait_ticks);
+  return hipGetLastError();
+}
+
+hipError_t launch_emu_flag(const uint64_t *t0_slot, uint64_t release_ticks, uint64_t next_issue_ticks,
+                           uint32_t *flag, uint32_t epoch, uint64_t *stamp_slot, hipStream_t s) {
+  hipLaunchKernelGGL(emu_flag_kernel, dim3(1), dim3(64), 0, s, t0_slot, release_ticks, next_issue_ticks,
+                     flag, epoch, stamp_slot);
+  return hipGetLastError();
+}
+
+}  // namespace fo

@@ -1,0 +1,88 @@
+// Internal launch interface between the C ABI (fo_api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/flashoverlap.h"
+
+namespace fo {
+
+// Workspace layout (32-bit words from the start of the workspace).  Every
+// counter is returned to zero by the kernel that observes its final value, so
+// the workspace is zero again after each completed call.
+constexpr int WS_CLAIM = 0;                  // [FO_MAX_CHUNKS] unit claim counters
+constexpr int WS_CHUNK_DONE = 64;            // [FO_MAX_CHUNKS] finished units per chunk
+constexpr int WS_TOTAL_DONE = 128;           // finished units, all chunks
+constexpr int WS_EXITED = 129;               // workgroups that have left the loop
+constexpr int WS_ABORT = 130;                // set when a wait timed out
+constexpr int WS_TILE_CTR = 256;             // split-K arrival counters, one per tile
+constexpr size_t WS_HEADER_BYTES = 1024;     // bytes before the tile counters
+
+// Output tile of one workgroup and k depth of one LDS stage.
+struct TileCfg {
+  int bm, bn;
+};
+
+struct GemmArgs {
+  const uint16_t *x;          // bf16 [m][k]
+  const uint16_t *w;          // bf16 [n][k]
+  void *y;                    // [m][n] fp32 or bf16
+  int32_t y_bf16;
+  int32_t rs_mode;            // 1: GEMM-RS (done flags), 0: AG-GEMM
+  int64_t m, n, k;
+  int32_t R, mc;              // chunks, rows per chunk
+  int32_t tiles_m, tiles_n;   // tiles per chunk
+  int32_t local;
+  int32_t strict;
+  int32_t total_units;
+  int32_t grid;
+  const uint32_t *arrived;    // device [R] or null
+  uint32_t *done_flags;       // device [R] or null
+  uint32_t epoch;
+  uint64_t timeout_ticks;
+  int32_t *status;
+  uint64_t *stamps;
+  uint32_t *ws32;             // counters
+  float *partials;            // split-K partial tiles
+  int32_t order[FO_MAX_CHUNKS];
+  int32_t split[FO_MAX_CHUNKS];
+  int32_t units[FO_MAX_CHUNKS];     // tiles * split
+  int32_t ctr_base[FO_MAX_CHUNKS];  // split chunk: first tile counter; -1 if unsplit
+  int32_t part_base[FO_MAX_CHUNKS]; // split chunk: first partial tile (tile*S + split)
+  int32_t kslice[FO_MAX_CHUNKS];    // k extent of one split (multiple of 64)
+};
+
+struct ReduceArgs {
+  const float *src[FO_MAX_CHUNKS];  // in summation sequence: seq[0] = local
+  int32_t chunk_of[FO_MAX_CHUNKS];  // chunk id of seq[i] (for the flags)
+  void *dst;
+  float *acc;                       // fp32 running sum between passes
+  int32_t dst_bf16;
+  int32_t R;
+  int64_t n4;                       // number of float4 vectors
+  int64_t per_wg4;                  // float4 vectors owned by one workgroup
+  const uint32_t *arrived;
+  uint32_t epoch;
+  uint64_t timeout_ticks;
+  int32_t *status;
+  uint64_t *stamps;
+};
+
+// Tile configuration chosen for a problem (host).
+TileCfg choose_tile(int64_t mc, int64_t n, int64_t k);
+size_t partial_slot_bytes(const TileCfg &t);
+
+hipError_t launch_gemm(const GemmArgs &a, const TileCfg &t, hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs &a, int grid, hipStream_t stream);
+
+// Emulator kernels.
+hipError_t launch_emu_start(uint64_t *t0_slot, uint64_t wait_ticks, hipStream_t s);
+hipError_t launch_emu_flag(const uint64_t *t0_slot, uint64_t release_ticks,
+                           uint64_t next_issue_ticks, uint32_t *flag, uint32_t epoch,
+                           uint64_t *stamp_slot, hipStream_t s);
+
+int device_num_cus();
+uint64_t device_wall_hz();
+
+}  // namespace fo

@@ -1,0 +1,118 @@
+// Chunk reduce-add for gfx950: dst = src[seq 0] + src[seq 1] + ... (fp32),
+// each peer source read only after its epoch flag shows it landed.
+//
+// The reduction inside the decomposed reduce-scatter (gist.science technical
+// summary §1: data parallelism needs reduce-scatter; §2: Flash-RS sums the
+// partial outputs into the slice that stays local).  HBM-bound: each workgroup
+// owns a contiguous range of 16-byte vectors and streams it with coalesced
+// 16-byte loads per lane; no workgroup waits for another, so there is no grid
+// barrier.  A pass adds the longest run of pending sources (in summation
+// order) that have all landed; the per-element addition order is therefore
+// fixed by the order argument alone, never by arrival timing.
+#include "fo_device.hpp"
+#include "fo_internal.hpp"
+
+namespace fo {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int RT = 256;  // threads per workgroup
+constexpr int RU = 4;    // vectors per thread per step (loads in flight)
+
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(RT) reduce_kernel(ReduceArgs a) {
+  __shared__ int s_avail;
+  const int tid = threadIdx.x;
+  const int64_t beg = (int64_t)blockIdx.x * a.per_wg4;
+  const int64_t end = (beg + a.per_wg4 < a.n4) ? beg + a.per_wg4 : a.n4;
+  if (blockIdx.x == 0 && tid == 0 && a.stamps) store_u64_relaxed(a.stamps, now_ticks());
+  if (beg >= end) return;
+
+  int added = 0;
+  while (added < a.R) {
+    if (tid == 0) {
+      int av = added;
+      uint64_t wait_from = 0;
+      for (;;) {
+        av = added;
+        while (av < a.R && (av == 0 || a.arrived == nullptr ||
+                            epoch_reached(load_relaxed(a.arrived + a.chunk_of[av]), a.epoch)))
+          ++av;
+        if (av > added) {
+          if (a.arrived) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+          break;
+        }
+        const uint64_t t = now_ticks();
+        if (wait_from == 0) wait_from = t;
+        if (t - wait_from > a.timeout_ticks) {
+          if (a.status) __hip_atomic_store(a.status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_SYSTEM);
+          av = -1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+      s_avail = av;
+    }
+    __syncthreads();
+    const int av = s_avail;
+    __syncthreads();
+    if (av < 0) return;
+    const bool last = (av == a.R);
+    const int first_src = (added == 0) ? 1 : added;
+
+    for (int64_t base = beg + tid; base < end; base += (int64_t)RT * RU) {
+      f32x4 v[RU];
+#pragma unroll
+      for (int q = 0; q < RU; ++q) {
+        const int64_t i = base + (int64_t)q * RT;
+        if (i < end)
+          v[q] = (added == 0) ? reinterpret_cast<const f32x4 *>(a.src[0])[i]
+                              : reinterpret_cast<const f32x4 *>(a.acc)[i];
+      }
+      for (int s = first_src; s < av; ++s) {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(a.src[s]);
+        f32x4 t[RU];
+#pragma unroll
+        for (int q = 0; q < RU; ++q) {
+          const int64_t i = base + (int64_t)q * RT;
+          if (i < end) t[q] = p[i];
+        }
+#pragma unroll
+        for (int q = 0; q < RU; ++q) v[q] += t[q];
+      }
+#pragma unroll
+      for (int q = 0; q < RU; ++q) {
+        const int64_t i = base + (int64_t)q * RT;
+        if (i >= end) continue;
+        if (last && OUT_BF16) {
+          const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[q][0]) | ((uint32_t)f32_to_bf16_rne(v[q][1]) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16_rne(v[q][2]) | ((uint32_t)f32_to_bf16_rne(v[q][3]) << 16);
+          reinterpret_cast<u32x2 *>(a.dst)[i] = u32x2{lo, hi};
+        } else if (last) {
+          reinterpret_cast<f32x4 *>(a.dst)[i] = v[q];
+        } else {
+          reinterpret_cast<f32x4 *>(a.acc)[i] = v[q];
+        }
+      }
+    }
+    added = av;
+  }
+
+  if (a.stamps) {
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_fetch_max(a.stamps + 1, now_ticks(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+hipError_t launch_reduce(const ReduceArgs &a, int grid, hipStream_t stream) {
+  if (a.dst_bf16)
+    hipLaunchKernelGGL(reduce_kernel<true>, dim3(grid), dim3(RT), 0, stream, a);
+  else
+    hipLaunchKernelGGL(reduce_kernel<false>, dim3(grid), dim3(RT), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace fo

@@ -1,0 +1,178 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, the ctypes struct matches the C layout, and argument
+validation rejects bad calls before any HIP call is made."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import sp_rank_adaptive_amd as fo
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flashoverlap.h")
+
+A = 0x10000          # an aligned fake device address (never dereferenced)
+A2 = 0x20000000
+WS = 0x40000000
+
+
+@pytest.fixture(scope="module")
+def L():
+    return fo.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:fo_status|size_t|const char \*)\s*(fo_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert set(names) == set(fo.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", fo.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(fo_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(L, n)
+
+
+def test_schedule_struct_layout_matches_header():
+    src = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "flashoverlap.h"
+int main(void){
+  printf("%zu", sizeof(fo_schedule));
+#define O(f) printf(" %zu", offsetof(fo_schedule, f));
+  O(nchunks) O(local) O(order) O(arrived) O(epoch) O(mode) O(timeout_ns) O(status)
+  O(stamps) O(split) O(max_workgroups) O(reserved)
+  printf("\n"); return 0; }
+"""
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        exe = os.path.join(d, "t")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        vals = [int(v) for v in subprocess.run([exe], capture_output=True, text=True,
+                                               check=True).stdout.split()]
+    S = fo._Sched
+    py = [ctypes.sizeof(S)] + [getattr(S, f).offset for f, _ in S._fields_]
+    assert vals == py
+
+
+def test_status_strings(L):
+    for code in range(0, 11):
+        s = fo.fo_status_string(code)
+        assert s and s != "unknown status"
+    assert fo.fo_status_string(99) == "unknown status"
+
+
+def test_workspace_bytes(L):
+    assert fo.fo_workspace_bytes(4096, 1792, 4096, 8) > 1024
+    assert fo.fo_workspace_bytes(4096, 1792, 4096, 7) == 0      # m % R != 0
+    assert fo.fo_workspace_bytes(0, 1, 8, 1) == 0
+    assert fo.fo_workspace_bytes(64, 64, 64, 65) == 0            # R > max
+
+
+def sched(R=4, **kw):
+    s = fo.Schedule(nchunks=R, **kw)
+    c, keep = s._c()
+    return c, keep
+
+
+def ag(L, x=A, w=A, y=A2, dt=fo.FO_F32, m=256, n=512, k=512, s=None, ws=WS, wsb=1 << 30):
+    if s is None:
+        s, keep = sched()
+    return L.fo_ag_gemm(x, w, y, dt, m, n, k, ctypes.byref(s) if s is not False else None,
+                        ws, wsb, None)
+
+
+def test_ag_gemm_validation(L):
+    assert ag(L, x=None) == fo.FO_ERR_NULL
+    assert ag(L, s=False) == fo.FO_ERR_NULL
+    assert ag(L, dt=7) == fo.FO_ERR_DTYPE
+    assert ag(L, m=255) == fo.FO_ERR_SHAPE                  # m % R
+    assert ag(L, n=0) == fo.FO_ERR_SHAPE
+    assert ag(L, k=12) == fo.FO_ERR_ALIGN                   # k % 8
+    assert ag(L, x=A + 8) == fo.FO_ERR_ALIGN
+    assert ag(L, y=A) == fo.FO_ERR_ALIAS                    # y overlaps x
+    assert ag(L, ws=None) == fo.FO_ERR_WORKSPACE
+    assert ag(L, wsb=16) == fo.FO_ERR_WORKSPACE
+    s, k1 = sched(order=[0, 1, 1, 2])
+    assert ag(L, s=s) == fo.FO_ERR_ORDER
+    s, k1 = sched(order=[0, 1, 2, 4])
+    assert ag(L, s=s) == fo.FO_ERR_ORDER
+    s, k1 = sched(local=4)
+    assert ag(L, s=s) == fo.FO_ERR_SCHEDULE
+    s, k1 = sched(epoch=0)
+    assert ag(L, s=s) == fo.FO_ERR_SCHEDULE
+    s, k1 = sched(mode=3)
+    assert ag(L, s=s) == fo.FO_ERR_SCHEDULE
+    s, k1 = sched(split=[1, 9, 1, 1])
+    assert ag(L, s=s) == fo.FO_ERR_SCHEDULE
+    s, k1 = sched(R=0)
+    assert ag(L, s=s) == fo.FO_ERR_SHAPE
+    s, k1 = sched(R=65)
+    assert ag(L, s=s) == fo.FO_ERR_SHAPE
+
+
+def test_gemm_rs_validation(L):
+    s, keep = sched()
+    assert L.fo_gemm_rs(A, A, None, None, 256, 512, 512, ctypes.byref(s), WS, 1 << 30, None) == fo.FO_ERR_NULL
+    s, keep = sched(arrived=A)        # GEMM-RS takes no arrival flags
+    assert L.fo_gemm_rs(A, A, A2, None, 256, 512, 512, ctypes.byref(s), WS, 1 << 30, None) == fo.FO_ERR_SCHEDULE
+    s, keep = sched()
+    assert L.fo_gemm_rs(A, A, A2, None, 256, 512, 500, ctypes.byref(s), WS, 1 << 30, None) == fo.FO_ERR_ALIGN
+
+
+def test_chunk_reduce_validation(L):
+    R = 4
+    n = 1024
+    srcs = (ctypes.c_void_p * R)(*[A + i * 0x100000 for i in range(R)])
+    s, keep = sched(R)
+    red = L.fo_chunk_reduce
+    assert red(None, fo.FO_F32, srcs, n, ctypes.byref(s), None) == fo.FO_ERR_NULL
+    assert red(A2, 5, srcs, n, ctypes.byref(s), None) == fo.FO_ERR_DTYPE
+    assert red(A2, fo.FO_F32, srcs, 0, ctypes.byref(s), None) == fo.FO_ERR_SHAPE
+    assert red(A2, fo.FO_F32, srcs, 1022, ctypes.byref(s), None) == fo.FO_ERR_ALIGN
+    assert red(A2 + 4, fo.FO_F32, srcs, n, ctypes.byref(s), None) == fo.FO_ERR_ALIGN
+    # dst overlapping a peer source is refused; dst == srcs[local] (fp32) is allowed
+    assert red(A + 0x100000, fo.FO_F32, srcs, n, ctypes.byref(s), None) == fo.FO_ERR_ALIAS
+    assert red(A, fo.FO_BF16, srcs, n, ctypes.byref(s), None) == fo.FO_ERR_ALIAS
+    bad = (ctypes.c_void_p * R)(*[A, A + 64, A + 0x200000, A + 0x300000])
+    assert red(A2, fo.FO_F32, bad, n, ctypes.byref(s), None) == fo.FO_ERR_ALIAS
+    nul = (ctypes.c_void_p * R)(*[A, None, A + 0x200000, A + 0x300000])
+    assert red(A2, fo.FO_F32, nul, n, ctypes.byref(s), None) == fo.FO_ERR_NULL
+    s, keep = sched(R, order=[3, 2, 1, 1])
+    assert red(A2, fo.FO_F32, srcs, n, ctypes.byref(s), None) == fo.FO_ERR_ORDER
+
+
+def test_emulate_validation(L):
+    P = ctypes.c_void_p
+    d = (P * 1)(A)
+    s = (P * 1)(A2)
+    b = (ctypes.c_size_t * 1)(64)
+    rel = (ctypes.c_int64 * 1)(100)
+    iss = (ctypes.c_int64 * 1)(200)             # issue after release
+    cid = (ctypes.c_int32 * 1)(1)
+    em = L.fo_emulate_arrivals
+    assert em(d, s, b, None, rel, cid, 0, A, 1, A, None) == fo.FO_OK   # nothing to do
+    assert em(d, s, b, None, rel, cid, -1, A, 1, A, None) == fo.FO_ERR_SHAPE
+    assert em(d, s, b, None, rel, cid, 1, None, 1, A, None) == fo.FO_ERR_NULL
+    assert em(d, s, b, None, rel, cid, 1, A, 1, None, None) == fo.FO_ERR_NULL
+    assert em(d, s, b, None, rel, cid, 1, A, 0, A, None) == fo.FO_ERR_SCHEDULE
+    assert em(d, s, b, iss, rel, cid, 1, A, 1, A, None) == fo.FO_ERR_SCHEDULE
+    bad = (ctypes.c_int32 * 1)(64)
+    assert em(d, s, b, None, rel, bad, 1, A, 1, A, None) == fo.FO_ERR_SCHEDULE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fo, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(fo, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        fo.lib()

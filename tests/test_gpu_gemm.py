@@ -1,0 +1,220 @@
+"""GPU parity of fo_ag_gemm / fo_gemm_rs against the fp64 oracle, through the C ABI."""
+import itertools
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from helpers import (bf16_bits_to_f64, check_exact, check_tolerance, dev_bf16, dev_f32, host,
+                     log)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def fo():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sp_rank_adaptive_amd as fo
+    fo.lib()
+    return fo
+
+
+class Epochs:
+    def __init__(self):
+        self.e = 0
+
+    def next(self):
+        self.e += 1
+        return self.e
+
+
+EP = Epochs()
+
+
+def workspace(fo, m, n, k, R):
+    nb = fo.fo_workspace_bytes(m, n, k, R)
+    assert nb > 0
+    return torch.zeros(nb, dtype=torch.uint8, device="cuda")
+
+
+def run_ag(fo, x, w, R, y_dtype=torch.float32, ws=None, **sched):
+    m, k = x.shape
+    n = w.shape[0]
+    y = torch.full((m, n), float("nan"), dtype=y_dtype, device="cuda")
+    if ws is None:
+        ws = workspace(fo, m, n, k, R)
+    s = fo.Schedule(nchunks=R, epoch=EP.next(), **sched)
+    fo.fo_ag_gemm(x, w, y, s, ws)
+    torch.cuda.synchronize()
+    return y, ws
+
+
+def gemm_case(cfg, mode, m=None):
+    xb, wb = wl.gemm_inputs(cfg, mode, m=m)
+    return xb, wb, dev_bf16(xb), dev_bf16(wb)
+
+
+def test_ag_gemm_tiny_int_bitexact_all_orders(fo, orc):
+    c = wl.CFG1
+    log(f"case: cfg1 int {c.m}x{c.n}x{c.k} R={c.R}")
+    xb, wb, x, w = gemm_case(c, "int")
+    ref = orc.gemm(xb, wb)
+    for order in itertools.permutations(range(c.R)):
+        for mode in (fo.FO_SCHED_READY_FIRST, fo.FO_SCHED_STRICT):
+            y, ws = run_ag(fo, x, w, c.R, order=list(order), mode=mode)
+            check_exact(host(y), ref, f"order {order} mode {mode}")
+            assert int(ws.sum()) == 0, "workspace not returned to zero"
+
+
+@pytest.mark.parametrize("local", [0, 1, 2, 3])
+def test_ag_gemm_tiny_every_local_rank(fo, orc, local):
+    c = wl.CFG1
+    xb, wb, x, w = gemm_case(c, "int")
+    y, _ = run_ag(fo, x, w, c.R, local=local)
+    check_exact(host(y), orc.gemm(xb, wb), f"local {local}")
+
+
+@pytest.mark.parametrize("m,n,k,R", [(210, 200, 136, 3), (64, 40, 8, 1), (520, 136, 200, 5),
+                                     (128, 128, 64, 2), (1024, 96, 1032, 4)])
+def test_ag_gemm_ragged_shapes(fo, orc, m, n, k, R):
+    log(f"case: ragged {m}x{n}x{k} R={R}")
+    for mode in ("int", "gauss"):
+        xb = wl.bf16_operand((m, k), mode, 1.0, 900 + m)
+        wb = wl.bf16_operand((n, k), mode, 0.02 if mode == "gauss" else 1.0, 901 + n)
+        ref = orc.gemm(xb, wb)
+        y, _ = run_ag(fo, dev_bf16(xb), dev_bf16(wb), R)
+        if mode == "int":
+            check_exact(host(y), ref, "int")
+        else:
+            check_tolerance(host(y), ref, what="gauss")
+
+
+def test_ag_gemm_bf16_output(fo, orc):
+    c = wl.CFG1
+    xb, wb, x, w = gemm_case(c, "gauss")
+    ref = orc.gemm(xb, wb)
+    y, _ = run_ag(fo, x, w, c.R, y_dtype=torch.bfloat16)
+    got = bf16_bits_to_f64(host(y))
+    check_tolerance(got, ref, frob_ref=bf16_bits_to_f64(orc.f64_to_bf16(ref)), what="bf16 out")
+    # integer inputs: the fp32 sums are exact, so the bf16 result is RNE of the exact value
+    xb, wb, x, w = gemm_case(c, "int")
+    ref = orc.gemm(xb, wb)
+    y, _ = run_ag(fo, x, w, c.R, y_dtype=torch.bfloat16)
+    assert np.array_equal(host(y), orc.f64_to_bf16(ref))
+
+
+def test_ag_gemm_split_k_exact_and_deterministic(fo, orc):
+    m, n, k, R = 512, 256, 1024, 4
+    xb = wl.bf16_operand((m, k), "int", 1.0, 950)
+    wb = wl.bf16_operand((n, k), "int", 1.0, 951)
+    ref = orc.gemm(xb, wb)
+    x, w = dev_bf16(xb), dev_bf16(wb)
+    for split in ([1, 4, 1, 2], [8, 8, 1, 1], [3, 1, 5, 1]):
+        y, ws = run_ag(fo, x, w, R, split=split)
+        check_exact(host(y), ref, f"split {split}")
+        assert int(ws.sum()) == 0
+    xb = wl.bf16_operand((m, k), "gauss", 1.0, 952)
+    wb = wl.bf16_operand((n, k), "gauss", 0.02, 953)
+    ref = orc.gemm(xb, wb)
+    x, w = dev_bf16(xb), dev_bf16(wb)
+    y1, _ = run_ag(fo, x, w, R, split=[1, 4, 1, 2])
+    y2, _ = run_ag(fo, x, w, R, split=[1, 4, 1, 2])
+    assert torch.equal(y1, y2), "split-K result not run-to-run deterministic"
+    check_tolerance(host(y1), ref, what="split gauss")
+    # unsplit chunks are bitwise identical whatever the other chunks' splits
+    y3, _ = run_ag(fo, x, w, R)
+    assert torch.equal(y1[0:128], y3[0:128]) and torch.equal(y1[256:384], y3[256:384])
+
+
+def test_ag_gemm_preset_flags_and_epoch_reuse(fo, orc):
+    c = wl.CFG1
+    xb, wb, x, w = gemm_case(c, "int")
+    ref = orc.gemm(xb, wb)
+    flags = torch.zeros(c.R, dtype=torch.int32, device="cuda")
+    ws = workspace(fo, c.m, c.n, c.k, c.R)
+    stamps = torch.zeros(2 * c.R + 2, dtype=torch.int64, device="cuda")
+    for _ in range(3):      # flags are never reset: each call raises the epoch
+        e = EP.next()
+        flags.fill_(e)
+        y = torch.full((c.m, c.n), float("nan"), device="cuda")
+        s = fo.Schedule(nchunks=c.R, epoch=e, arrived=flags, stamps=stamps)
+        fo.fo_ag_gemm(x, w, y, s, ws)
+        torch.cuda.synchronize()
+        check_exact(host(y), ref, "preset flags")
+        assert int(ws.sum()) == 0
+        st = host(stamps).astype(np.int64)
+        assert st[2 * c.R + 1] >= st[2 * c.R] > 0
+
+
+def test_ag_gemm_timeout_from_unset_flag(fo):
+    """A flag the host never sets: the bounded wait ends with FO_ERR_TIMEOUT and
+    the kernel exits; the workspace is clean afterwards."""
+    c = wl.CFG1
+    xb, wb, x, w = gemm_case(c, "int")
+    flags = torch.zeros(c.R, dtype=torch.int32, device="cuda")
+    e = EP.next()
+    flags.fill_(e)
+    flags[2] = 0                        # chunk 2 never lands
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = workspace(fo, c.m, c.n, c.k, c.R)
+    y = torch.zeros((c.m, c.n), device="cuda")
+    s = fo.Schedule(nchunks=c.R, epoch=e, arrived=flags, status=status, timeout_ns=2_000_000)
+    fo.fo_ag_gemm(x, w, y, s, ws)
+    torch.cuda.synchronize()
+    assert int(status.item()) == fo.FO_ERR_TIMEOUT
+    assert int(ws.sum()) == 0
+    # the next call on the same workspace works
+    flags.fill_(EP.next())
+    s = fo.Schedule(nchunks=c.R, epoch=EP.e, arrived=flags)
+    fo.fo_ag_gemm(x, w, y, s, ws)
+    torch.cuda.synchronize()
+
+
+def test_ag_gemm_full_size_sampled_rows(fo, orc):
+    for cfg in (wl.CFG2, wl.CFG5):
+        log(f"case: cfg{cfg.cfg} gauss {cfg.m}x{cfg.n}x{cfg.k} R={cfg.R}")
+        xb, wb, x, w = gemm_case(cfg, "gauss")
+        y, _ = run_ag(fo, x, w, cfg.R)
+        rows = np.sort(np.random.Generator(np.random.PCG64(7 + cfg.cfg)).choice(cfg.m, 48, replace=False))
+        mc = cfg.m // cfg.R
+        rows = np.unique(np.concatenate([rows, [0, mc - 1, mc, cfg.m - 1]]))
+        ref = orc.gemm(xb[rows], wb)
+        check_tolerance(host(y)[rows], ref, what=f"cfg{cfg.cfg}")
+
+
+def test_ag_gemm_full_size_int_sampled_rows(fo, orc):
+    cfg = wl.CFG2
+    xb, wb, x, w = gemm_case(cfg, "int")
+    y, _ = run_ag(fo, x, w, cfg.R, arrived=None)
+    rows = np.arange(0, cfg.m, 97)
+    check_exact(host(y)[rows], orc.gemm(xb[rows], wb), "cfg2 int")
+
+
+def test_gemm_rs_parity_done_flags_and_order(fo, orc):
+    cfg = wl.CFG3
+    for mode in ("int", "gauss"):
+        log(f"case: cfg3 gemm_rs {mode}")
+        xb, wb, x, w = gemm_case(cfg, mode)
+        part = torch.full((cfg.m, cfg.n), float("nan"), device="cuda")
+        done = torch.zeros(cfg.R, dtype=torch.int32, device="cuda")
+        stamps = torch.zeros(2 * cfg.R + 2, dtype=torch.int64, device="cuda")
+        ws = workspace(fo, cfg.m, cfg.n, cfg.k, cfg.R)
+        e = EP.next()
+        s = fo.Schedule(nchunks=cfg.R, epoch=e, stamps=stamps)
+        fo.fo_gemm_rs(x, w, part, done, s, ws)
+        torch.cuda.synchronize()
+        assert (host(done) == e).all()
+        rows = np.unique(np.concatenate([np.arange(0, cfg.m, 131), [cfg.m - 1]]))
+        ref = orc.gemm(xb[rows], wb)
+        if mode == "int":
+            check_exact(host(part)[rows], ref, "rs int")
+        else:
+            check_tolerance(host(part)[rows], ref, what="rs gauss")
+        st = host(stamps).astype(np.int64)
+        R = cfg.R
+        # the local chunk is claimed last: its first claim follows every peer's
+        first = st[:R]
+        assert first[0] >= first[1:].max()
