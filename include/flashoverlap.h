@@ -96,7 +96,7 @@ typedef struct fo_schedule {
   uint64_t        timeout_ns;  /* bound on one flag wait; 0 = 10 s              */
   int32_t        *status;      /* device [1], optional: receives FO_ERR_TIMEOUT */
   uint64_t       *stamps;      /* device, optional wall-clock timeline (ticks of
-                                  the device wall clock, fo_wall_clock_hz):
+                                  the device wall clock, rate from fo_device_info):
                                   GEMM calls: [2R+2] = per-chunk first claim,
                                   per-chunk completion, kernel start, last
                                   output written.  fo_chunk_reduce: [2] = first
@@ -113,8 +113,10 @@ typedef struct fo_schedule {
 
 /* Workspace bytes that fo_ag_gemm / fo_gemm_rs need for an m x n x k problem
  * in R chunks with the automatic split policy (or any split vector whose split
- * chunks fit; the call checks).  The workspace must be zero-filled once before
- * its first use; every call leaves it zeroed again when it completes. */
+ * chunks fit; the call checks).  The workspace starts with work counters and
+ * ends with split-K partial tiles.  It must be zero-filled once before its
+ * first use; every call leaves the counters zero again when it completes
+ * (also after FO_ERR_TIMEOUT); the partial tiles need no initialisation. */
 size_t fo_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t nchunks);
 
 /* Chunked AG-GEMM (technical summary §2, Flash-AG; row/column-parallel
