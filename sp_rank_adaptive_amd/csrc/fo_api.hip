@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "fo_internal.hpp"
@@ -100,21 +102,31 @@ struct GemmPlan {
   int64_t mc;
   int tiles_m, tiles_n, tiles;
   int kt_total;
-  size_t counter_bytes, partial_offset, partial_capacity_tiles, total_bytes;
+  size_t counter_bytes, partial_offset, total_bytes;
 };
 
-GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, int R) {
+// Workspace bound over every tile configuration the library may pick.
+GemmPlan plan_workspace(int64_t m, int64_t n, int64_t k, int R) {
   GemmPlan p{};
   p.mc = m / R;
-  p.tile = choose_tile(p.mc, n, k);
+  int bm = 0, bn = 0;
+  max_tile_dims(&bm, &bn);
+  const int64_t most_tiles = ((p.mc + 127) / 128) * ((n + 127) / 128);      // smallest tiles
+  const int64_t padded = ((p.mc + bm - 1) / bm * bm) * ((n + bn - 1) / bn * bn);
+  (void)k;
+  p.counter_bytes = WS_HEADER_BYTES + (size_t)R * most_tiles * sizeof(uint32_t);
+  p.partial_offset = (p.counter_bytes + 255) & ~(size_t)255;
+  p.total_bytes = p.partial_offset + (size_t)kMaxSplit * padded * sizeof(float);
+  return p;
+}
+
+GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, int R, int grid, bool leave_room) {
+  GemmPlan p = plan_workspace(m, n, k, R);
+  p.tile = choose_tile(p.mc, n, k, R, grid, leave_room);
   p.tiles_m = (int)((p.mc + p.tile.bm - 1) / p.tile.bm);
   p.tiles_n = (int)((n + p.tile.bn - 1) / p.tile.bn);
   p.tiles = p.tiles_m * p.tiles_n;
   p.kt_total = (int)((k + 63) / 64);
-  p.counter_bytes = WS_HEADER_BYTES + (size_t)R * p.tiles * sizeof(uint32_t);
-  p.partial_offset = (p.counter_bytes + 255) & ~(size_t)255;
-  p.partial_capacity_tiles = (size_t)p.tiles * kMaxSplit;
-  p.total_bytes = p.partial_offset + p.partial_capacity_tiles * partial_slot_bytes(p.tile);
   return p;
 }
 
@@ -133,12 +145,18 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
   const size_t ybytes = (size_t)m * n * (y_bf16 ? 2 : 4);
   if (overlaps(y, ybytes, x, (size_t)m * k * 2) || overlaps(y, ybytes, w, (size_t)n * k * 2))
     return FO_ERR_ALIAS;
-  const GemmPlan p = plan_gemm(m, n, k, R);
   if (!ws) return FO_ERR_WORKSPACE;
-  if (ws_bytes < p.counter_bytes || !aligned16(ws)) return FO_ERR_WORKSPACE;
+  if (ws_bytes < plan_workspace(m, n, k, R).total_bytes || !aligned16(ws)) return FO_ERR_WORKSPACE;
 
   const DevInfo *I = dev_info();
   if (!I) return FO_ERR_HIP;
+
+  // Workgroups: one per CU.  With arrival flags the tile configuration must
+  // leave registers free on every SIMD, so the one-wave timer and flag
+  // kernels of a copy engine emulator can run beside the persistent grid.
+  const int full = I->cus;
+  const int grid_cap = s->max_workgroups > 0 ? s->max_workgroups : full;
+  const GemmPlan p = plan_gemm(m, n, k, R, grid_cap, s->arrived != nullptr);
 
   GemmArgs a{};
   a.x = static_cast<const uint16_t *>(x);
@@ -151,6 +169,26 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
   a.mc = (int32_t)p.mc;
   a.tiles_m = p.tiles_m;
   a.tiles_n = p.tiles_n;
+  // Rectangles of each chunk's tile grid, one per XCD: the shape that
+  // minimises the operand rows one XCD streams over all R chunks (X rows of
+  // its row band in every chunk plus W rows of its column band).
+  {
+    const int shapes[4][2] = {{1, 8}, {2, 4}, {4, 2}, {8, 1}};
+    int64_t best = -1;
+    for (const auto &sh : shapes) {
+      const int gm = sh[0], gn = sh[1];
+      int64_t cost = (int64_t)R * ((p.tiles_m + gm - 1) / gm) * p.tile.bm +
+                     (int64_t)((p.tiles_n + gn - 1) / gn) * p.tile.bn;
+      if (gm > p.tiles_m || gn > p.tiles_n) cost += (int64_t)1 << 40;   // empty rectangles
+      if (best < 0 || cost < best) { best = cost; a.gm = gm; a.gn = gn; }
+    }
+    for (int g = 0; g < XCDS; ++g) {
+      const int i = g / a.gn, j = g % a.gn;
+      const int rows = (i + 1) * p.tiles_m / a.gm - i * p.tiles_m / a.gm;
+      const int cols = (j + 1) * p.tiles_n / a.gn - j * p.tiles_n / a.gn;
+      a.gtiles[g] = rows * cols;
+    }
+  }
   a.local = s->local;
   a.strict = s->mode == FO_SCHED_STRICT ? 1 : 0;
   a.arrived = s->arrived;
@@ -162,13 +200,6 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
   a.ws32 = static_cast<uint32_t *>(ws);
   a.partials = reinterpret_cast<float *>(static_cast<char *>(ws) + p.partial_offset);
   expand_order(s, a.order);
-
-  // Workgroups: one per CU; with arrival flags leave one CU per XCD free for
-  // the emulator's timer and flag kernels on the side stream.
-  int occ = 1;
-  const int full = I->cus * occ;
-  int grid_cap = s->max_workgroups > 0 ? s->max_workgroups : full;
-  if (s->arrived && s->max_workgroups == 0) grid_cap = full > 16 ? full - 8 : full;
 
   // Split policy.
   int split[FO_MAX_CHUNKS];
@@ -243,7 +274,7 @@ extern "C" {
 
 size_t fo_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t nchunks) {
   if (m <= 0 || n <= 0 || k <= 0 || nchunks < 1 || nchunks > FO_MAX_CHUNKS || m % nchunks) return 0;
-  return plan_gemm(m, n, k, nchunks).total_bytes;
+  return plan_workspace(m, n, k, nchunks).total_bytes;
 }
 
 fo_status fo_ag_gemm(const void *x, const void *w, void *y, fo_dtype y_dtype, int64_t m, int64_t n,

@@ -1,6 +1,6 @@
 // Persistent chunked GEMM for gfx950: bf16 MFMA (16x16x32), fp32 accumulate,
-// LDS-staged double-buffered tiles, work claimed chunk by chunk as the chunks'
-// epoch flags show them landed.
+// LDS-staged double-buffered tiles fed by a register prefetch pipeline, work
+// claimed chunk by chunk as the chunks' epoch flags show them landed.
 //
 // This is the partitioned computation of FlashOverlap (euno.news
 // "Methodology" step 2: the GEMM is split into sub-tasks on the same row
@@ -11,13 +11,28 @@
 // only that chunk's work remains (Flash-AG), and in GEMM-RS mode the chunk that
 // stays local is produced last (Flash-RS).
 //
-// One workgroup = 4 waves (one per SIMD) computing a BM x BN output tile; each
-// wave owns a (BM/2) x (BN/2) quadrant made of 16x16 MFMA blocks.  Operand
-// tiles of BM x 64 (X rows) and BN x 64 (W rows, i.e. output columns) sit in
-// LDS with a 16-byte XOR swizzle so the MFMA fragment reads of 8 consecutive
-// rows hit distinct bank groups.
+// Layout and schedule
+//  - One workgroup = 4 waves (one per SIMD) computing a BM x BN output tile;
+//    each wave owns a (BM/2) x (BN/2) quadrant of 16x16 MFMA blocks.
+//  - Operand tiles of BM x BK (X rows) and BN x BK (W rows = output columns)
+//    sit in an LDS ring of STAGES buffers with a 16-byte XOR swizzle, so the
+//    fragment reads of 8 consecutive rows hit distinct bank groups.
+//  - The copy engine behind the buffer loads writes each stage straight into
+//    LDS (no register staging, no LDS store instructions); STAGES-1 stages are
+//    in flight while one is multiplied, one barrier per stage.
+//  - Each chunk's tile grid is cut into 8 rectangles, one per XCD (workgroup
+//    b runs on XCD b % 8); a workgroup claims from its own XCD's rectangle
+//    first, so each XCD's L2 serves a few X row blocks and W column blocks to
+//    its 32 CUs, and steals from the chunk's other rectangles when its own is
+//    empty.  The host picks the rectangle shape that minimises the operand
+//    rows one XCD streams over all chunks.
 #include "fo_device.hpp"
 #include "fo_internal.hpp"
+
+#include <stdio.h>
+#include <stdlib.h>
+#include <type_traits>
+#include <utility>
 
 namespace fo {
 
@@ -25,195 +40,371 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BK = 64;    // k depth of one LDS stage (two MFMA k-steps of 32)
 constexpr int NT = 256;   // threads per workgroup
+constexpr uint32_t kBufDword3 = 0x00020000u;   // raw buffer, 32-bit data format (gfx9)
 
-template <int BM, int BN>
+// Tile of BM x BN outputs; k staged through an LDS ring of STAGES buffers,
+// BK at a time (BK = 32 or 64: one or two MFMA k-steps per stage).
+template <int BM, int BN, int BK, int STAGES>
 struct Cfg {
   static constexpr int WTM = BM / 2, WTN = BN / 2;   // wave tile
   static constexpr int FM = WTM / 16, FN = WTN / 16; // MFMA blocks per wave
-  static constexpr int AV = BM * 8 / NT;             // 16-byte loads per thread (X)
-  static constexpr int BV = BN * 8 / NT;             // 16-byte loads per thread (W)
-  static constexpr int A_BYTES = BM * BK * 2;
-  static constexpr int B_BYTES = BN * BK * 2;
+  static constexpr int ROWB = BK * 2;                // LDS bytes per operand row
+  static constexpr int CH = BK / 8;                  // 16-byte pieces per row
+  static constexpr int RSTEP = NT / CH;              // rows covered by one load round
+  static constexpr int AV = BM / RSTEP;              // load rounds per stage (X)
+  static constexpr int BV = BN / RSTEP;              // load rounds per stage (W)
+  static constexpr int V = AV + BV;
+  static constexpr int KS = BK / 32;                 // MFMA k-steps per stage
+  static constexpr int A_BYTES = BM * ROWB;
+  static constexpr int B_BYTES = BN * ROWB;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int LDS = STAGES * STAGE;
+  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(STAGES >= 2 && STAGES <= 4, "STAGES");
   static_assert(BM % 32 == 0 && BN % 32 == 0, "tile");
-  static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "tile loads");
+  static_assert(BM % RSTEP == 0 && BN % RSTEP == 0, "tile loads");
+  static_assert(LDS + 64 <= 160 * 1024, "LDS");
+  // 16-byte piece `ch` of row `r` lives at piece ch ^ swz(r): the fragment
+  // reads of 8 consecutive rows then cover 8 distinct 16-byte bank groups.
+  __device__ static constexpr int swz(int r) { return BK == 64 ? (r & 7) : ((r >> 1) & 3); }
 };
+
+// LDS byte address of a shared-memory pointer (the DMA destination base).
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// 16 bytes per lane from a buffer resource straight into LDS: lane L's bytes
+// land at m0 + 16 L.  Issued from asm so the compiler does not wait for
+// every outstanding copy before each LDS read; waits are explicit
+// (wait_vm) and a workgroup barrier follows them before any read.
+__device__ __forceinline__ void dma16(uint32_t m0, int voff, __amdgpu_buffer_rsrc_t rs, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m0), "v"(voff), "s"(rs), "s"(soff) : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+  }(std::make_integer_sequence<int, N>{});
+}
 
 struct ClaimState {
-  uint64_t landed;     // bit c: chunk c seen landed (acquire done)
-  uint64_t exhausted;  // bit c: chunk c has no unit left
+  uint64_t acquired;   // bit c: this workgroup has done the acquire for chunk c
 };
 
-// Thread 0 of a workgroup: pick the next unit.  Returns the chunk (>= 0) and
-// sets `unit`; -1 when every chunk is exhausted; -2 on abort or timeout.
-__device__ int claim_unit(const GemmArgs &a, ClaimState &st, int &unit, uint64_t t_begin) {
+struct Unit {
+  int c;      // chunk, -1 finished, -2 abort
+  int tm, tn; // tile row / column inside the chunk
+  int sp;     // split index
+  int first;  // 1 for the first unit of group 0 (chunk start stamp)
+};
+
+__device__ __forceinline__ uint32_t group_units(const GemmArgs &a, int c, int g) {
+  return (uint32_t)(a.gtiles[g] * a.split[c]);
+}
+
+// Group g of a chunk is rectangle (g / gn, g % gn) of the chunk's tile grid,
+// cut into gm row bands and gn column bands; its tiles are numbered row by
+// row.  Rectangle g is the XCD g queue, so an XCD streams a few X row blocks
+// and a few W column blocks instead of every row block of the chunk.
+__device__ __forceinline__ void group_tile(const GemmArgs &a, int g, int tl, int &tm, int &tn) {
+  const int i = g / a.gn, j = g - (g / a.gn) * a.gn;
+  const int rlo = i * a.tiles_m / a.gm;
+  const int clo = j * a.tiles_n / a.gn, chi = (j + 1) * a.tiles_n / a.gn;
+  const int ncols = chi - clo;
+  tm = rlo + tl / ncols;
+  tn = clo + tl - (tl / ncols) * ncols;
+}
+
+// Wave 0 of a workgroup picks the next unit (all 64 lanes call this).
+// One round trip reads every arrival flag and every (chunk, group) claim
+// counter in parallel across the lanes; the workgroup then takes the first
+// chunk in priority order that has landed and has work (its own XCD's group
+// if that has work, else the group with the most left) with one fetch-add.
+// STRICT mode only looks at the first chunk in order that still has work.
+__device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_hint) {
+  const int lane = threadIdx.x & 63;
+  const int R = a.R;
   uint64_t wait_from = 0;
+  Unit r{-1, 0, 0, 0, 0};
   for (;;) {
-    bool waiting = false;
-    for (int s = 0; s < a.R; ++s) {
-      const int c = a.order[s];
-      const uint64_t bit = 1ull << c;
-      if (st.exhausted & bit) continue;
-      if (!(st.landed & bit)) {
-        if (a.arrived == nullptr || c == a.local) {
-          st.landed |= bit;
-        } else if (epoch_reached(load_relaxed(a.arrived + c), a.epoch)) {
-          // flag seen: make the copy's data visible before any read of it
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
-          st.landed |= bit;
-        } else {
-          waiting = true;
-          if (a.strict) break;
+    // landed[s]: chunk order[s] usable
+    uint64_t landed = 0;
+    {
+      bool ok = false;
+      if (lane < R) {
+        const int c = a.order[lane];
+        ok = a.arrived == nullptr || c == a.local ||
+             epoch_reached(load_relaxed(a.arrived + c), a.epoch);
+      }
+      landed = __ballot(ok);
+    }
+    // remaining work per (order position, group): 8 groups per position
+    uint32_t rem_own = 0, best_rem = 0;
+    int pick_s = -1, pick_g = -1;
+    uint64_t has_work = 0;   // bit s: position s has work in some group
+    for (int base = 0; base < R * XCDS; base += 64) {
+      const int pidx = base + lane;
+      uint32_t left = 0;
+      if (pidx < R * XCDS) {
+        const int sidx = pidx / XCDS, g = pidx % XCDS;
+        const int c = a.order[sidx];
+        const uint32_t cnt = load_relaxed(a.ws32 + WS_CLAIM + c * XCDS + g);
+        const uint32_t tot = group_units(a, c, g);
+        left = cnt < tot ? tot - cnt : 0;
+      }
+      const uint64_t m = __ballot(left > 0);
+      for (uint64_t mm = m; mm; mm &= mm - 1) has_work |= 1ull << ((base + __builtin_ctzll(mm)) / XCDS);
+      // first eligible position in this batch
+      for (int sidx = base / XCDS; sidx < (base + 64) / XCDS && sidx < R && pick_s < 0; ++sidx) {
+        const uint64_t gm = (m >> (sidx * XCDS - base)) & 0xFFull;
+        if (!gm) continue;
+        // first claim of a workgroup: the q-th workgroup of an XCD skips the
+        // first q units its XCD's group has left (in priority order over
+        // landed chunks), so the XCD's workgroups start on distinct units
+        // instead of racing for the first chunk's few
+        if (rank_hint >= 0 && !a.strict && ((landed >> sidx) & 1) && ((gm >> xg) & 1)) {
+          const uint32_t own = __shfl(left, sidx * XCDS - base + xg);
+          if ((uint32_t)rank_hint >= own) { rank_hint -= (int)own; continue; }
+        }
+        if (a.strict) {
+          // strict: the first position with work decides, landed or not
+          if (!((landed >> sidx) & 1)) { pick_s = -2; break; }
+        } else if (!((landed >> sidx) & 1)) {
           continue;
         }
+        pick_s = sidx;
+        if ((gm >> xg) & 1) {
+          pick_g = xg;
+        } else {
+          // the group with the most work left
+          for (uint64_t g2 = gm; g2; g2 &= g2 - 1) {
+            const int g = __builtin_ctzll(g2);
+            const uint32_t lv = __shfl(left, sidx * XCDS - base + g);
+            if (lv > best_rem) { best_rem = lv; pick_g = g; }
+          }
+        }
       }
-      const uint32_t u = fetch_add_relaxed(a.ws32 + WS_CLAIM + c, 1u);
-      if ((int)u < a.units[c]) {
-        unit = (int)u;
-        return c;
-      }
-      st.exhausted |= bit;
+      if (pick_s != -1) break;
     }
-    if (!waiting) return -1;
-    if (load_relaxed(a.ws32 + WS_ABORT)) return -2;
+    (void)rem_own;
+    if (pick_s < 0 && rank_hint >= 0) {   // fewer units than workgroups: normal claim
+      rank_hint = -1;
+      continue;
+    }
+    rank_hint = -1;
+    if (pick_s >= 0) {
+      const int c = a.order[pick_s];
+      if (!((st.acquired >> c) & 1ull)) {
+        // first use of a landed peer chunk: make the copy's data visible
+        if (a.arrived != nullptr && c != a.local) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+        st.acquired |= 1ull << c;
+      }
+      uint32_t u = 0;
+      if (lane == 0) u = fetch_add_relaxed(a.ws32 + WS_CLAIM + c * XCDS + pick_g, 1u);
+      u = __builtin_amdgcn_readfirstlane(u);
+      if (u < group_units(a, c, pick_g)) {
+        const int S = a.split[c];
+        const int tl = (int)u / S;
+        r.c = c;
+        r.sp = (int)u - tl * S;
+        group_tile(a, pick_g, tl, r.tm, r.tn);
+        r.first = (pick_g == 0 && u == 0);
+        return r;
+      }
+      continue;   // lost the race for the last unit: look again
+    }
+    if (has_work == 0) { r.c = -1; return r; }   // every chunk fully claimed
+    // work left only in chunks that have not landed: wait
+    if (load_relaxed(a.ws32 + WS_ABORT)) { r.c = -2; return r; }
     const uint64_t t = now_ticks();
     if (wait_from == 0) wait_from = t;
     if (t - wait_from > a.timeout_ticks) {
-      if (a.status) __hip_atomic_store(a.status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_SYSTEM);
-      __hip_atomic_store(a.ws32 + WS_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return -2;
+      if (lane == 0) {
+        if (a.status) __hip_atomic_store(a.status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(a.ws32 + WS_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      r.c = -2;
+      return r;
     }
-    (void)t_begin;
     __builtin_amdgcn_s_sleep(4);
   }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int BK, int STAGES>
 __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
-  using C = Cfg<BM, BN>;
+  using C = Cfg<BM, BN, BK, STAGES>;
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
-  __shared__ int s_chunk, s_unit, s_last;
+  __shared__ Unit s_unit;
+  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t K = a.k, N = a.n;
+  const int xg = (int)(blockIdx.x % XCDS);
 
-  ClaimState st{0ull, 0ull};
-  const uint64_t t_begin = now_ticks();
-  if (blockIdx.x == 0 && tid == 0 && a.stamps) store_u64_relaxed(a.stamps + 2 * a.R, t_begin);
+  ClaimState st{0ull};
+  int rank_hint = (int)(blockIdx.x / XCDS);   // this workgroup's rank inside its XCD
+  // The stage buffers are written only by the copy engine (asm below): hand
+  // the buffer to an opaque asm so the compiler cannot assume it is never
+  // written and fold the fragment reads away.
+  asm volatile("" :: "v"(lds) : "memory");
+  if (blockIdx.x == 0 && tid == 0 && a.stamps) store_u64_relaxed(a.stamps + 2 * a.R, now_ticks());
 
   for (;;) {
-    if (tid == 0) {
-      int u = 0;
-      const int c = claim_unit(a, st, u, t_begin);
-      s_chunk = c;
-      s_unit = u;
+    if (wave == 0) {
+      const Unit u = claim_unit(a, st, xg, rank_hint);
+      if (lane == 0) s_unit = u;
     }
     __syncthreads();
-    const int c = s_chunk;
-    const int u = s_unit;
+    Unit un = s_unit;
+    un.c = __builtin_amdgcn_readfirstlane(un.c);
+    un.tm = __builtin_amdgcn_readfirstlane(un.tm);
+    un.tn = __builtin_amdgcn_readfirstlane(un.tn);
+    un.sp = __builtin_amdgcn_readfirstlane(un.sp);
+    const int c = un.c;
     if (c < 0) break;
-    if (u == 0 && tid == 0 && a.stamps) store_u64_relaxed(a.stamps + c, now_ticks());
+    if (un.first && tid == 0 && a.stamps) store_u64_relaxed(a.stamps + c, now_ticks());
 
     const int S = a.split[c];
-    const int tile = u / S;
-    const int sp = u - tile * S;
-    const int tm = tile / a.tiles_n;
-    const int tn = tile - tm * a.tiles_n;
-    const int64_t row0 = (int64_t)c * a.mc + (int64_t)tm * BM;
+    const int sp = un.sp;
+    const int tile = un.tm * a.tiles_n + un.tn;
+    const int64_t row0 = (int64_t)c * a.mc + (int64_t)un.tm * BM;
     const int64_t rowlim = (int64_t)(c + 1) * a.mc;
-    const int64_t col0 = (int64_t)tn * BN;
+    const int64_t col0 = (int64_t)un.tn * BN;
     const int64_t k0 = (int64_t)sp * a.kslice[c];
     const int64_t k1 = (k0 + a.kslice[c] < K) ? k0 + a.kslice[c] : K;
     const int KT = (int)((k1 - k0 + BK - 1) / BK);
 
-    u32x4 ra[C::AV], rb[C::BV];
-    auto gload = [&](int64_t kk) {
+    // Stage layout in LDS: BM rows of X then BN rows of W, ROWB bytes each,
+    // 16-byte pieces XOR-swizzled.  Load round v of a stage fills LDS slots
+    // [256 v, 256 v + 256) (wave w: 64 slots at m0 = base + 4096 v + 1024 w);
+    // slot s holds row s / CH, piece s % CH, i.e. logical piece
+    // (s % CH) ^ swz(row) of that row.  Thread t always fills slot t of a
+    // round, so its row inside a round, its piece and hence its byte offset
+    // in the operand are fixed; the round and the k position go into the
+    // uniform offset.  Rows past the chunk end or past n read as zero (buffer
+    // size), and so does k past the split's end (per-thread offset moved past
+    // the buffer).
+    const int tr = tid / C::CH;
+    const int tch = (tid % C::CH) ^ C::swz(tr);
+    const int nra = (int)((rowlim - row0 < BM) ? rowlim - row0 : BM);
+    const int nrb = (int)((N - col0 < BN) ? N - col0 : BN);
+    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.x + row0 * K), (short)0, (int)(nra * K * 2), (int)kBufDword3);
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.w + col0 * K), (short)0, (int)(nrb * K * 2), (int)kBufDword3);
+    const int voff = (int)((tr * K + tch * 8) * 2);
+    const uint32_t lds0 = lds_addr(lds) + (uint32_t)(__builtin_amdgcn_readfirstlane(wave) * 1024);
+
+    auto issue = [&](int stage) {
+      const int kk = (int)(k0 + (int64_t)stage * BK);          // uniform
+      const int vo = (kk + tch * 8 < k1) ? voff : 0x40000000;   // k past the end reads zero
+      const uint32_t base = lds0 + (uint32_t)((stage % STAGES) * C::STAGE);
 #pragma unroll
-      for (int v = 0; v < C::AV; ++v) {
-        const int idx = tid + v * NT;
-        const int r = idx >> 3, ch = idx & 7;
-        const int64_t row = row0 + r, kc = kk + ch * 8;
-        if (row < rowlim && kc < k1)
-          ra[v] = *reinterpret_cast<const u32x4 *>(a.x + row * K + kc);
-        else
-          ra[v] = u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int v = 0; v < C::BV; ++v) {
-        const int idx = tid + v * NT;
-        const int r = idx >> 3, ch = idx & 7;
-        const int64_t col = col0 + r, kc = kk + ch * 8;
-        if (col < N && kc < k1)
-          rb[v] = *reinterpret_cast<const u32x4 *>(a.w + col * K + kc);
-        else
-          rb[v] = u32x4{0u, 0u, 0u, 0u};
-      }
-    };
-    auto sstore = [&](int stage) {
-      char *A = lds + stage * C::STAGE;
-      char *B = A + C::A_BYTES;
-#pragma unroll
-      for (int v = 0; v < C::AV; ++v) {
-        const int idx = tid + v * NT;
-        const int r = idx >> 3, ch = idx & 7;
-        *reinterpret_cast<u32x4 *>(A + r * 128 + ((ch ^ (r & 7)) << 4)) = ra[v];
-      }
-#pragma unroll
-      for (int v = 0; v < C::BV; ++v) {
-        const int idx = tid + v * NT;
-        const int r = idx >> 3, ch = idx & 7;
-        *reinterpret_cast<u32x4 *>(B + r * 128 + ((ch ^ (r & 7)) << 4)) = rb[v];
+      for (int v = 0; v < C::V; ++v) {
+        const bool isA = v < C::AV;
+        const int rs = C::RSTEP * (isA ? v : v - C::AV);
+        dma16(base + (uint32_t)(v * 4096), vo, isA ? rsa : rsb, (int)((rs * K + kk) * 2));
       }
     };
 
+    // The first k-step starts the accumulators from an inline zero operand
+    // instead of zero-filled registers: with zero-filled registers the
+    // register allocator shares one zero and cannot keep each MFMA's result in
+    // its accumulator registers, and copies accumulators every k-step.
     f32x4 acc[C::FM][C::FN];
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    gload(k0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < KT) gload(k0 + (int64_t)(kt + 1) * BK);
-      const char *A = lds + cur * C::STAGE;
+    auto compute = [&](auto firstc, int stage) {
+      constexpr bool first = decltype(firstc)::value;
+      const char *A = lds + (stage % STAGES) * C::STAGE;
       const char *B = A + C::A_BYTES;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < C::KS; ++ks) {
         const int ch = ks * 4 + (lane >> 4);
-        const int swz = ((ch ^ (lane & 7)) << 4);
+        const int swz = ((ch ^ C::swz(lane & 15)) << 4);
         bf16x8 af[C::FM], bfr[C::FN];
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-          const int r = wm * C::WTM + i * 16 + (lane & 15);
-          af[i] = *reinterpret_cast<const bf16x8 *>(A + r * 128 + swz);
-        }
+        for (int i = 0; i < C::FM; ++i)
+          af[i] = *reinterpret_cast<const bf16x8 *>(A + (wm * C::WTM + i * 16 + (lane & 15)) * C::ROWB + swz);
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          const int r = wn * C::WTN + j * 16 + (lane & 15);
-          bfr[j] = *reinterpret_cast<const bf16x8 *>(B + r * 128 + swz);
-        }
+        for (int j = 0; j < C::FN; ++j)
+          bfr[j] = *reinterpret_cast<const bf16x8 *>(B + (wn * C::WTN + j * 16 + (lane & 15)) * C::ROWB + swz);
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-          for (int j = 0; j < C::FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < C::FN; ++j) {
+            if (first && ks == 0)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          }
       }
-      if (kt + 1 < KT) sstore(cur ^ 1);
+    };
+
+    // Wait until stage j has landed: the stages issued after it may stay in
+    // flight (each stage is V copies per wave).
+    auto wait_stage = [&](int j) {
+      const int later = ((j + STAGES - 1 < KT) ? j + STAGES - 1 : KT) - (j + 1);
+      if constexpr (STAGES >= 4) { if (later >= 2) { wait_vm<2 * C::V>(); return; } }
+      if constexpr (STAGES >= 3) { if (later >= 1) { wait_vm<C::V>(); return; } }
+      wait_vm<0>();
+    };
+
+    // prologue: stages 0 .. STAGES-2 in flight.  The LDS buffers about to be
+    // filled may still be read by the previous unit's last k-steps.
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p)
+      if (p < KT) issue(p);
+
+    // iteration j: wait for stage j; barrier (stage j visible to every wave,
+    // and every wave is done with stage j-1, whose buffer is refilled next);
+    // issue stage j+STAGES-1; multiply stage j.
+    wait_stage(0);
+    __syncthreads();
+    if (STAGES - 1 < KT) issue(STAGES - 1);
+    compute(std::true_type{}, 0);
+    for (int j = 1; j < KT; ++j) {
+      wait_stage(j);
       __syncthreads();
+      if (j + STAGES - 1 < KT) issue(j + STAGES - 1);
+      compute(std::false_type{}, j);
     }
 
-    bool write_out = true;
-    if (S > 1) {
+    // Output of one 16x16 block: lane holds rows 4*(lane/16)+v, column lane%16.
+    auto store_block = [&](int i, int j, const f32x4 &val) {
+      const int64_t col = col0 + wn * C::WTN + j * 16 + (lane & 15);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t row = row0 + wm * C::WTM + i * 16 + (lane >> 4) * 4 + v;
+        if (row < rowlim && col < N) {
+          if (a.y_bf16)
+            reinterpret_cast<uint16_t *>(a.y)[row * N + col] = f32_to_bf16_rne(val[v]);
+          else
+            reinterpret_cast<float *>(a.y)[row * N + col] = val[v];
+        }
+      }
+    };
+
+    if (S == 1) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) store_block(i, j, acc[i][j]);
+    } else {
       // Deterministic split-K: every split stores its fp32 partial tile; the
       // split that arrives last sums the S partials in split order 0..S-1.
       const int ctr = a.ctr_base[c] + tile;
@@ -230,44 +421,51 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
         s_last = (old == (uint32_t)(S - 1));
       }
       __syncthreads();
-      write_out = s_last != 0;
-      if (write_out) {
+      if (s_last) {
         fence_acquire_agent();
-        f32x4 sum[C::FM][C::FN];
-        for (int q = 0; q < S; ++q) {
-          const f32x4 *p = reinterpret_cast<const f32x4 *>(a.partials + (pbase + q) * (BM * BN));
+        // The whole workgroup sums the tile's S partials in split order; each
+        // thread takes 16-byte pieces t, t + 256, ... of the fragment-ordered
+        // partial tile, four pieces at a time so 4 S loads are in flight.
+        const f32x4 *p0 = reinterpret_cast<const f32x4 *>(a.partials + pbase * (BM * BN));
+        constexpr int PIECES = BM * BN / 4;           // f32x4 pieces per partial tile
+        constexpr int PER = PIECES / NT;              // pieces per thread
+        static_assert(PIECES % NT == 0, "pieces");
+        for (int base = 0; base < PER; base += 4) {
+          f32x4 sum[4];
 #pragma unroll
-          for (int i = 0; i < C::FM; ++i)
+          for (int u = 0; u < 4; ++u)
+            if (base + u < PER) sum[u] = p0[(base + u) * NT + tid];
+          for (int q = 1; q < S; ++q) {
+            f32x4 t[4];
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j) {
-              const f32x4 v = (q == sp) ? acc[i][j] : p[((wave * C::FM + i) * C::FN + j) * 64 + lane];
-              sum[i][j] = (q == 0) ? v : sum[i][j] + v;
-            }
-        }
+            for (int u = 0; u < 4; ++u)
+              if (base + u < PER) t[u] = p0[(size_t)q * PIECES + (base + u) * NT + tid];
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
+            for (int u = 0; u < 4; ++u)
+              if (base + u < PER) sum[u] = sum[u] + t[u];
+          }
 #pragma unroll
-          for (int j = 0; j < C::FN; ++j) acc[i][j] = sum[i][j];
-      }
-    }
-
-    if (write_out) {
+          for (int u = 0; u < 4; ++u) {
+            if (base + u >= PER) continue;
+            // piece index -> (wave, block i, block j, lane) of the MFMA layout
+            const int f = (base + u) * NT + tid;
+            const int ln = f & 63, blk = f >> 6;
+            const int wv = blk / (C::FM * C::FN), ij = blk - wv * (C::FM * C::FN);
+            const int bi = ij / C::FN, bj = ij - bi * C::FN;
+            const int64_t col = col0 + (wv & 1) * C::WTN + bj * 16 + (ln & 15);
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          const int64_t col = col0 + wn * C::WTN + j * 16 + (lane & 15);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int64_t row = row0 + wm * C::WTM + i * 16 + (lane >> 4) * 4 + v;
-            if (row < rowlim && col < N) {
-              if (a.y_bf16)
-                reinterpret_cast<uint16_t *>(a.y)[row * N + col] = f32_to_bf16_rne(acc[i][j][v]);
-              else
-                reinterpret_cast<float *>(a.y)[row * N + col] = acc[i][j][v];
+            for (int v = 0; v < 4; ++v) {
+              const int64_t row = row0 + (wv >> 1) * C::WTM + bi * 16 + (ln >> 4) * 4 + v;
+              if (row < rowlim && col < N) {
+                if (a.y_bf16)
+                  reinterpret_cast<uint16_t *>(a.y)[row * N + col] = f32_to_bf16_rne(sum[u][v]);
+                else
+                  reinterpret_cast<float *>(a.y)[row * N + col] = sum[u][v];
+              }
             }
           }
         }
+      }
     }
 
     // Completion accounting; in GEMM-RS mode the chunk's done flag is released
@@ -291,7 +489,7 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
     const uint32_t e = fetch_add_acq_rel(a.ws32 + WS_EXITED, 1u);
     if (e == (uint32_t)(a.grid - 1)) {
       for (int c = 0; c < a.R; ++c) {
-        a.ws32[WS_CLAIM + c] = 0u;
+        for (int g = 0; g < XCDS; ++g) a.ws32[WS_CLAIM + c * XCDS + g] = 0u;
         a.ws32[WS_CHUNK_DONE + c] = 0u;
         if (a.ctr_base[c] >= 0) {
           const int ntiles = a.units[c] / a.split[c];
@@ -305,19 +503,74 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
   }
 }
 
-TileCfg choose_tile(int64_t mc, int64_t n, int64_t k) {
-  (void)mc; (void)n; (void)k;
-  return TileCfg{128, 128};
+namespace {
+
+struct Cand {
+  int bm, bn, bk, stages;
+};
+
+// Tile configurations compiled into the library.
+constexpr Cand kCands[] = {{256, 256, 32, 4}, {256, 160, 64, 3}, {128, 224, 64, 3}, {128, 128, 64, 4}};
+
+// Relative cost of a tile shape per output element: operand bytes staged per
+// flop fall as 1/BM + 1/BN, so larger tiles run closer to the MFMA rate.
+double tile_eff(int bm, int bn) { return 1.0 / (1.0 + 48.0 / bm + 48.0 / bn); }
+
+bool parse_env_tile(Cand *out) {
+  const char *e = getenv("FO_TILE");
+  if (!e) return false;
+  int bm = 0, bn = 0;
+  if (sscanf(e, "%dx%d", &bm, &bn) != 2) return false;
+  for (const Cand &c : kCands)
+    if (c.bm == bm && c.bn == bn) { *out = c; return true; }
+  return false;
+}
+
+}  // namespace
+
+TileCfg choose_tile(int64_t mc, int64_t n, int64_t k, int R, int grid, bool leave_room) {
+  (void)k;
+  Cand pick{};
+  if (parse_env_tile(&pick) && !(leave_room && pick.bm == 256 && pick.bn == 256))
+    return TileCfg{pick.bm, pick.bn, pick.stages};
+  if (grid < 1) grid = 1;
+  double best = 0;
+  bool have = false;
+  for (const Cand &c : kCands) {
+    // the 256 x 256 tile takes the whole register file of each SIMD: with
+    // arrival flags a one-wave emulator kernel must still fit beside it
+    if (leave_room && c.bm == 256 && c.bn == 256) continue;
+    const int64_t tiles = ((mc + c.bm - 1) / c.bm) * ((n + c.bn - 1) / c.bn) * R;
+    const int64_t waves = (tiles + grid - 1) / grid;
+    const double cost = (double)waves * c.bm * c.bn / tile_eff(c.bm, c.bn);
+    if (!have || cost < best) { best = cost; pick = c; have = true; }
+  }
+  return TileCfg{pick.bm, pick.bn, pick.stages};
+}
+
+void max_tile_dims(int *bm, int *bn) {
+  int m = 0, n = 0;
+  for (const Cand &c : kCands) {
+    if (c.bm > m) m = c.bm;
+    if (c.bn > n) n = c.bn;
+  }
+  *bm = m;
+  *bn = n;
 }
 
 size_t partial_slot_bytes(const TileCfg &t) { return (size_t)t.bm * t.bn * sizeof(float); }
 
 hipError_t launch_gemm(const GemmArgs &a, const TileCfg &t, hipStream_t stream) {
-  if (t.bm == 128 && t.bn == 128) {
-    hipLaunchKernelGGL((gemm_kernel<128, 128>), dim3(a.grid), dim3(NT), 0, stream, a);
-  } else {
+  if (t.bm == 256 && t.bn == 256)
+    hipLaunchKernelGGL((gemm_kernel<256, 256, 32, 4>), dim3(a.grid), dim3(NT), 0, stream, a);
+  else if (t.bm == 256 && t.bn == 160)
+    hipLaunchKernelGGL((gemm_kernel<256, 160, 64, 3>), dim3(a.grid), dim3(NT), 0, stream, a);
+  else if (t.bm == 128 && t.bn == 224)
+    hipLaunchKernelGGL((gemm_kernel<128, 224, 64, 3>), dim3(a.grid), dim3(NT), 0, stream, a);
+  else if (t.bm == 128 && t.bn == 128)
+    hipLaunchKernelGGL((gemm_kernel<128, 128, 64, 4>), dim3(a.grid), dim3(NT), 0, stream, a);
+  else
     return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }
 

@@ -4,24 +4,25 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/flashoverlap.h"
+#include "flashoverlap.h"
 
 namespace fo {
 
 // Workspace layout (32-bit words from the start of the workspace).  Every
-// counter is returned to zero by the kernel that observes its final value, so
-// the workspace is zero again after each completed call.
-constexpr int WS_CLAIM = 0;                  // [FO_MAX_CHUNKS] unit claim counters
-constexpr int WS_CHUNK_DONE = 64;            // [FO_MAX_CHUNKS] finished units per chunk
-constexpr int WS_TOTAL_DONE = 128;           // finished units, all chunks
-constexpr int WS_EXITED = 129;               // workgroups that have left the loop
-constexpr int WS_ABORT = 130;                // set when a wait timed out
-constexpr int WS_TILE_CTR = 256;             // split-K arrival counters, one per tile
-constexpr size_t WS_HEADER_BYTES = 1024;     // bytes before the tile counters
+// counter is returned to zero by the last workgroup to leave the kernel, so
+// the counters are zero again after each completed call.
+constexpr int XCDS = 8;                      // work-queue groups (one per XCD)
+constexpr int WS_CLAIM = 0;                  // [FO_MAX_CHUNKS][XCDS] unit claim counters
+constexpr int WS_CHUNK_DONE = 512;           // [FO_MAX_CHUNKS] finished units per chunk
+constexpr int WS_TOTAL_DONE = 576;           // finished units, all chunks
+constexpr int WS_EXITED = 577;               // workgroups that have left the loop
+constexpr int WS_ABORT = 578;                // set when a wait timed out
+constexpr int WS_TILE_CTR = 1024;            // split-K arrival counters, one per tile
+constexpr size_t WS_HEADER_BYTES = 4096;     // bytes before the tile counters
 
-// Output tile of one workgroup and k depth of one LDS stage.
+// Output tile of one workgroup and the depth of its LDS stage ring.
 struct TileCfg {
-  int bm, bn;
+  int bm, bn, stages;
 };
 
 struct GemmArgs {
@@ -33,6 +34,8 @@ struct GemmArgs {
   int64_t m, n, k;
   int32_t R, mc;              // chunks, rows per chunk
   int32_t tiles_m, tiles_n;   // tiles per chunk
+  int32_t gm, gn;             // each chunk's tile grid is cut into gm x gn rectangles
+  int32_t gtiles[XCDS];       // tiles per rectangle (work-queue group)
   int32_t local;
   int32_t strict;
   int32_t total_units;
@@ -70,8 +73,10 @@ struct ReduceArgs {
 };
 
 // Tile configuration chosen for a problem (host).
-TileCfg choose_tile(int64_t mc, int64_t n, int64_t k);
+TileCfg choose_tile(int64_t mc, int64_t n, int64_t k, int R, int grid, bool leave_room);
 size_t partial_slot_bytes(const TileCfg &t);
+// Largest tile area any configuration can use (bounds the partial-tile area).
+void max_tile_dims(int *bm, int *bn);
 
 hipError_t launch_gemm(const GemmArgs &a, const TileCfg &t, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs &a, int grid, hipStream_t stream);
