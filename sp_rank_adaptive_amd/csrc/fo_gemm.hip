@@ -39,6 +39,7 @@ namespace fo {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NT = 256;   // threads per workgroup
 constexpr uint32_t kBufDword3 = 0x00020000u;   // raw buffer, 32-bit data format (gfx9)
@@ -327,30 +328,49 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
     // register allocator shares one zero and cannot keep each MFMA's result in
     // its accumulator registers, and copies accumulators every k-step.
     f32x4 acc[C::FM][C::FN];
-    auto compute = [&](auto firstc, int stage) {
+    // One stage: read every fragment of k-step 0, then issue k-step 0's MFMAs
+    // interleaved with the fragment reads of k-step 1, then k-step 1's MFMAs.
+    // The schedule is pinned: left alone, the scheduler reuses one register
+    // quad for all X fragments and waits for each read before its MFMAs.
+    auto compute = [&](auto firstc, auto bufc) {
       constexpr bool first = decltype(firstc)::value;
-      const char *A = lds + (stage % STAGES) * C::STAGE;
+      constexpr int buf = decltype(bufc)::value;
+      const char *A = lds + buf * C::STAGE;
       const char *B = A + C::A_BYTES;
+      bf16x8 af[C::KS][C::FM], bfr[C::KS][C::FN];
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         const int ch = ks * 4 + (lane >> 4);
         const int swz = ((ch ^ C::swz(lane & 15)) << 4);
-        bf16x8 af[C::FM], bfr[C::FN];
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
-          af[i] = *reinterpret_cast<const bf16x8 *>(A + (wm * C::WTM + i * 16 + (lane & 15)) * C::ROWB + swz);
+          af[ks][i] = *reinterpret_cast<const bf16x8 *>(A + (wm * C::WTM + i * 16 + (lane & 15)) * C::ROWB + swz);
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8 *>(B + (wn * C::WTN + j * 16 + (lane & 15)) * C::ROWB + swz);
+          bfr[ks][j] = *reinterpret_cast<const bf16x8 *>(B + (wn * C::WTN + j * 16 + (lane & 15)) * C::ROWB + swz);
+      }
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
           for (int j = 0; j < C::FN; ++j) {
             if (first && ks == 0)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][i], bfr[ks][j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
             else
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
           }
+      // pinned order (mask 0x100: LDS reads, 0x008: MFMA)
+      constexpr int NF = C::FM + C::FN, NM = C::FM * C::FN;
+      __builtin_amdgcn_sched_group_barrier(0x100, NF, 0);
+      if constexpr (C::KS == 2) {
+        static_for<NF>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        });
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NM - NF, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
       }
     };
 
@@ -372,16 +392,24 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
 
     // iteration j: wait for stage j; barrier (stage j visible to every wave,
     // and every wave is done with stage j-1, whose buffer is refilled next);
-    // issue stage j+STAGES-1; multiply stage j.
+    // issue stage j+STAGES-1; multiply stage j (LDS buffer j % STAGES).
+    // Iteration 0 is peeled; the rest are unrolled STAGES at a time so each
+    // buffer offset is a constant.
     wait_stage(0);
     __syncthreads();
     if (STAGES - 1 < KT) issue(STAGES - 1);
-    compute(std::true_type{}, 0);
-    for (int j = 1; j < KT; ++j) {
-      wait_stage(j);
-      __syncthreads();
-      if (j + STAGES - 1 < KT) issue(j + STAGES - 1);
-      compute(std::false_type{}, j);
+    compute(std::true_type{}, std::integral_constant<int, 0>{});
+    for (int j0 = 1; j0 < KT; j0 += STAGES) {
+      static_for<STAGES>([&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        const int j = j0 + p;
+        if (j < KT) {
+          wait_stage(j);
+          __syncthreads();
+          if (j + STAGES - 1 < KT) issue(j + STAGES - 1);
+          compute(std::false_type{}, std::integral_constant<int, (1 + p) % STAGES>{});
+        }
+      });
     }
 
     // Output of one 16x16 block: lane holds rows 4*(lane/16)+v, column lane%16.
@@ -400,10 +428,56 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
     };
 
     if (S == 1) {
+      // Stage the tile in LDS (the stage ring is idle now) so every lane
+      // writes 16-byte row pieces; a tile too large for LDS goes in two row
+      // halves (the waves of one half write their quadrants each pass).
+      // padded fp32 row (spreads the staging writes over banks) when it fits
+      constexpr int SROW = (BM / 2 * (BN + 4) * 4 <= C::LDS) ? BN + 4 : BN;
+      constexpr int HALVES = (BM * SROW * 4 <= C::LDS) ? 1 : 2;
+      static_assert(BM / HALVES * SROW * 4 <= C::LDS, "epilogue staging");
+      constexpr int HROWS = BM / HALVES;
+      constexpr int CPR = BN / 4;                                   // 16-byte pieces per row
+      float *stg = reinterpret_cast<float *>(lds);
+      const bool vec_ok = ((N & 3) == 0) && (!a.y_bf16 || (N & 3) == 0);
 #pragma unroll
-      for (int i = 0; i < C::FM; ++i)
+      for (int h = 0; h < HALVES; ++h) {
+        __syncthreads();
+        if (HALVES == 1 || wm == h) {
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j) store_block(i, j, acc[i][j]);
+          for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const int r = (HALVES == 1 ? wm * C::WTM : 0) + i * 16 + (lane >> 4) * 4 + v;
+                stg[r * SROW + wn * C::WTN + j * 16 + (lane & 15)] = acc[i][j][v];
+              }
+        }
+        __syncthreads();
+        for (int cidx = tid; cidx < HROWS * CPR; cidx += NT) {
+          const int r = cidx / CPR, cc = cidx - (cidx / CPR) * CPR;
+          const int64_t row = row0 + h * HROWS + r;
+          const int64_t col = col0 + cc * 4;
+          if (row >= rowlim || col >= N) continue;
+          const f32x4 val = *reinterpret_cast<const f32x4 *>(stg + r * SROW + cc * 4);
+          if (vec_ok && col + 4 <= N) {
+            if (a.y_bf16) {
+              const uint32_t lo = (uint32_t)f32_to_bf16_rne(val[0]) | ((uint32_t)f32_to_bf16_rne(val[1]) << 16);
+              const uint32_t hi = (uint32_t)f32_to_bf16_rne(val[2]) | ((uint32_t)f32_to_bf16_rne(val[3]) << 16);
+              *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.y) + row * N + col) = u32x2{lo, hi};
+            } else {
+              *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.y) + row * N + col) = val;
+            }
+          } else {
+            for (int e = 0; e < 4 && col + e < N; ++e) {
+              if (a.y_bf16)
+                reinterpret_cast<uint16_t *>(a.y)[row * N + col + e] = f32_to_bf16_rne(val[e]);
+              else
+                reinterpret_cast<float *>(a.y)[row * N + col + e] = val[e];
+            }
+          }
+        }
+      }
     } else {
       // Deterministic split-K: every split stores its fp32 partial tile; the
       // split that arrives last sums the S partials in split order 0..S-1.
