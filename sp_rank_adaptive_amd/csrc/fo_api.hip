@@ -103,6 +103,7 @@ struct GemmPlan {
   int tiles_m, tiles_n, tiles;
   int kt_total;
   size_t counter_bytes, partial_offset, total_bytes;
+  int ready_off;
 };
 
 // Workspace bound over every tile configuration the library may pick.
@@ -114,7 +115,8 @@ GemmPlan plan_workspace(int64_t m, int64_t n, int64_t k, int R) {
   const int64_t most_tiles = ((p.mc + 127) / 128) * ((n + 127) / 128);      // smallest tiles
   const int64_t padded = ((p.mc + bm - 1) / bm * bm) * ((n + bn - 1) / bn * bn);
   (void)k;
-  p.counter_bytes = WS_HEADER_BYTES + (size_t)R * most_tiles * sizeof(uint32_t);
+  p.ready_off = (int)(WS_TILE_CTR + R * most_tiles);
+  p.counter_bytes = WS_HEADER_BYTES + 2 * (size_t)R * most_tiles * sizeof(uint32_t);
   p.partial_offset = (p.counter_bytes + 255) & ~(size_t)255;
   p.total_bytes = p.partial_offset + (size_t)kMaxSplit * padded * sizeof(float);
   return p;
@@ -231,6 +233,7 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
     a.split[c] = sk;
     a.kslice[c] = kt_per * 64;
     a.units[c] = p.tiles * sk;
+    a.red_units[c] = sk > 1 ? p.tiles * RED_SLICES : 0;
     if (sk > 1) {
       a.ctr_base[c] = (int32_t)ctr_used;
       a.part_base[c] = (int32_t)part_used;
@@ -240,8 +243,9 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
       a.ctr_base[c] = -1;
       a.part_base[c] = -1;
     }
-    total_units += a.units[c];
+    total_units += a.units[c] + a.red_units[c];
   }
+  a.ready_off = p.ready_off;
   if (part_used > 0 && ws_bytes < p.partial_offset + part_used * partial_slot_bytes(p.tile))
     return FO_ERR_WORKSPACE;
   if (total_units > (int64_t)1 << 30) return FO_ERR_SHAPE;

@@ -48,6 +48,17 @@ __device__ __forceinline__ uint32_t fetch_add_relaxed(uint32_t *p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ void store_relaxed_agent(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t load_relaxed_agent(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// On gfx950 an agent-scope release fence writes the XCD's L2 back to memory
+// and an acquire fence invalidates it: both are paid by every workgroup on
+// the XCD, so the kernels fence only where data actually changes hands.
 __device__ __forceinline__ void fence_release_agent() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
 }

@@ -106,8 +106,9 @@ struct ClaimState {
 struct Unit {
   int c;      // chunk, -1 finished, -2 abort
   int tm, tn; // tile row / column inside the chunk
-  int sp;     // split index
+  int sp;     // split index, or the row slice of a reduce unit
   int first;  // 1 for the first unit of group 0 (chunk start stamp)
+  int red;    // 1: reduce unit (sum a split tile's partials over one row slice)
 };
 
 __device__ __forceinline__ uint32_t group_units(const GemmArgs &a, int c, int g) {
@@ -128,77 +129,85 @@ __device__ __forceinline__ void group_tile(const GemmArgs &a, int g, int tl, int
 }
 
 // Wave 0 of a workgroup picks the next unit (all 64 lanes call this).
-// One round trip reads every arrival flag and every (chunk, group) claim
-// counter in parallel across the lanes; the workgroup then takes the first
-// chunk in priority order that has landed and has work (its own XCD's group
-// if that has work, else the group with the most left) with one fetch-add.
+// One round trip reads every arrival flag and every claim counter in
+// parallel across the lanes; then a scan in priority order takes the first
+// chunk that has landed and has work: a GEMM unit (its own XCD's group if
+// that has work, else the group with the most left) with one fetch-add, or,
+// once every GEMM unit of a split chunk is claimed, one of its reduce units.
+// A reduce unit may be claimed before its tile is published; it then waits
+// for a split that is already running, never for unclaimed work.
 // STRICT mode only looks at the first chunk in order that still has work.
 __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_hint) {
   const int lane = threadIdx.x & 63;
   const int R = a.R;
   uint64_t wait_from = 0;
-  Unit r{-1, 0, 0, 0, 0};
+  Unit r{-1, 0, 0, 0, 0, 0};
   for (;;) {
-    // landed[s]: chunk order[s] usable
-    uint64_t landed = 0;
-    {
-      bool ok = false;
-      if (lane < R) {
-        const int c = a.order[lane];
-        ok = a.arrived == nullptr || c == a.local ||
-             epoch_reached(load_relaxed(a.arrived + c), a.epoch);
-      }
-      landed = __ballot(ok);
+    // landed[s]: chunk order[s] usable; red[s]: split chunk with reduce units left
+    bool ok = false, redp = false;
+    if (lane < R) {
+      const int c = a.order[lane];
+      ok = a.arrived == nullptr || c == a.local ||
+           epoch_reached(load_relaxed(a.arrived + c), a.epoch);
+      if (a.red_units[c] > 0) redp = load_relaxed(a.ws32 + WS_RED_CLAIM + c) < (uint32_t)a.red_units[c];
     }
-    // remaining work per (order position, group): 8 groups per position
-    uint32_t rem_own = 0, best_rem = 0;
-    int pick_s = -1, pick_g = -1;
-    uint64_t has_work = 0;   // bit s: position s has work in some group
-    for (int base = 0; base < R * XCDS; base += 64) {
-      const int pidx = base + lane;
-      uint32_t left = 0;
+    const uint64_t landed = __ballot(ok);
+    const uint64_t red_left = __ballot(redp);
+    // GEMM units left per (order position, group), 8 positions per batch
+    uint64_t gmask[FO_MAX_CHUNKS / 8];
+    uint32_t left[FO_MAX_CHUNKS / 8];
+    const int nb = (R + 7) / 8;
+    uint64_t has_work = 0;
+    for (int b = 0; b < nb; ++b) {
+      const int pidx = b * 64 + lane;
+      uint32_t lv = 0;
       if (pidx < R * XCDS) {
         const int sidx = pidx / XCDS, g = pidx % XCDS;
         const int c = a.order[sidx];
         const uint32_t cnt = load_relaxed(a.ws32 + WS_CLAIM + c * XCDS + g);
         const uint32_t tot = group_units(a, c, g);
-        left = cnt < tot ? tot - cnt : 0;
+        lv = cnt < tot ? tot - cnt : 0;
       }
-      const uint64_t m = __ballot(left > 0);
-      for (uint64_t mm = m; mm; mm &= mm - 1) has_work |= 1ull << ((base + __builtin_ctzll(mm)) / XCDS);
-      // first eligible position in this batch
-      for (int sidx = base / XCDS; sidx < (base + 64) / XCDS && sidx < R && pick_s < 0; ++sidx) {
-        const uint64_t gm = (m >> (sidx * XCDS - base)) & 0xFFull;
-        if (!gm) continue;
+      left[b] = lv;
+      gmask[b] = __ballot(lv > 0);
+      for (uint64_t mm = gmask[b]; mm; mm &= mm - 1) has_work |= 1ull << (b * 8 + __builtin_ctzll(mm) / XCDS);
+    }
+    int pick_s = -1, pick_g = -1, pick_red = 0;
+    for (int sidx = 0; sidx < R; ++sidx) {
+      const int b = sidx / 8;
+      const uint64_t gm = (gmask[b] >> ((sidx % 8) * XCDS)) & 0xFFull;
+      const bool redw = ((red_left >> sidx) & 1) && gm == 0;
+      if (!gm && !redw) continue;
+      const bool is_landed = (landed >> sidx) & 1;
+      if (!is_landed) {
+        if (a.strict) break;   // strict: the first chunk with work decides
+        continue;
+      }
+      if (gm) {
         // first claim of a workgroup: the q-th workgroup of an XCD skips the
         // first q units its XCD's group has left (in priority order over
         // landed chunks), so the XCD's workgroups start on distinct units
-        // instead of racing for the first chunk's few
-        if (rank_hint >= 0 && !a.strict && ((landed >> sidx) & 1) && ((gm >> xg) & 1)) {
-          const uint32_t own = __shfl(left, sidx * XCDS - base + xg);
+        if (rank_hint >= 0 && !a.strict && ((gm >> xg) & 1)) {
+          const uint32_t own = __shfl(left[b], (sidx % 8) * XCDS + xg);
           if ((uint32_t)rank_hint >= own) { rank_hint -= (int)own; continue; }
-        }
-        if (a.strict) {
-          // strict: the first position with work decides, landed or not
-          if (!((landed >> sidx) & 1)) { pick_s = -2; break; }
-        } else if (!((landed >> sidx) & 1)) {
-          continue;
         }
         pick_s = sidx;
         if ((gm >> xg) & 1) {
           pick_g = xg;
         } else {
-          // the group with the most work left
+          uint32_t best = 0;
           for (uint64_t g2 = gm; g2; g2 &= g2 - 1) {
             const int g = __builtin_ctzll(g2);
-            const uint32_t lv = __shfl(left, sidx * XCDS - base + g);
-            if (lv > best_rem) { best_rem = lv; pick_g = g; }
+            const uint32_t lv = __shfl(left[b], (sidx % 8) * XCDS + g);
+            if (lv > best) { best = lv; pick_g = g; }
           }
         }
+      } else {
+        pick_s = sidx;
+        pick_red = 1;
       }
-      if (pick_s != -1) break;
+      break;
     }
-    (void)rem_own;
     if (pick_s < 0 && rank_hint >= 0) {   // fewer units than workgroups: normal claim
       rank_hint = -1;
       continue;
@@ -211,6 +220,50 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
         if (a.arrived != nullptr && c != a.local) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
         st.acquired |= 1ull << c;
       }
+      if (pick_red) {
+        uint32_t v = 0;
+        if (lane == 0) v = fetch_add_relaxed(a.ws32 + WS_RED_CLAIM + c, 1u);
+        v = __builtin_amdgcn_readfirstlane(v);
+        if (v >= (uint32_t)a.red_units[c]) continue;   // all taken: look again
+        // wait for the v / RED_SLICES-th tile of the chunk to be published
+        uint32_t e = 0;
+        if (lane == 0) {
+          const uint32_t *slot = a.ws32 + a.ready_off + a.ctr_base[c] + v / RED_SLICES;
+          const uint64_t t0 = now_ticks();
+          while ((e = load_relaxed(slot)) == 0u) {
+            if (load_relaxed(a.ws32 + WS_ABORT) || now_ticks() - t0 > a.timeout_ticks) break;
+            __builtin_amdgcn_s_sleep(2);
+          }
+        }
+        e = __builtin_amdgcn_readfirstlane(e);
+        if (e == 0u) {   // abort or timeout while waiting
+          if (lane == 0) {
+            if (a.status) __hip_atomic_store(a.status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_SYSTEM);
+            __hip_atomic_store(a.ws32 + WS_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          r.c = -2;
+          return r;
+        }
+        const int tile = (int)e - 1;
+        // The tile counter reads S only after all S splits counted themselves;
+        // reading it, then an acquire fence, orders this unit's reads of the
+        // partials after every split's release fence.
+        if (lane == 0) {
+          const uint32_t *ctr = a.ws32 + WS_TILE_CTR + a.ctr_base[c] + tile;
+          const uint64_t t0 = now_ticks();   // bounded like every other wait
+          while (load_relaxed_agent(ctr) < (uint32_t)a.split[c] && now_ticks() - t0 <= a.timeout_ticks)
+            __builtin_amdgcn_s_sleep(1);
+        }
+        fence_acquire_agent();
+        r.c = c;
+        r.tm = tile / a.tiles_n;
+        r.tn = tile - r.tm * a.tiles_n;
+        r.sp = (int)(v % RED_SLICES);
+        r.first = 0;
+        r.red = 1;
+        return r;
+      }
       uint32_t u = 0;
       if (lane == 0) u = fetch_add_relaxed(a.ws32 + WS_CLAIM + c * XCDS + pick_g, 1u);
       u = __builtin_amdgcn_readfirstlane(u);
@@ -221,11 +274,12 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
         r.sp = (int)u - tl * S;
         group_tile(a, pick_g, tl, r.tm, r.tn);
         r.first = (pick_g == 0 && u == 0);
+        r.red = 0;
         return r;
       }
       continue;   // lost the race for the last unit: look again
     }
-    if (has_work == 0) { r.c = -1; return r; }   // every chunk fully claimed
+    if (has_work == 0 && red_left == 0) { r.c = -1; return r; }   // every unit claimed
     // work left only in chunks that have not landed: wait
     if (load_relaxed(a.ws32 + WS_ABORT)) { r.c = -2; return r; }
     const uint64_t t = now_ticks();
@@ -276,6 +330,7 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
     un.tm = __builtin_amdgcn_readfirstlane(un.tm);
     un.tn = __builtin_amdgcn_readfirstlane(un.tn);
     un.sp = __builtin_amdgcn_readfirstlane(un.sp);
+    un.red = __builtin_amdgcn_readfirstlane(un.red);
     const int c = un.c;
     if (c < 0) break;
     if (un.first && tid == 0 && a.stamps) store_u64_relaxed(a.stamps + c, now_ticks());
@@ -289,6 +344,56 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
     const int64_t k0 = (int64_t)sp * a.kslice[c];
     const int64_t k1 = (k0 + a.kslice[c] < K) ? k0 + a.kslice[c] : K;
     const int KT = (int)((k1 - k0 + BK - 1) / BK);
+
+    // Output piece writer: 4 consecutive fp32 values at (row, col) of a
+    // row-major destination with leading dimension ld, stored as fp32 or bf16
+    // (round to nearest even), masked to ncols columns.
+    auto put4 = [&](char *base, int64_t ld, int64_t row, int64_t col, int64_t ncols, bool bf16,
+                    bool vec_ok, const f32x4 &val) {
+      if (vec_ok && col + 4 <= ncols) {
+        if (bf16) {
+          const uint32_t lo = (uint32_t)f32_to_bf16_rne(val[0]) | ((uint32_t)f32_to_bf16_rne(val[1]) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16_rne(val[2]) | ((uint32_t)f32_to_bf16_rne(val[3]) << 16);
+          *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(base) + row * ld + col) = u32x2{lo, hi};
+        } else {
+          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(base) + row * ld + col) = val;
+        }
+      } else {
+        for (int e = 0; e < 4 && col + e < ncols; ++e) {
+          if (bf16)
+            reinterpret_cast<uint16_t *>(base)[row * ld + col + e] = f32_to_bf16_rne(val[e]);
+          else
+            reinterpret_cast<float *>(base)[row * ld + col + e] = val[e];
+        }
+      }
+    };
+
+    if (un.red) {
+      // Reduce unit: row slice sp of a split tile whose S partials are all
+      // written; sum them in split order 0..S-1 and store the output rows.
+      const size_t pbase = (size_t)a.part_base[c] + (size_t)tile * S;
+      const float *P = a.partials + pbase * (size_t)(BM * BN);
+      constexpr int ROWS = BM / RED_SLICES;
+      constexpr int PPR = BN / 4;                       // pieces per row
+      static_assert(BM % RED_SLICES == 0, "slices");
+      const int r0 = un.sp * ROWS;
+      const bool vec_ok = (N & 3) == 0;
+      for (int pc = tid; pc < ROWS * PPR; pc += NT) {
+        const int rr = r0 + pc / PPR, cc = pc - (pc / PPR) * PPR;
+        const size_t off = (size_t)rr * BN + (size_t)cc * 4;
+        f32x4 t[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (q < S) t[q] = *reinterpret_cast<const f32x4 *>(P + (size_t)q * (BM * BN) + off);
+        f32x4 sum = t[0];
+#pragma unroll
+        for (int q = 1; q < 8; ++q)
+          if (q < S) sum = sum + t[q];
+        const int64_t row = row0 + rr;
+        if (row < rowlim && col0 + cc * 4 < N)
+          put4(reinterpret_cast<char *>(a.y), N, row, col0 + cc * 4, N, a.y_bf16 != 0, vec_ok, sum);
+      }
+    } else {
 
     // Stage layout in LDS: BM rows of X then BN rows of W, ROWB bytes each,
     // 16-byte pieces XOR-swizzled.  Load round v of a stage fills LDS slots
@@ -412,25 +517,13 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
       });
     }
 
-    // Output of one 16x16 block: lane holds rows 4*(lane/16)+v, column lane%16.
-    auto store_block = [&](int i, int j, const f32x4 &val) {
-      const int64_t col = col0 + wn * C::WTN + j * 16 + (lane & 15);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t row = row0 + wm * C::WTM + i * 16 + (lane >> 4) * 4 + v;
-        if (row < rowlim && col < N) {
-          if (a.y_bf16)
-            reinterpret_cast<uint16_t *>(a.y)[row * N + col] = f32_to_bf16_rne(val[v]);
-          else
-            reinterpret_cast<float *>(a.y)[row * N + col] = val[v];
-        }
-      }
-    };
-
-    if (S == 1) {
-      // Stage the tile in LDS (the stage ring is idle now) so every lane
-      // writes 16-byte row pieces; a tile too large for LDS goes in two row
-      // halves (the waves of one half write their quadrants each pass).
+    // Epilogue: stage the tile in LDS (the stage ring is idle now) so every
+    // lane writes 16-byte row pieces; a tile too large for LDS goes in two
+    // row halves (the waves of one half write their quadrants each pass).
+    // Unsplit: the tile goes to the output.  Split: the fp32 partial goes to
+    // its workspace slot (row-major BM x BN); the split that completes the
+    // tile publishes it for the reduce units.
+    {
       // padded fp32 row (spreads the staging writes over banks) when it fits
       constexpr int SROW = (BM / 2 * (BN + 4) * 4 <= C::LDS) ? BN + 4 : BN;
       constexpr int HALVES = (BM * SROW * 4 <= C::LDS) ? 1 : 2;
@@ -438,7 +531,14 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
       constexpr int HROWS = BM / HALVES;
       constexpr int CPR = BN / 4;                                   // 16-byte pieces per row
       float *stg = reinterpret_cast<float *>(lds);
-      const bool vec_ok = ((N & 3) == 0) && (!a.y_bf16 || (N & 3) == 0);
+      const bool to_out = (S == 1);
+      char *dbase = to_out ? reinterpret_cast<char *>(a.y)
+                           : reinterpret_cast<char *>(a.partials + ((size_t)a.part_base[c] + (size_t)tile * S + sp) * (size_t)(BM * BN));
+      const int64_t ld = to_out ? N : BN;
+      const int64_t rbase = to_out ? row0 : 0, cbase = to_out ? col0 : 0;
+      const int64_t rlim = to_out ? rowlim : BM, clim = to_out ? N : BN;
+      const bool vec_ok = to_out ? (N & 3) == 0 : true;
+      const bool bf = to_out && a.y_bf16;
 #pragma unroll
       for (int h = 0; h < HALVES; ++h) {
         __syncthreads();
@@ -456,123 +556,78 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
         __syncthreads();
         for (int cidx = tid; cidx < HROWS * CPR; cidx += NT) {
           const int r = cidx / CPR, cc = cidx - (cidx / CPR) * CPR;
-          const int64_t row = row0 + h * HROWS + r;
-          const int64_t col = col0 + cc * 4;
-          if (row >= rowlim || col >= N) continue;
+          const int64_t row = rbase + h * HROWS + r;
+          const int64_t col = cbase + cc * 4;
+          if (row >= rlim || col >= clim) continue;
           const f32x4 val = *reinterpret_cast<const f32x4 *>(stg + r * SROW + cc * 4);
-          if (vec_ok && col + 4 <= N) {
-            if (a.y_bf16) {
-              const uint32_t lo = (uint32_t)f32_to_bf16_rne(val[0]) | ((uint32_t)f32_to_bf16_rne(val[1]) << 16);
-              const uint32_t hi = (uint32_t)f32_to_bf16_rne(val[2]) | ((uint32_t)f32_to_bf16_rne(val[3]) << 16);
-              *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.y) + row * N + col) = u32x2{lo, hi};
-            } else {
-              *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.y) + row * N + col) = val;
-            }
-          } else {
-            for (int e = 0; e < 4 && col + e < N; ++e) {
-              if (a.y_bf16)
-                reinterpret_cast<uint16_t *>(a.y)[row * N + col + e] = f32_to_bf16_rne(val[e]);
-              else
-                reinterpret_cast<float *>(a.y)[row * N + col + e] = val[e];
-            }
-          }
+          put4(dbase, ld, row, col, clim, bf, vec_ok, val);
         }
       }
-    } else {
-      // Deterministic split-K: every split stores its fp32 partial tile; the
-      // split that arrives last sums the S partials in split order 0..S-1.
-      const int ctr = a.ctr_base[c] + tile;
-      const size_t pbase = (size_t)a.part_base[c] + (size_t)tile * S;
-      f32x4 *mine = reinterpret_cast<f32x4 *>(a.partials + (pbase + sp) * (BM * BN));
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) mine[((wave * C::FM + i) * C::FN + j) * 64 + lane] = acc[i][j];
-      fence_release_agent();
-      __syncthreads();
-      if (tid == 0) {
-        const uint32_t old = fetch_add_acq_rel(a.ws32 + WS_TILE_CTR + ctr, 1u);
-        s_last = (old == (uint32_t)(S - 1));
-      }
-      __syncthreads();
-      if (s_last) {
-        fence_acquire_agent();
-        // The whole workgroup sums the tile's S partials in split order; each
-        // thread takes 16-byte pieces t, t + 256, ... of the fragment-ordered
-        // partial tile, four pieces at a time so 4 S loads are in flight.
-        const f32x4 *p0 = reinterpret_cast<const f32x4 *>(a.partials + pbase * (BM * BN));
-        constexpr int PIECES = BM * BN / 4;           // f32x4 pieces per partial tile
-        constexpr int PER = PIECES / NT;              // pieces per thread
-        static_assert(PIECES % NT == 0, "pieces");
-        for (int base = 0; base < PER; base += 4) {
-          f32x4 sum[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (base + u < PER) sum[u] = p0[(base + u) * NT + tid];
-          for (int q = 1; q < S; ++q) {
-            f32x4 t[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (base + u < PER) t[u] = p0[(size_t)q * PIECES + (base + u) * NT + tid];
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              if (base + u < PER) sum[u] = sum[u] + t[u];
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if (base + u >= PER) continue;
-            // piece index -> (wave, block i, block j, lane) of the MFMA layout
-            const int f = (base + u) * NT + tid;
-            const int ln = f & 63, blk = f >> 6;
-            const int wv = blk / (C::FM * C::FN), ij = blk - wv * (C::FM * C::FN);
-            const int bi = ij / C::FN, bj = ij - bi * C::FN;
-            const int64_t col = col0 + (wv & 1) * C::WTN + bj * 16 + (ln & 15);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int64_t row = row0 + (wv >> 1) * C::WTM + bi * 16 + (ln >> 4) * 4 + v;
-              if (row < rowlim && col < N) {
-                if (a.y_bf16)
-                  reinterpret_cast<uint16_t *>(a.y)[row * N + col] = f32_to_bf16_rne(sum[u][v]);
-                else
-                  reinterpret_cast<float *>(a.y)[row * N + col] = sum[u][v];
-              }
-            }
+      if (!to_out) {
+        // Publish the partial: write it back past this XCD's L2, then count
+        // the split.  The split that completes the tile lists it for the
+        // reduce units; they order their reads after the release fences of
+        // all S splits through the tile counter (see the reduce unit).
+        fence_release_agent();
+        __syncthreads();
+        if (tid == 0) {
+          const uint32_t old = fetch_add_relaxed(a.ws32 + WS_TILE_CTR + a.ctr_base[c] + tile, 1u);
+          if (old == (uint32_t)(S - 1)) {
+            const uint32_t idx = fetch_add_relaxed(a.ws32 + WS_RED_READY + c, 1u);
+            store_relaxed_agent(a.ws32 + a.ready_off + a.ctr_base[c] + idx, (uint32_t)(tile + 1));
           }
         }
       }
     }
+    }   // GEMM unit
 
-    // Completion accounting; in GEMM-RS mode the chunk's done flag is released
-    // after every output element of the chunk is stored.
+    // Completion accounting.  In GEMM-RS mode the chunk's done flag is
+    // released after every output element of the chunk is stored: each unit
+    // writes its stores back (release fence) before it counts itself, and
+    // the unit that completes the chunk acquires before releasing the flag.
+    // Without done flags the counters only feed the stamps: no fences.
     if (a.done_flags) fence_release_agent();
     __syncthreads();
     if (tid == 0) {
-      const uint32_t d = fetch_add_acq_rel(a.ws32 + WS_CHUNK_DONE + c, 1u);
-      if (d == (uint32_t)(a.units[c] - 1)) {
+      const uint32_t d = fetch_add_relaxed(a.ws32 + WS_CHUNK_DONE + c, 1u);
+      if (d == (uint32_t)(a.units[c] + a.red_units[c] - 1)) {
         if (a.stamps) store_u64_relaxed(a.stamps + a.R + c, now_ticks());
-        if (a.done_flags) store_release(a.done_flags + c, a.epoch);
+        if (a.done_flags) {
+          fence_acquire_agent();
+          store_release(a.done_flags + c, a.epoch);
+        }
       }
-      const uint32_t t = fetch_add_acq_rel(a.ws32 + WS_TOTAL_DONE, 1u);
+      const uint32_t t = fetch_add_relaxed(a.ws32 + WS_TOTAL_DONE, 1u);
       if (t == (uint32_t)(a.total_units - 1) && a.stamps)
         store_u64_relaxed(a.stamps + 2 * a.R + 1, now_ticks());
     }
   }
 
-  // The last workgroup to leave returns every counter to zero for the next call.
+  // The last workgroup to leave returns every counter to zero for the next
+  // call.  Every counter access is atomic; the fences order the other
+  // workgroups' last accesses before the resets.
   if (tid == 0) {
-    const uint32_t e = fetch_add_acq_rel(a.ws32 + WS_EXITED, 1u);
+    fence_release_agent();
+    const uint32_t e = fetch_add_relaxed(a.ws32 + WS_EXITED, 1u);
     if (e == (uint32_t)(a.grid - 1)) {
+      fence_acquire_agent();
+      uint32_t *W = a.ws32;
       for (int c = 0; c < a.R; ++c) {
-        for (int g = 0; g < XCDS; ++g) a.ws32[WS_CLAIM + c * XCDS + g] = 0u;
-        a.ws32[WS_CHUNK_DONE + c] = 0u;
+        for (int g = 0; g < XCDS; ++g) store_relaxed_agent(W + WS_CLAIM + c * XCDS + g, 0u);
+        store_relaxed_agent(W + WS_CHUNK_DONE + c, 0u);
+        store_relaxed_agent(W + WS_RED_CLAIM + c, 0u);
+        store_relaxed_agent(W + WS_RED_READY + c, 0u);
         if (a.ctr_base[c] >= 0) {
           const int ntiles = a.units[c] / a.split[c];
-          for (int t = 0; t < ntiles; ++t) a.ws32[WS_TILE_CTR + a.ctr_base[c] + t] = 0u;
+          for (int t = 0; t < ntiles; ++t) {
+            store_relaxed_agent(W + WS_TILE_CTR + a.ctr_base[c] + t, 0u);
+            store_relaxed_agent(W + a.ready_off + a.ctr_base[c] + t, 0u);
+          }
         }
       }
-      a.ws32[WS_TOTAL_DONE] = 0u;
-      a.ws32[WS_ABORT] = 0u;
-      a.ws32[WS_EXITED] = 0u;
+      store_relaxed_agent(W + WS_TOTAL_DONE, 0u);
+      store_relaxed_agent(W + WS_ABORT, 0u);
+      store_relaxed_agent(W + WS_EXITED, 0u);
     }
   }
 }

@@ -17,8 +17,12 @@ constexpr int WS_CHUNK_DONE = 512;           // [FO_MAX_CHUNKS] finished units p
 constexpr int WS_TOTAL_DONE = 576;           // finished units, all chunks
 constexpr int WS_EXITED = 577;               // workgroups that have left the loop
 constexpr int WS_ABORT = 578;                // set when a wait timed out
-constexpr int WS_TILE_CTR = 1024;            // split-K arrival counters, one per tile
+constexpr int WS_RED_CLAIM = 640;            // [FO_MAX_CHUNKS] reduce units claimed
+constexpr int WS_RED_READY = 704;            // [FO_MAX_CHUNKS] split tiles published
+constexpr int WS_TILE_CTR = 1024;            // split-K arrival counters, one per tile,
+                                             // then the ready lists (same size)
 constexpr size_t WS_HEADER_BYTES = 4096;     // bytes before the tile counters
+constexpr int RED_SLICES = 8;                // reduce units (row slices) per split tile
 
 // Output tile of one workgroup and the depth of its LDS stage ring.
 struct TileCfg {
@@ -51,9 +55,11 @@ struct GemmArgs {
   int32_t order[FO_MAX_CHUNKS];
   int32_t split[FO_MAX_CHUNKS];
   int32_t units[FO_MAX_CHUNKS];     // tiles * split
-  int32_t ctr_base[FO_MAX_CHUNKS];  // split chunk: first tile counter; -1 if unsplit
+  int32_t ctr_base[FO_MAX_CHUNKS];  // split chunk: first tile counter / ready slot; -1 if unsplit
   int32_t part_base[FO_MAX_CHUNKS]; // split chunk: first partial tile (tile*S + split)
   int32_t kslice[FO_MAX_CHUNKS];    // k extent of one split (multiple of 64)
+  int32_t red_units[FO_MAX_CHUNKS]; // split chunk: tiles * RED_SLICES reduce units, else 0
+  int32_t ready_off;                // word offset of the ready lists (after the tile counters)
 };
 
 struct ReduceArgs {
