@@ -80,6 +80,20 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // land at m0 + 16 L.  Issued from asm so the compiler does not wait for
 // every outstanding copy before each LDS read; waits are explicit
 // (wait_vm) and a workgroup barrier follows them before any read.
+// 16-byte store written through every cache level to memory (system-scope
+// cache policy).  Output that another agent or XCD consumes is stored this
+// way, so a unit only has to wait for its own stores to be acknowledged
+// (wait_stores) before it counts itself, instead of a release fence that
+// writes back the whole L2 of its XCD.  The compiler does not track these
+// stores: every path that issues them ends in wait_stores.
+__device__ __forceinline__ void store_wt16(void *p, const f32x4 &v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" :: "v"(p), "v"(v) : "memory");
+}
+
+__device__ __forceinline__ void wait_stores() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 __device__ __forceinline__ void dma16(uint32_t m0, int voff, __amdgpu_buffer_rsrc_t rs, int soff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :: "s"(m0), "v"(voff), "s"(rs), "s"(soff) : "memory");
@@ -348,8 +362,19 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
     // Output piece writer: 4 consecutive fp32 values at (row, col) of a
     // row-major destination with leading dimension ld, stored as fp32 or bf16
     // (round to nearest even), masked to ncols columns.
+    // With wt (fp32 only) the store is written through to memory.
     auto put4 = [&](char *base, int64_t ld, int64_t row, int64_t col, int64_t ncols, bool bf16,
-                    bool vec_ok, const f32x4 &val) {
+                    bool vec_ok, bool wt, const f32x4 &val) {
+      if (wt) {
+        float *q = reinterpret_cast<float *>(base) + row * ld + col;
+        if (vec_ok && col + 4 <= ncols) {
+          store_wt16(q, val);
+        } else {
+          for (int e = 0; e < 4 && col + e < ncols; ++e)
+            __hip_atomic_store(q + e, val[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+        return;
+      }
       if (vec_ok && col + 4 <= ncols) {
         if (bf16) {
           const uint32_t lo = (uint32_t)f32_to_bf16_rne(val[0]) | ((uint32_t)f32_to_bf16_rne(val[1]) << 16);
@@ -391,7 +416,8 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
           if (q < S) sum = sum + t[q];
         const int64_t row = row0 + rr;
         if (row < rowlim && col0 + cc * 4 < N)
-          put4(reinterpret_cast<char *>(a.y), N, row, col0 + cc * 4, N, a.y_bf16 != 0, vec_ok, sum);
+          put4(reinterpret_cast<char *>(a.y), N, row, col0 + cc * 4, N, a.y_bf16 != 0, vec_ok,
+               a.done_flags != nullptr, sum);
       }
     } else {
 
@@ -539,6 +565,9 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
       const int64_t rlim = to_out ? rowlim : BM, clim = to_out ? N : BN;
       const bool vec_ok = to_out ? (N & 3) == 0 : true;
       const bool bf = to_out && a.y_bf16;
+      // split partials (read by reduce units on any XCD) and GEMM-RS output
+      // (read by the consumer of the done flags) are written through
+      const bool wt = !to_out || a.done_flags != nullptr;
 #pragma unroll
       for (int h = 0; h < HALVES; ++h) {
         __syncthreads();
@@ -560,15 +589,15 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
           const int64_t col = cbase + cc * 4;
           if (row >= rlim || col >= clim) continue;
           const f32x4 val = *reinterpret_cast<const f32x4 *>(stg + r * SROW + cc * 4);
-          put4(dbase, ld, row, col, clim, bf, vec_ok, val);
+          put4(dbase, ld, row, col, clim, bf, vec_ok, wt, val);
         }
       }
       if (!to_out) {
-        // Publish the partial: write it back past this XCD's L2, then count
-        // the split.  The split that completes the tile lists it for the
-        // reduce units; they order their reads after the release fences of
-        // all S splits through the tile counter (see the reduce unit).
-        fence_release_agent();
+        // Publish the partial: once its write-through stores are acknowledged,
+        // count the split.  The split that completes the tile lists it for
+        // the reduce units, which read the tile counter before their reads
+        // of the partials (see the reduce unit).
+        wait_stores();
         __syncthreads();
         if (tid == 0) {
           const uint32_t old = fetch_add_relaxed(a.ws32 + WS_TILE_CTR + a.ctr_base[c] + tile, 1u);
@@ -582,11 +611,11 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
     }   // GEMM unit
 
     // Completion accounting.  In GEMM-RS mode the chunk's done flag is
-    // released after every output element of the chunk is stored: each unit
-    // writes its stores back (release fence) before it counts itself, and
+    // released after every output element of the chunk is in memory: each
+    // unit waits for its write-through stores before it counts itself, and
     // the unit that completes the chunk acquires before releasing the flag.
-    // Without done flags the counters only feed the stamps: no fences.
-    if (a.done_flags) fence_release_agent();
+    // Without done flags the counters only feed the stamps.
+    if (a.done_flags) wait_stores();
     __syncthreads();
     if (tid == 0) {
       const uint32_t d = fetch_add_relaxed(a.ws32 + WS_CHUNK_DONE + c, 1u);
