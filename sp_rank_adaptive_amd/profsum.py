@@ -53,12 +53,13 @@ def source_hash(path=GEMM_SRC):
 
 
 def _per_dispatch(rows):
-    """{dispatch id: (kernel name, {counter: summed value})} in dispatch order."""
+    """[(kernel name, {counter: summed value, "_ns": duration})] in dispatch order."""
     out = {}
     for r in rows:
         d = int(r["Dispatch_Id"])
         name, vals = out.setdefault(d, (r["Kernel_Name"], {}))
         vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        vals["_ns"] = float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     return [out[d] for d in sorted(out)]
 
 
@@ -131,24 +132,28 @@ def cmd_traffic(fetch_dir, write_dir, out_json, out_md, cmd):
     _write(out_md, "\n".join(lines) + "\n")
 
 
-def cmd_counters(d, out_md, cmd, simds=1024):
+def cmd_counters(d, out_md, cmd, simds=1024, clock_hz=2.4e9):
     disp = _per_dispatch(_rows(_one(d, "_counter_collection.csv")))
     launches, kern = _gemm_launches(disp)
     lines = ["# GEMM counters (MFMA busy, bf16 MFMA flops, LDS bank conflicts)", "", "Command:", "",
              "```", cmd, "```", "",
-             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs); "
-             "bf16 flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; LDS conflict = "
-             "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.", "",
-             "| launch | kernel | MFMA busy % | bf16 GFLOP | LDS conflict % | dispatches |",
-             "|---|---|---:|---:|---:|---:|"]
+             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x 2.4 GHz x dispatch duration in "
+             "this counter run); bf16 flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; LDS conflict = "
+             "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.  Each 16x16x32 bf16 MFMA counts 16 busy "
+             "cycles, so the busy fraction equals the fraction of dense bf16 peak reached during "
+             "the dispatch.", "",
+             "| launch | kernel | dispatch us | MFMA busy % | bf16 GFLOP | LDS conflict % | dispatches |",
+             "|---|---|---:|---:|---:|---:|---:|"]
     for k, vals in launches.items():
         if not vals:
             continue
         med = lambda f: statistics.median(f(v) for v in vals)
-        busy = med(lambda v: v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / max(v.get("GRBM_GUI_ACTIVE", 1), 1) / simds)
+        dur = med(lambda v: v["_ns"])
+        busy = med(lambda v: v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / (simds * clock_hz * v["_ns"] * 1e-9))
         fl = med(lambda v: v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0) * 512 / 1e9)
         conf = med(lambda v: v.get("SQ_LDS_BANK_CONFLICT", 0) / max(v.get("SQ_LDS_IDX_ACTIVE", 1), 1))
-        lines.append(f"| {k} | `{kern[k]}` | {100 * busy:.1f} | {fl:.2f} | {100 * conf:.2f} | {len(vals)} |")
+        lines.append(f"| {k} | `{kern[k]}` | {dur / 1e3:.1f} | {100 * busy:.1f} | {fl:.2f} | "
+                     f"{100 * conf:.2f} | {len(vals)} |")
     _write(out_md, "\n".join(lines) + "\n")
 
 
