@@ -41,14 +41,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int NT = 256;   // threads per workgroup
+constexpr int NT = 256;   // threads per k-group (4 waves, one per SIMD)
 constexpr uint32_t kBufDword3 = 0x00020000u;   // raw buffer, 32-bit data format (gfx9)
 
 // Tile of BM x BN outputs; k staged through an LDS ring of STAGES buffers,
-// BK at a time (BK = 32 or 64: one or two MFMA k-steps per stage).
-template <int BM, int BN, int BK, int STAGES>
+// BK at a time (BK = 32 or 64: one or two MFMA k-steps per stage).  The
+// waves of one k-group form a WGM x WGN grid over the tile.
+template <int BM, int BN, int BK, int STAGES, int WGM = 2, int WGN = 2>
 struct Cfg {
-  static constexpr int WTM = BM / 2, WTN = BN / 2;   // wave tile
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN;   // wave tile
   static constexpr int FM = WTM / 16, FN = WTN / 16; // MFMA blocks per wave
   static constexpr int ROWB = BK * 2;                // LDS bytes per operand row
   static constexpr int CH = BK / 8;                  // 16-byte pieces per row
@@ -64,6 +65,7 @@ struct Cfg {
   static_assert(BK == 32 || BK == 64, "BK");
   static_assert(STAGES >= 2 && STAGES <= 4, "STAGES");
   static_assert(BM % 32 == 0 && BN % 32 == 0, "tile");
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
   static_assert(BM % RSTEP == 0 && BN % RSTEP == 0, "tile loads");
   static_assert(LDS + 64 <= 160 * 1024, "LDS");
   // 16-byte piece `ch` of row `r` lives at piece ch ^ swz(r): the fragment
@@ -96,8 +98,20 @@ __device__ __forceinline__ void wait_stores() {
 
 __device__ __forceinline__ void dma16(uint32_t m0, int voff, __amdgpu_buffer_rsrc_t rs, int soff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(m0), "v"(voff), "s"(rs), "s"(soff) : "memory");
+               :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(rs),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory");
 }
+
+// Raw buffer resource over `bytes` bytes at p, built from wave-uniform
+// (scalar) values so it can feed the scalar operand of a buffer load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *p, int bytes) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0,
+                                          __builtin_amdgcn_readfirstlane(bytes), (int)kBufDword3);
+}
+
 
 // Wait until at most N of this wave's vector-memory operations are pending.
 template <int N>
@@ -311,9 +325,97 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
   }
 }
 
-template <int BM, int BN, int BK, int STAGES>
-__global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
-  using C = Cfg<BM, BN, BK, STAGES>;
+// Output piece writer: 4 consecutive fp32 values at (row, col) of a row-major
+// destination with leading dimension ld, stored as fp32 or bf16 (round to
+// nearest even), masked to ncols columns.  With wt (fp32 only) the store is
+// written through to memory.
+__device__ __forceinline__ void put4(char *base, int64_t ld, int64_t row, int64_t col, int64_t ncols,
+                                     bool bf16, bool vec_ok, bool wt, const f32x4 &val) {
+  if (wt) {
+    float *q = reinterpret_cast<float *>(base) + row * ld + col;
+    if (vec_ok && col + 4 <= ncols) {
+      store_wt16(q, val);
+    } else {
+      for (int e = 0; e < 4 && col + e < ncols; ++e)
+        __hip_atomic_store(q + e, val[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    return;
+  }
+  if (vec_ok && col + 4 <= ncols) {
+    if (bf16) {
+      const uint32_t lo = (uint32_t)f32_to_bf16_rne(val[0]) | ((uint32_t)f32_to_bf16_rne(val[1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_rne(val[2]) | ((uint32_t)f32_to_bf16_rne(val[3]) << 16);
+      *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(base) + row * ld + col) = u32x2{lo, hi};
+    } else {
+      *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(base) + row * ld + col) = val;
+    }
+  } else {
+    for (int e = 0; e < 4 && col + e < ncols; ++e) {
+      if (bf16)
+        reinterpret_cast<uint16_t *>(base)[row * ld + col + e] = f32_to_bf16_rne(val[e]);
+      else
+        reinterpret_cast<float *>(base)[row * ld + col + e] = val[e];
+    }
+  }
+}
+
+// Reduce unit: row slice `slice` of split tile `tile` of chunk c, whose S
+// partials are all written; sums them in split order 0..S-1 and stores the
+// output rows.
+template <int BM, int BN, int NTT>
+__device__ __forceinline__ void reduce_unit(const GemmArgs &a, int c, int tile, int slice, int64_t row0,
+                                         int64_t rowlim, int64_t col0) {
+  const int tid = threadIdx.x;
+  const int64_t N = a.n;
+  const int S = a.split[c];
+  const size_t pbase = (size_t)a.part_base[c] + (size_t)tile * S;
+  const float *P = a.partials + pbase * (size_t)(BM * BN);
+  constexpr int ROWS = BM / RED_SLICES;
+  constexpr int PPR = BN / 4;                       // pieces per row
+  static_assert(BM % RED_SLICES == 0, "slices");
+  const int r0 = slice * ROWS;
+  const bool vec_ok = (N & 3) == 0;
+  for (int pc = tid; pc < ROWS * PPR; pc += NTT) {
+    const int rr = r0 + pc / PPR, cc = pc - (pc / PPR) * PPR;
+    const size_t off = (size_t)rr * BN + (size_t)cc * 4;
+    f32x4 t[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q < S) t[q] = *reinterpret_cast<const f32x4 *>(P + (size_t)q * (BM * BN) + off);
+    f32x4 sum = t[0];
+#pragma unroll
+    for (int q = 1; q < 8; ++q)
+      if (q < S) sum = sum + t[q];
+    const int64_t row = row0 + rr;
+    if (row < rowlim && col0 + cc * 4 < N)
+      put4(reinterpret_cast<char *>(a.y), N, row, col0 + cc * 4, N, a.y_bf16 != 0, vec_ok,
+           a.done_flags != nullptr, sum);
+  }
+}
+
+// Wait for this wave's copies of stage j when `later` stages issued after it
+// may stay in flight (VR copies per stage and wave).
+// Wait for this wave's copies of stage j when `later` stages issued after it
+// may stay in flight (VR copies per stage and wave).
+template <int VR, int STAGES>
+__device__ __forceinline__ void wait_later(int later) {
+  if constexpr (STAGES >= 4) { if (later >= 2) { wait_vm<2 * VR>(); return; } }
+  if constexpr (STAGES >= 3) { if (later >= 1) { wait_vm<VR>(); return; } }
+  wait_vm<0>();
+}
+
+// KG k-groups of WGM x WGN waves over the tile.  With KG = 2 group g
+// multiplies k-step g of every stage into its own accumulators (BK = 32 KG);
+// the groups' tiles are summed in LDS before the store.  Every 4 waves form a
+// copy group that issues the stage copies (round v goes to copy group
+// v % NCG), so each SIMD runs NTT / 256 waves.
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int KG>
+__device__ __forceinline__ void gemm_body(const GemmArgs &a) {
+  using C = Cfg<BM, BN, BK, STAGES, WGM, WGN>;
+  constexpr int NTT = 64 * WGM * WGN * KG;
+  constexpr int NCG = NTT / NT;   // copy groups of 4 waves
+  static_assert(NTT % NT == 0, "whole copy groups");
+  static_assert(KG == 1 || C::KS == KG, "one k-step per k-group");
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
   __shared__ Unit s_unit;
   __shared__ int s_last;
@@ -321,7 +423,12 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int grp = __builtin_amdgcn_readfirstlane(wave / (WGM * WGN));   // k-group
+  const int gw = wave % (WGM * WGN);                                     // wave in its k-group
+  const int wm = gw / WGN, wn = gw % WGN;
+  const int cg = __builtin_amdgcn_readfirstlane(wave >> 2);             // copy group
+  const int cw = wave & 3;                                               // wave in its copy group
+  const int gtid = tid & (NT - 1);                                       // thread in its copy group
   const int64_t K = a.k, N = a.n;
   const int xg = (int)(blockIdx.x % XCDS);
 
@@ -359,71 +466,14 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
     const int64_t k1 = (k0 + a.kslice[c] < K) ? k0 + a.kslice[c] : K;
     const int KT = (int)((k1 - k0 + BK - 1) / BK);
 
-    // Output piece writer: 4 consecutive fp32 values at (row, col) of a
-    // row-major destination with leading dimension ld, stored as fp32 or bf16
-    // (round to nearest even), masked to ncols columns.
-    // With wt (fp32 only) the store is written through to memory.
-    auto put4 = [&](char *base, int64_t ld, int64_t row, int64_t col, int64_t ncols, bool bf16,
-                    bool vec_ok, bool wt, const f32x4 &val) {
-      if (wt) {
-        float *q = reinterpret_cast<float *>(base) + row * ld + col;
-        if (vec_ok && col + 4 <= ncols) {
-          store_wt16(q, val);
-        } else {
-          for (int e = 0; e < 4 && col + e < ncols; ++e)
-            __hip_atomic_store(q + e, val[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        }
-        return;
-      }
-      if (vec_ok && col + 4 <= ncols) {
-        if (bf16) {
-          const uint32_t lo = (uint32_t)f32_to_bf16_rne(val[0]) | ((uint32_t)f32_to_bf16_rne(val[1]) << 16);
-          const uint32_t hi = (uint32_t)f32_to_bf16_rne(val[2]) | ((uint32_t)f32_to_bf16_rne(val[3]) << 16);
-          *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(base) + row * ld + col) = u32x2{lo, hi};
-        } else {
-          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(base) + row * ld + col) = val;
-        }
-      } else {
-        for (int e = 0; e < 4 && col + e < ncols; ++e) {
-          if (bf16)
-            reinterpret_cast<uint16_t *>(base)[row * ld + col + e] = f32_to_bf16_rne(val[e]);
-          else
-            reinterpret_cast<float *>(base)[row * ld + col + e] = val[e];
-        }
-      }
-    };
-
     if (un.red) {
-      // Reduce unit: row slice sp of a split tile whose S partials are all
-      // written; sum them in split order 0..S-1 and store the output rows.
-      const size_t pbase = (size_t)a.part_base[c] + (size_t)tile * S;
-      const float *P = a.partials + pbase * (size_t)(BM * BN);
-      constexpr int ROWS = BM / RED_SLICES;
-      constexpr int PPR = BN / 4;                       // pieces per row
-      static_assert(BM % RED_SLICES == 0, "slices");
-      const int r0 = un.sp * ROWS;
-      const bool vec_ok = (N & 3) == 0;
-      for (int pc = tid; pc < ROWS * PPR; pc += NT) {
-        const int rr = r0 + pc / PPR, cc = pc - (pc / PPR) * PPR;
-        const size_t off = (size_t)rr * BN + (size_t)cc * 4;
-        f32x4 t[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (q < S) t[q] = *reinterpret_cast<const f32x4 *>(P + (size_t)q * (BM * BN) + off);
-        f32x4 sum = t[0];
-#pragma unroll
-        for (int q = 1; q < 8; ++q)
-          if (q < S) sum = sum + t[q];
-        const int64_t row = row0 + rr;
-        if (row < rowlim && col0 + cc * 4 < N)
-          put4(reinterpret_cast<char *>(a.y), N, row, col0 + cc * 4, N, a.y_bf16 != 0, vec_ok,
-               a.done_flags != nullptr, sum);
-      }
+      reduce_unit<BM, BN, NTT>(a, c, tile, un.sp, row0, rowlim, col0);
     } else {
 
     // Stage layout in LDS: BM rows of X then BN rows of W, ROWB bytes each,
     // 16-byte pieces XOR-swizzled.  Load round v of a stage fills LDS slots
-    // [256 v, 256 v + 256) (wave w: 64 slots at m0 = base + 4096 v + 1024 w);
+    // [256 v, 256 v + 256) (wave w of copy group v % NCG, which issues round
+    // v: 64 slots at m0 = base + 4096 v + 1024 w);
     // slot s holds row s / CH, piece s % CH, i.e. logical piece
     // (s % CH) ^ swz(row) of that row.  Thread t always fills slot t of a
     // round, so its row inside a round, its piece and hence its byte offset
@@ -431,16 +481,14 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
     // uniform offset.  Rows past the chunk end or past n read as zero (buffer
     // size), and so does k past the split's end (per-thread offset moved past
     // the buffer).
-    const int tr = tid / C::CH;
-    const int tch = (tid % C::CH) ^ C::swz(tr);
+    const int tr = gtid / C::CH;
+    const int tch = (gtid % C::CH) ^ C::swz(tr);
     const int nra = (int)((rowlim - row0 < BM) ? rowlim - row0 : BM);
     const int nrb = (int)((N - col0 < BN) ? N - col0 : BN);
-    const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.x + row0 * K), (short)0, (int)(nra * K * 2), (int)kBufDword3);
-    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.w + col0 * K), (short)0, (int)(nrb * K * 2), (int)kBufDword3);
+    const __amdgpu_buffer_rsrc_t rsa = uniform_rsrc(a.x + row0 * K, (int)(nra * K * 2));
+    const __amdgpu_buffer_rsrc_t rsb = uniform_rsrc(a.w + col0 * K, (int)(nrb * K * 2));
     const int voff = (int)((tr * K + tch * 8) * 2);
-    const uint32_t lds0 = lds_addr(lds) + (uint32_t)(__builtin_amdgcn_readfirstlane(wave) * 1024);
+    const uint32_t lds0 = lds_addr(lds) + (uint32_t)(__builtin_amdgcn_readfirstlane(cw) * 1024);
 
     auto issue = [&](int stage) {
       const int kk = (int)(k0 + (int64_t)stage * BK);          // uniform
@@ -448,6 +496,7 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
       const uint32_t base = lds0 + (uint32_t)((stage % STAGES) * C::STAGE);
 #pragma unroll
       for (int v = 0; v < C::V; ++v) {
+        if (NCG > 1 && v % NCG != cg) continue;
         const bool isA = v < C::AV;
         const int rs = C::RSTEP * (isA ? v : v - C::AV);
         dma16(base + (uint32_t)(v * 4096), vo, isA ? rsa : rsb, (int)((rs * K + kk) * 2));
@@ -468,6 +517,30 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
       constexpr int buf = decltype(bufc)::value;
       const char *A = lds + buf * C::STAGE;
       const char *B = A + C::A_BYTES;
+      if constexpr (KG > 1) {
+        // this group's k-step of the stage: read its fragments, then the MFMAs
+        const int ch = grp * 4 + (lane >> 4);
+        const int swz = ((ch ^ C::swz(lane & 15)) << 4);
+        bf16x8 af[C::FM], bfr[C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+          af[i] = *reinterpret_cast<const bf16x8 *>(A + (wm * C::WTM + i * 16 + (lane & 15)) * C::ROWB + swz);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+          bfr[j] = *reinterpret_cast<const bf16x8 *>(B + (wn * C::WTN + j * 16 + (lane & 15)) * C::ROWB + swz);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) {
+            if (first)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          }
+        __builtin_amdgcn_sched_group_barrier(0x100, C::FM + C::FN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, C::FM * C::FN, 0);
+        return;
+      } else {
       bf16x8 af[C::KS][C::FM], bfr[C::KS][C::FN];
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
@@ -503,15 +576,20 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
       } else {
         __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
       }
+      }
     };
 
     // Wait until stage j has landed: the stages issued after it may stay in
     // flight (each stage is V copies per wave).
     auto wait_stage = [&](int j) {
       const int later = ((j + STAGES - 1 < KT) ? j + STAGES - 1 : KT) - (j + 1);
-      if constexpr (STAGES >= 4) { if (later >= 2) { wait_vm<2 * C::V>(); return; } }
-      if constexpr (STAGES >= 3) { if (later >= 1) { wait_vm<C::V>(); return; } }
-      wait_vm<0>();
+      if constexpr (NCG == 1) {
+        wait_later<C::V, STAGES>(later);
+      } else {
+        static_assert(NCG == 2, "copy groups");
+        if (cg == 0) wait_later<(C::V + 1) / 2, STAGES>(later);
+        else wait_later<C::V / 2, STAGES>(later);
+      }
     };
 
     // prologue: stages 0 .. STAGES-2 in flight.  The LDS buffers about to be
@@ -554,6 +632,7 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
       constexpr int SROW = (BM / 2 * (BN + 4) * 4 <= C::LDS) ? BN + 4 : BN;
       constexpr int HALVES = (BM * SROW * 4 <= C::LDS) ? 1 : 2;
       static_assert(BM / HALVES * SROW * 4 <= C::LDS, "epilogue staging");
+      static_assert(HALVES == 1 || HALVES == WGM, "a staging pass holds whole wave rows");
       constexpr int HROWS = BM / HALVES;
       constexpr int CPR = BN / 4;                                   // 16-byte pieces per row
       float *stg = reinterpret_cast<float *>(lds);
@@ -570,20 +649,27 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
       const bool wt = !to_out || a.done_flags != nullptr;
 #pragma unroll
       for (int h = 0; h < HALVES; ++h) {
-        __syncthreads();
-        if (HALVES == 1 || wm == h) {
+        // the last k-group stores its tile, then each other group adds its
+        // own in turn (group KG-1 + ... + group 0, a fixed order)
 #pragma unroll
-          for (int i = 0; i < C::FM; ++i)
+        for (int g = KG - 1; g >= 0; --g) {
+          __syncthreads();
+          if (grp == g && (HALVES == 1 || wm == h)) {
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j)
+            for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                const int r = (HALVES == 1 ? wm * C::WTM : 0) + i * 16 + (lane >> 4) * 4 + v;
-                stg[r * SROW + wn * C::WTN + j * 16 + (lane & 15)] = acc[i][j][v];
-              }
+              for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                  const int r = (HALVES == 1 ? wm * C::WTM : 0) + i * 16 + (lane >> 4) * 4 + v;
+                  float *q = stg + r * SROW + wn * C::WTN + j * 16 + (lane & 15);
+                  if (g == KG - 1) *q = acc[i][j][v];
+                  else *q = *q + acc[i][j][v];
+                }
+          }
         }
         __syncthreads();
-        for (int cidx = tid; cidx < HROWS * CPR; cidx += NT) {
+        for (int cidx = tid; cidx < HROWS * CPR; cidx += NTT) {
           const int r = cidx / CPR, cc = cidx - (cidx / CPR) * CPR;
           const int64_t row = rbase + h * HROWS + r;
           const int64_t col = cbase + cc * 4;
@@ -661,14 +747,35 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
   }
 }
 
+template <int BM, int BN, int BK, int STAGES>
+__global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
+  gemm_body<BM, BN, BK, STAGES, 2, 2, 1>(a);
+}
+
+// Two k-groups: two waves per SIMD.  The register cap leaves VGPRs free on
+// every SIMD, so a one-wave kernel of a copy-engine emulator still fits
+// beside the persistent grid.  On gfx950 the compiler counts this attribute
+// in pairs of the unified VGPR/AGPR file: 120 caps each wave at 240, so two
+// waves leave 32 of each lane's 512 registers free.
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int KG>
+__global__ void __launch_bounds__(2 * NT, 1) __attribute__((amdgpu_num_vgpr(120)))
+gemm_kernel_w8(GemmArgs a) {
+  gemm_body<BM, BN, BK, STAGES, WGM, WGN, KG>(a);
+}
+
 namespace {
 
 struct Cand {
   int bm, bn, bk, stages;
+  bool room;   // leaves registers free on every SIMD for a one-wave kernel
 };
 
-// Tile configurations compiled into the library.
-constexpr Cand kCands[] = {{256, 256, 32, 4}, {256, 160, 64, 3}, {128, 224, 64, 3}, {128, 128, 64, 4}};
+// Tile configurations compiled into the library (the launcher below maps
+// each to its wave layout): 256 x 256 as 8 waves in a 2 x 4 grid; 128 x 224
+// as two k-groups of 2 x 2 waves; 256 x 160 and 128 x 128 as 2 x 2 waves.
+// The 256 x 160 kernel holds almost every register of a SIMD.
+constexpr Cand kCands[] = {{256, 256, 32, 4, true}, {256, 160, 64, 3, false},
+                           {128, 224, 64, 3, true}, {128, 128, 64, 4, true}};
 
 // Relative cost of a tile shape per output element: operand bytes staged per
 // flop fall as 1/BM + 1/BN, so larger tiles run closer to the MFMA rate.
@@ -689,15 +796,15 @@ bool parse_env_tile(Cand *out) {
 TileCfg choose_tile(int64_t mc, int64_t n, int64_t k, int R, int grid, bool leave_room) {
   (void)k;
   Cand pick{};
-  if (parse_env_tile(&pick) && !(leave_room && pick.bm == 256 && pick.bn == 256))
+  if (parse_env_tile(&pick) && !(leave_room && !pick.room))
     return TileCfg{pick.bm, pick.bn, pick.stages};
   if (grid < 1) grid = 1;
   double best = 0;
   bool have = false;
   for (const Cand &c : kCands) {
-    // the 256 x 256 tile takes the whole register file of each SIMD: with
-    // arrival flags a one-wave emulator kernel must still fit beside it
-    if (leave_room && c.bm == 256 && c.bn == 256) continue;
+    // with arrival flags a one-wave emulator kernel must still fit beside
+    // the persistent grid
+    if (leave_room && !c.room) continue;
     const int64_t tiles = ((mc + c.bm - 1) / c.bm) * ((n + c.bn - 1) / c.bn) * R;
     const int64_t waves = (tiles + grid - 1) / grid;
     const double cost = (double)waves * c.bm * c.bn / tile_eff(c.bm, c.bn);
@@ -720,11 +827,11 @@ size_t partial_slot_bytes(const TileCfg &t) { return (size_t)t.bm * t.bn * sizeo
 
 hipError_t launch_gemm(const GemmArgs &a, const TileCfg &t, hipStream_t stream) {
   if (t.bm == 256 && t.bn == 256)
-    hipLaunchKernelGGL((gemm_kernel<256, 256, 32, 4>), dim3(a.grid), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel_w8<256, 256, 32, 4, 2, 4, 1>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
   else if (t.bm == 256 && t.bn == 160)
     hipLaunchKernelGGL((gemm_kernel<256, 160, 64, 3>), dim3(a.grid), dim3(NT), 0, stream, a);
   else if (t.bm == 128 && t.bn == 224)
-    hipLaunchKernelGGL((gemm_kernel<128, 224, 64, 3>), dim3(a.grid), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel_w8<128, 224, 64, 3, 2, 2, 2>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
   else if (t.bm == 128 && t.bn == 128)
     hipLaunchKernelGGL((gemm_kernel<128, 128, 64, 4>), dim3(a.grid), dim3(NT), 0, stream, a);
   else

@@ -221,8 +221,15 @@ def test_gemm_rs_parity_done_flags_and_order(fo, orc):
             check_exact(host(part)[rows], ref, "rs int")
         else:
             check_tolerance(host(part)[rows], ref, what="rs gauss")
-        st = host(stamps).astype(np.int64)
-        R = cfg.R
-        # the local chunk is claimed last: its first claim follows every peer's
-        first = st[:R]
-        assert first[0] >= first[1:].max()
+    # Claim order: with fewer workgroups than units the claims come in rounds,
+    # and the local chunk is claimed only after every peer chunk's units (with
+    # one unit per workgroup every chunk is claimed in the same instant).
+    part = torch.full((cfg.m, cfg.n), float("nan"), device="cuda")
+    stamps = torch.zeros(2 * cfg.R + 2, dtype=torch.int64, device="cuda")
+    e = EP.next()
+    fo.fo_gemm_rs(x, w, part, done, fo.Schedule(nchunks=cfg.R, epoch=e, stamps=stamps, max_workgroups=64), ws)
+    torch.cuda.synchronize()
+    assert (host(done) == e).all()
+    check_tolerance(host(part)[rows], ref, what="rs gauss, 64 workgroups")
+    first = host(stamps).astype(np.int64)[:cfg.R]
+    assert first[0] >= first[1:].max()
