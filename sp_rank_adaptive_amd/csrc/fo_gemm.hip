@@ -404,18 +404,22 @@ __device__ __forceinline__ void wait_later(int later) {
   wait_vm<0>();
 }
 
-// KG k-groups of WGM x WGN waves over the tile.  With KG = 2 group g
-// multiplies k-step g of every stage into its own accumulators (BK = 32 KG);
-// the groups' tiles are summed in LDS before the store.  Every 4 waves form a
-// copy group that issues the stage copies (round v goes to copy group
-// v % NCG), so each SIMD runs NTT / 256 waves.
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int KG>
+// Compute waves: KG k-groups of WGM x WGN waves over the tile.  With KG = 2
+// group g multiplies k-step g of every stage into its own accumulators
+// (BK = 32 KG); the groups' tiles are summed in LDS before the store.
+// Without PC every 4 waves form a copy group that also issues the stage
+// copies (round v goes to copy group v % NCG).  With PC four extra producer
+// waves issue every copy and wait for it, so a compute wave never stalls
+// behind a full load queue: the two kinds of wave share each SIMD.
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int KG, bool PC>
 __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
   using C = Cfg<BM, BN, BK, STAGES, WGM, WGN>;
-  constexpr int NTT = 64 * WGM * WGN * KG;
-  constexpr int NCG = NTT / NT;   // copy groups of 4 waves
+  constexpr int NCW = WGM * WGN * KG;          // compute waves
+  constexpr int NTT = 64 * NCW + (PC ? NT : 0);
+  constexpr int NCG = PC ? 1 : NTT / NT;       // copy groups of 4 waves
   static_assert(NTT % NT == 0, "whole copy groups");
   static_assert(KG == 1 || C::KS == KG, "one k-step per k-group");
+  static_assert(!PC || KG == 1, "producer waves feed one k-group");
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
   __shared__ Unit s_unit;
   __shared__ int s_last;
@@ -423,8 +427,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int grp = __builtin_amdgcn_readfirstlane(wave / (WGM * WGN));   // k-group
-  const int gw = wave % (WGM * WGN);                                     // wave in its k-group
+  const bool prod = !PC || wave < 4;                                     // issues stage copies
+  const bool cons = !PC || wave >= 4;                                    // multiplies
+  const int cwave = PC ? (wave >= 4 ? wave - 4 : 0) : wave;              // index among compute waves
+  const int grp = __builtin_amdgcn_readfirstlane(cwave / (WGM * WGN));  // k-group
+  const int gw = cwave % (WGM * WGN);                                    // wave in its k-group
   const int wm = gw / WGN, wn = gw % WGN;
   const int cg = __builtin_amdgcn_readfirstlane(wave >> 2);             // copy group
   const int cw = wave & 3;                                               // wave in its copy group
@@ -540,6 +547,54 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
         __builtin_amdgcn_sched_group_barrier(0x100, C::FM + C::FN, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, C::FM * C::FN, 0);
         return;
+      } else if constexpr (PC && C::KS == 2) {
+        // Both k-steps with few live fragments: k-step 0's MFMAs go column by
+        // column; after column j its W fragment is dead and k-step 1's W
+        // fragment j is read in its place, and k-step 1's X fragments are read
+        // during the last column.  Peak: 2 FM + FN fragments.
+        const int sw0 = (((lane >> 4) ^ C::swz(lane & 15)) << 4);
+        const int sw1 = (((4 + (lane >> 4)) ^ C::swz(lane & 15)) << 4);
+        auto rda = [&](int i, int swz) {
+          return *reinterpret_cast<const bf16x8 *>(A + (wm * C::WTM + i * 16 + (lane & 15)) * C::ROWB + swz);
+        };
+        auto rdb = [&](int j, int swz) {
+          return *reinterpret_cast<const bf16x8 *>(B + (wn * C::WTN + j * 16 + (lane & 15)) * C::ROWB + swz);
+        };
+        bf16x8 a0[C::FM], a1[C::FM], b0[C::FN], b1[C::FN];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) a0[i] = rda(i, sw0);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) b0[j] = rdb(j, sw0);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i) {
+            if (first)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[i], b0[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
+          }
+          b1[j] = rdb(j, sw1);
+          if (j == C::FN - 1) {
+#pragma unroll
+            for (int i = 0; i < C::FM; ++i) a1[i] = rda(i, sw1);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
+        // pinned order (mask 0x100: LDS reads, 0x008: MFMA)
+        __builtin_amdgcn_sched_group_barrier(0x100, C::FM + C::FN, 0);
+        static_for<C::FN - 1>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x008, C::FM, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        });
+        __builtin_amdgcn_sched_group_barrier(0x008, C::FM, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1 + C::FM, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, C::FM * C::FN, 0);
+        return;
       } else {
       bf16x8 af[C::KS][C::FM], bfr[C::KS][C::FN];
 #pragma unroll
@@ -595,28 +650,30 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
     // prologue: stages 0 .. STAGES-2 in flight.  The LDS buffers about to be
     // filled may still be read by the previous unit's last k-steps.
     __syncthreads();
+    if (prod) {
 #pragma unroll
-    for (int p = 0; p < STAGES - 1; ++p)
-      if (p < KT) issue(p);
+      for (int p = 0; p < STAGES - 1; ++p)
+        if (p < KT) issue(p);
+    }
 
     // iteration j: wait for stage j; barrier (stage j visible to every wave,
     // and every wave is done with stage j-1, whose buffer is refilled next);
     // issue stage j+STAGES-1; multiply stage j (LDS buffer j % STAGES).
     // Iteration 0 is peeled; the rest are unrolled STAGES at a time so each
     // buffer offset is a constant.
-    wait_stage(0);
+    if (prod) wait_stage(0);
     __syncthreads();
-    if (STAGES - 1 < KT) issue(STAGES - 1);
-    compute(std::true_type{}, std::integral_constant<int, 0>{});
+    if (prod && STAGES - 1 < KT) issue(STAGES - 1);
+    if (cons) compute(std::true_type{}, std::integral_constant<int, 0>{});
     for (int j0 = 1; j0 < KT; j0 += STAGES) {
       static_for<STAGES>([&](auto pc) {
         constexpr int p = decltype(pc)::value;
         const int j = j0 + p;
         if (j < KT) {
-          wait_stage(j);
+          if (prod) wait_stage(j);
           __syncthreads();
-          if (j + STAGES - 1 < KT) issue(j + STAGES - 1);
-          compute(std::false_type{}, std::integral_constant<int, (1 + p) % STAGES>{});
+          if (prod && j + STAGES - 1 < KT) issue(j + STAGES - 1);
+          if (cons) compute(std::false_type{}, std::integral_constant<int, (1 + p) % STAGES>{});
         }
       });
     }
@@ -654,7 +711,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
 #pragma unroll
         for (int g = KG - 1; g >= 0; --g) {
           __syncthreads();
-          if (grp == g && (HALVES == 1 || wm == h)) {
+          if (cons && grp == g && (HALVES == 1 || wm == h)) {
 #pragma unroll
             for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -749,7 +806,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
 
 template <int BM, int BN, int BK, int STAGES>
 __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
-  gemm_body<BM, BN, BK, STAGES, 2, 2, 1>(a);
+  gemm_body<BM, BN, BK, STAGES, 2, 2, 1, false>(a);
 }
 
 // Two k-groups: two waves per SIMD.  The register cap leaves VGPRs free on
@@ -757,10 +814,10 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
 // beside the persistent grid.  On gfx950 the compiler counts this attribute
 // in pairs of the unified VGPR/AGPR file: 120 caps each wave at 240, so two
 // waves leave 32 of each lane's 512 registers free.
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int KG>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int KG, bool PC>
 __global__ void __launch_bounds__(2 * NT, 1) __attribute__((amdgpu_num_vgpr(120)))
 gemm_kernel_w8(GemmArgs a) {
-  gemm_body<BM, BN, BK, STAGES, WGM, WGN, KG>(a);
+  gemm_body<BM, BN, BK, STAGES, WGM, WGN, KG, PC>(a);
 }
 
 namespace {
@@ -772,7 +829,8 @@ struct Cand {
 
 // Tile configurations compiled into the library (the launcher below maps
 // each to its wave layout): 256 x 256 as 8 waves in a 2 x 4 grid; 128 x 224
-// as two k-groups of 2 x 2 waves; 256 x 160 and 128 x 128 as 2 x 2 waves.
+// as 4 producer waves + 2 x 2 compute waves; 256 x 160 and 128 x 128 as
+// 2 x 2 waves.
 // The 256 x 160 kernel holds almost every register of a SIMD.
 constexpr Cand kCands[] = {{256, 256, 32, 4, true}, {256, 160, 64, 3, false},
                            {128, 224, 64, 3, true}, {128, 128, 64, 4, true}};
@@ -827,11 +885,11 @@ size_t partial_slot_bytes(const TileCfg &t) { return (size_t)t.bm * t.bn * sizeo
 
 hipError_t launch_gemm(const GemmArgs &a, const TileCfg &t, hipStream_t stream) {
   if (t.bm == 256 && t.bn == 256)
-    hipLaunchKernelGGL((gemm_kernel_w8<256, 256, 32, 4, 2, 4, 1>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel_w8<256, 256, 32, 4, 2, 4, 1, false>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
   else if (t.bm == 256 && t.bn == 160)
     hipLaunchKernelGGL((gemm_kernel<256, 160, 64, 3>), dim3(a.grid), dim3(NT), 0, stream, a);
   else if (t.bm == 128 && t.bn == 224)
-    hipLaunchKernelGGL((gemm_kernel_w8<128, 224, 64, 3, 2, 2, 2>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel_w8<128, 224, 64, 3, 2, 2, 1, true>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
   else if (t.bm == 128 && t.bn == 128)
     hipLaunchKernelGGL((gemm_kernel<128, 128, 64, 4>), dim3(a.grid), dim3(NT), 0, stream, a);
   else
