@@ -345,7 +345,7 @@ fo_status fo_chunk_reduce(void *dst, fo_dtype dst_dtype, const float *const *src
   // 4 workgroups of 256 threads per CU keeps enough bytes in flight; with
   // arrival flags, wave slots stay free for the emulator's one-wave kernels.
   int grid = s->max_workgroups > 0 ? s->max_workgroups : I->cus * 4;
-  const int64_t min_per = 256 * 4;   // one full step of the workgroup
+  const int64_t min_per = 256 * 2;   // one full step of the workgroup
   int64_t per = (a.n4 + grid - 1) / grid;
   if (per < min_per) per = min_per;
   per = (per + 255) / 256 * 256;

@@ -170,6 +170,45 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
   const int R = a.R;
   uint64_t wait_from = 0;
   Unit r{-1, 0, 0, 0, 0, 0};
+  // First claim of a workgroup: its own XCD's group, the q-th unit in
+  // priority order over the landed chunks, taken as if no unit were claimed
+  // yet (true at the start of a call), so only the flags are read before the
+  // fetch-add; if the fetch-add shows the group exhausted, the general claim
+  // below takes over.
+  if (rank_hint >= 0 && !a.strict) {
+    bool ok = false;
+    if (lane < R) {
+      const int c = a.order[lane];
+      ok = a.arrived == nullptr || c == a.local || epoch_reached(load_relaxed(a.arrived + c), a.epoch);
+    }
+    const uint64_t landed = __ballot(ok);
+    uint32_t q = (uint32_t)rank_hint;
+    int pick = -1;
+    for (int sidx = 0; sidx < R; ++sidx) {
+      if (!((landed >> sidx) & 1)) continue;
+      const uint32_t nu = group_units(a, a.order[sidx], xg);
+      if (q < nu) { pick = a.order[sidx]; break; }
+      q -= nu;
+    }
+    if (pick >= 0) {
+      rank_hint = -1;
+      if (a.arrived != nullptr && pick != a.local) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+      st.acquired |= 1ull << pick;
+      uint32_t u = 0;
+      if (lane == 0) u = fetch_add_relaxed(a.ws32 + WS_CLAIM + pick * XCDS + xg, 1u);
+      u = __builtin_amdgcn_readfirstlane(u);
+      if (u < group_units(a, pick, xg)) {
+        const int S = a.split[pick];
+        const int tl = (int)u / S;
+        r.c = pick;
+        r.sp = (int)u - tl * S;
+        group_tile(a, xg, tl, r.tm, r.tn);
+        r.first = (xg == 0 && u == 0);
+        r.red = 0;
+        return r;
+      }
+    }
+  }
   for (;;) {
     // landed[s]: chunk order[s] usable; red[s]: split chunk with reduce units left
     bool ok = false, redp = false;
@@ -760,7 +799,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
     // Without done flags the counters only feed the stamps.
     if (a.done_flags) wait_stores();
     __syncthreads();
-    if (tid == 0) {
+    if (tid == 0 && (a.done_flags || a.stamps)) {
       const uint32_t d = fetch_add_relaxed(a.ws32 + WS_CHUNK_DONE + c, 1u);
       if (d == (uint32_t)(a.units[c] + a.red_units[c] - 1)) {
         if (a.stamps) store_u64_relaxed(a.stamps + a.R + c, now_ticks());
@@ -776,13 +815,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
   }
 
   // The last workgroup to leave returns every counter to zero for the next
-  // call.  Every counter access is atomic; the fences order the other
-  // workgroups' last accesses before the resets.
+  // call.  Every counter access is a device-scope atomic performed at the
+  // device's coherence point, and each of a workgroup's counter atomics has
+  // returned (its result steers the workgroup) before the workgroup counts
+  // its exit; the last workgroup issues the resets after its own count has
+  // returned.  No cache maintenance is needed, and none is paid: a release
+  // fence here would write back the XCD's L2 once per workgroup.
   if (tid == 0) {
-    fence_release_agent();
     const uint32_t e = fetch_add_relaxed(a.ws32 + WS_EXITED, 1u);
     if (e == (uint32_t)(a.grid - 1)) {
-      fence_acquire_agent();
       uint32_t *W = a.ws32;
       for (int c = 0; c < a.R; ++c) {
         for (int g = 0; g < XCDS; ++g) store_relaxed_agent(W + WS_CLAIM + c * XCDS + g, 0u);

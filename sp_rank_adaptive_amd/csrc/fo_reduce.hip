@@ -18,7 +18,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int RT = 256;  // threads per workgroup
-constexpr int RU = 4;    // vectors per thread per step (loads in flight)
+constexpr int RU = 2;    // vectors per thread per step
+constexpr int KB = 8;    // sources whose loads are issued together
 
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(RT) reduce_kernel(ReduceArgs a) {
@@ -61,42 +62,59 @@ __global__ void __launch_bounds__(RT) reduce_kernel(ReduceArgs a) {
     if (av < 0) return;
     const bool last = (av == a.R);
     const int first_src = (added == 0) ? 1 : added;
+    const f32x4 *init = (added == 0) ? reinterpret_cast<const f32x4 *>(a.src[0])
+                                     : reinterpret_cast<const f32x4 *>(a.acc);
 
-    for (int64_t base = beg + tid; base < end; base += (int64_t)RT * RU) {
+    // One step: RU vectors per thread.  Loads of up to KB sources are issued
+    // together (bytes in flight hide HBM latency), then added in summation
+    // order.  `full`: every vector of the step is inside the range.  Every
+    // byte is touched once, so loads and stores carry the streaming
+    // (nontemporal) hint.
+    auto step = [&](int64_t base, bool full) {
       f32x4 v[RU];
 #pragma unroll
       for (int q = 0; q < RU; ++q) {
         const int64_t i = base + (int64_t)q * RT;
-        if (i < end)
-          v[q] = (added == 0) ? reinterpret_cast<const f32x4 *>(a.src[0])[i]
-                              : reinterpret_cast<const f32x4 *>(a.acc)[i];
+        if (full || i < end) v[q] = __builtin_nontemporal_load(init + i);
       }
-      for (int s = first_src; s < av; ++s) {
-        const f32x4 *p = reinterpret_cast<const f32x4 *>(a.src[s]);
-        f32x4 t[RU];
+      for (int s0 = first_src; s0 < av; s0 += KB) {
+        f32x4 t[KB][RU];
 #pragma unroll
-        for (int q = 0; q < RU; ++q) {
-          const int64_t i = base + (int64_t)q * RT;
-          if (i < end) t[q] = p[i];
+        for (int k = 0; k < KB; ++k) {
+          if (s0 + k < av) {
+            const f32x4 *p = reinterpret_cast<const f32x4 *>(a.src[s0 + k]);
+#pragma unroll
+            for (int q = 0; q < RU; ++q) {
+              const int64_t i = base + (int64_t)q * RT;
+              if (full || i < end) t[k][q] = __builtin_nontemporal_load(p + i);
+            }
+          }
         }
 #pragma unroll
-        for (int q = 0; q < RU; ++q) v[q] += t[q];
+        for (int k = 0; k < KB; ++k)
+          if (s0 + k < av) {
+#pragma unroll
+            for (int q = 0; q < RU; ++q) v[q] += t[k][q];
+          }
       }
 #pragma unroll
       for (int q = 0; q < RU; ++q) {
         const int64_t i = base + (int64_t)q * RT;
-        if (i >= end) continue;
+        if (!full && i >= end) continue;
         if (last && OUT_BF16) {
           const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[q][0]) | ((uint32_t)f32_to_bf16_rne(v[q][1]) << 16);
           const uint32_t hi = (uint32_t)f32_to_bf16_rne(v[q][2]) | ((uint32_t)f32_to_bf16_rne(v[q][3]) << 16);
           reinterpret_cast<u32x2 *>(a.dst)[i] = u32x2{lo, hi};
         } else if (last) {
-          reinterpret_cast<f32x4 *>(a.dst)[i] = v[q];
+          __builtin_nontemporal_store(v[q], reinterpret_cast<f32x4 *>(a.dst) + i);
         } else {
-          reinterpret_cast<f32x4 *>(a.acc)[i] = v[q];
+          __builtin_nontemporal_store(v[q], reinterpret_cast<f32x4 *>(a.acc) + i);
         }
       }
-    }
+    };
+    int64_t w = beg;
+    for (; w + (int64_t)RT * RU <= end; w += (int64_t)RT * RU) step(w + tid, true);
+    if (w < end) step(w + tid, false);
     added = av;
   }
 
