@@ -156,8 +156,47 @@ def ticks_to_us(t, hz):
     return float(t) * 1e6 / hz
 
 
-def measure_tail_ag(fo, cfg, hz, reps=5, link_bw=wl.LINK_BW, naive=False):
-    """Exposed tail of the AG-GEMM under emulated ring arrivals (us)."""
+def _hip_wait_value():
+    """hipStreamWaitValue32 from the HIP runtime (for the sliced baseline)."""
+    import ctypes
+    L = ctypes.CDLL("libamdhip64.so")
+    f = L.hipStreamWaitValue32
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint, ctypes.c_uint32]
+    f.restype = ctypes.c_int
+    return f
+
+
+_SIDE = []
+
+
+def side_stream():
+    """The one side stream every emulated arrival runs on.  HIP multiplexes
+    streams over a few hardware queues; a stream created per measurement can
+    land on the main stream's queue, and the consumer kernel then waits behind
+    the whole arrival sequence."""
+    import torch
+    if not _SIDE:
+        _SIDE.append(torch.cuda.Stream())
+    return _SIDE[0]
+
+
+def _emulate(fo, dsts, srcs, order, nbytes, flags, e, es, side, link_bw):
+    """Enqueue ring arrivals of `order` on the side stream: chunk s lands at
+    s * B / BW, its copy issued B / BW earlier."""
+    import torch
+    rel = wl.ring_release_ns(nbytes, len(order), link_bw)
+    iss = [r - nbytes / link_bw * 1e9 for r in rel]
+    with torch.cuda.stream(side):
+        fo.fo_emulate_arrivals(dsts, srcs, rel, order, flags, e, es, issue_ns=iss, stream=side)
+
+
+def measure_tail_ag(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LINK_BW):
+    """Exposed tail of the AG-GEMM under emulated ring arrivals (us): time
+    from the last chunk's landing to the last output written.
+      flashoverlap: one persistent launch, ready-first claims over the flags;
+      strict: the same launch taking chunks exactly in priority order;
+      naive: wait for every chunk, then one GEMM launch;
+      sliced: one launch per chunk, each after a stream wait on its flag."""
     import torch
     xb, wb = wl.gemm_inputs(cfg, "gauss")
     staging = dev_bf16(xb)
@@ -167,38 +206,135 @@ def measure_tail_ag(fo, cfg, hz, reps=5, link_bw=wl.LINK_BW, naive=False):
     mc = cfg.m // cfg.R
     order = wl.ring_arrival_order(cfg.R, cfg.local)
     nbytes = mc * cfg.k * 2
-    rel = wl.ring_release_ns(nbytes, len(order), link_bw)
-    iss = [r - nbytes / link_bw * 1e9 for r in rel]
     flags = torch.zeros(cfg.R, dtype=torch.int32, device="cuda")
     es = torch.zeros(cfg.R + 2, dtype=torch.int64, device="cuda")
     gs = torch.zeros(2 * cfg.R + 2, dtype=torch.int64, device="cuda")
     ws = torch.zeros(fo.fo_workspace_bytes(cfg.m, cfg.n, cfg.k, cfg.R), dtype=torch.uint8, device="cuda")
-    side = torch.cuda.Stream()
+    side = side_stream()
     main = torch.cuda.current_stream()
+    wait_value = _hip_wait_value() if schedule == "sliced" else None
     tails, spans = [], []
-    for rep in range(reps):
+    for rep in range(reps + 1):   # the first repetition is a warm-up
         e = 100 + rep
         torch.cuda.synchronize()
-        with torch.cuda.stream(side):
-            fo.fo_emulate_arrivals([x[q * mc:(q + 1) * mc] for q in order],
-                                   [staging[q * mc:(q + 1) * mc] for q in order],
-                                   rel, order, flags, e, es, issue_ns=iss, stream=side)
-        if naive:
+        _emulate(fo, [x[q * mc:(q + 1) * mc] for q in order], [staging[q * mc:(q + 1) * mc] for q in order],
+                 order, nbytes, flags, e, es, side, link_bw)
+        if schedule == "naive":
             ev = torch.cuda.Event()
             ev.record(side)
             main.wait_event(ev)
             fo.fo_ag_gemm(x, w, y, fo.Schedule(nchunks=cfg.R, epoch=e, stamps=gs), ws)
+            done_idx = 2 * cfg.R + 1
+        elif schedule == "sliced":
+            one = torch.zeros(4, dtype=torch.int64, device="cuda")
+            for q in [cfg.local] + order:
+                if q != cfg.local:
+                    st = wait_value(main.cuda_stream, flags[q:q + 1].data_ptr(), e, 0, 0xFFFFFFFF)
+                    if st != 0:
+                        raise RuntimeError(f"hipStreamWaitValue32 failed ({st})")
+                rows = slice(q * mc, (q + 1) * mc)
+                fo.fo_ag_gemm(x[rows], w, y[rows], fo.Schedule(nchunks=1, epoch=e, stamps=one), ws)
+            gs = one
+            done_idx = 3
         else:
-            fo.fo_ag_gemm(x, w, y, fo.Schedule(nchunks=cfg.R, epoch=e, arrived=flags, stamps=gs,
+            mode = fo.FO_SCHED_STRICT if schedule == "strict" else fo.FO_SCHED_READY_FIRST
+            fo.fo_ag_gemm(x, w, y, fo.Schedule(nchunks=cfg.R, epoch=e, arrived=flags, stamps=gs, mode=mode,
                                                timeout_ns=5_000_000_000), ws)
+            done_idx = 2 * cfg.R + 1
         torch.cuda.synchronize()
         e_st = es.cpu().numpy().astype(np.int64)
         g_st = gs.cpu().numpy().astype(np.int64)
         last_arrival = max(e_st[1 + q] for q in order)
-        done = g_st[2 * cfg.R + 1]
-        tails.append(ticks_to_us(done - last_arrival, hz))
-        spans.append(ticks_to_us(last_arrival - e_st[0], hz))
+        if rep > 0:
+            tails.append(ticks_to_us(g_st[done_idx] - last_arrival, hz))
+            spans.append(ticks_to_us(last_arrival - e_st[0], hz))
     return float(np.median(tails)), float(np.median(spans))
+
+
+def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LINK_BW):
+    """Exposed tail of GEMM-RS + chunk reduce-add: the 7 incoming fp32
+    partials of the local shard land by emulated ring arrivals; the tail is
+    the time from the last landing to the bf16 shard written.
+      flashoverlap: GEMM-RS, then a reduce that adds partials as they land;
+      naive: wait for every partial, then GEMM-RS and the reduce."""
+    import torch
+    xb, wb = wl.gemm_inputs(cfg, "gauss")
+    x, w = dev_bf16(xb), dev_bf16(wb)
+    mc = cfg.m // cfg.R
+    part = torch.empty((cfg.m, cfg.n), device="cuda")
+    done = torch.zeros(cfg.R, dtype=torch.int32, device="cuda")
+    inc = wl.incoming_partials(cfg, "gauss")
+    staging = [None if a is None else torch.from_numpy(a).cuda() for a in inc]
+    inbox = [None if a is None else torch.empty_like(a) for a in staging]
+    shard = torch.empty((mc, cfg.n), dtype=torch.bfloat16, device="cuda")
+    order = wl.ring_arrival_order(cfg.R, cfg.local)
+    nbytes = mc * cfg.n * 4
+    flags = torch.zeros(cfg.R, dtype=torch.int32, device="cuda")
+    es = torch.zeros(cfg.R + 2, dtype=torch.int64, device="cuda")
+    rs_st = torch.zeros(2, dtype=torch.int64, device="cuda")
+    ws = torch.zeros(fo.fo_workspace_bytes(cfg.m, cfg.n, cfg.k, cfg.R), dtype=torch.uint8, device="cuda")
+    side = side_stream()
+    main = torch.cuda.current_stream()
+    tails = []
+    for rep in range(reps + 1):   # the first repetition is a warm-up
+        e = 200 + rep
+        rs_st.zero_()
+        torch.cuda.synchronize()
+        _emulate(fo, [inbox[q] for q in order], [staging[q] for q in order], order, nbytes, flags, e, es,
+                 side, link_bw)
+        if schedule == "naive":
+            ev = torch.cuda.Event()
+            ev.record(side)
+            main.wait_event(ev)
+        fo.fo_gemm_rs(x, w, part, done, fo.Schedule(nchunks=cfg.R, epoch=e), ws)
+        srcs = [part[cfg.local * mc:(cfg.local + 1) * mc] if q == cfg.local else inbox[q] for q in range(cfg.R)]
+        arrived = None if schedule == "naive" else flags
+        fo.fo_chunk_reduce(shard, srcs, fo.Schedule(nchunks=cfg.R, epoch=e, arrived=arrived, stamps=rs_st,
+                                                    timeout_ns=5_000_000_000))
+        torch.cuda.synchronize()
+        e_st = es.cpu().numpy().astype(np.int64)
+        last_arrival = max(e_st[1 + q] for q in order)
+        if rep > 0:
+            tails.append(ticks_to_us(int(rs_st[1].item()) - last_arrival, hz))
+    return float(np.median(tails))
+
+
+def measure_tail_dp(fo, cfg, hz, schedule="flashoverlap", reps=1, link_bw=wl.LINK_BW):
+    """Exposed tail of the DP gradient reduce-add (in place into the local
+    shard): the 7 peer chunks land by emulated arrivals in a seeded order; the
+    tail is the time from the last landing to the reduce's completion."""
+    import torch
+    n, R, local = cfg.n, cfg.R, 0
+    srcs = [torch.randn(n, device="cuda") * 1e-3 for _ in range(R)]
+    staging = [None if q == local else torch.randn(n, device="cuda") * 1e-3 for q in range(R)]
+    order = wl.seeded_permutation([q for q in range(R) if q != local], 4)
+    flags = torch.zeros(R, dtype=torch.int32, device="cuda")
+    es = torch.zeros(R + 2, dtype=torch.int64, device="cuda")
+    st = torch.zeros(2, dtype=torch.int64, device="cuda")
+    side = side_stream()
+    main = torch.cuda.current_stream()
+    tails = []
+    for rep in range(reps + 1):   # the first repetition is a warm-up
+        e = 300 + rep
+        st.zero_()
+        torch.cuda.synchronize()
+        _emulate(fo, [srcs[q] for q in order], [staging[q] for q in order], order, n * 4, flags, e, es, side,
+                 link_bw)
+        if schedule == "naive":
+            ev = torch.cuda.Event()
+            ev.record(side)
+            main.wait_event(ev)
+        fo.fo_chunk_reduce(srcs[local], srcs, fo.Schedule(nchunks=R, local=local, order=[local] + order,
+                                                          epoch=e, arrived=None if schedule == "naive" else flags,
+                                                          stamps=st, timeout_ns=5_000_000_000))
+        torch.cuda.synchronize()
+        e_st = es.cpu().numpy().astype(np.int64)
+        last_arrival = max(e_st[1 + q] for q in order)
+        if rep > 0:
+            tails.append(ticks_to_us(int(st[1].item()) - last_arrival, hz))
+    del srcs, staging
+    torch.cuda.empty_cache()
+    return float(np.median(tails))
 
 
 def chunk_gemm_us(fo, cfg, reps=20):
@@ -301,6 +437,7 @@ def main():
     cus, lds, hz = fo.fo_device_info()
     log(f"device: {torch.cuda.get_device_name(0)} CUs={cus} LDS/CU={lds} wall_clock={hz} Hz")
 
+    side_stream()   # created first, so it gets a hardware queue of its own
     path = Path(fo)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -369,14 +506,27 @@ def main():
         gbps, ms = reduce_rate(fo, wl.CFG4)
         out["dp_reduce_cfg4"] = {"us": round(ms * 1e3, 1), "gbps": round(gbps, 1),
                                  "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
-        cg = chunk_gemm_us(fo, c2)
-        tail, span = measure_tail_ag(fo, c2, hz)
-        ntail, _ = measure_tail_ag(fo, c2, hz, naive=True)
-        out["tail_cfg2_50GBps"] = {"flashoverlap_us": round(tail, 2), "naive_us": round(ntail, 2),
-                                   "chunk_gemm_us": round(cg, 2),
-                                   "tail_over_chunk_gemm": round(tail / cg, 3),
-                                   "last_arrival_us": round(span, 1)}
-        log(f"tail: flashoverlap {tail:.1f} us naive {ntail:.1f} us chunk gemm {cg:.1f} us")
+        tails = {}
+        for cfg, key in ((c2, "cfg2_ag_gemm"), (wl.CFG5, "cfg5_qkv_ag_gemm")):
+            cg = chunk_gemm_us(fo, cfg)
+            at70 = 2.0 * (cfg.m // cfg.R) * cfg.n * cfg.k / (0.7 * PEAK_BF16_TFLOPS * 1e12) * 1e6
+            row = {"chunk_gemm_us": round(cg, 2), "chunk_gemm_at_70pct_peak_us": round(at70, 2)}
+            for sched in ("flashoverlap", "strict", "naive", "sliced"):
+                if cfg is wl.CFG5 and sched in ("strict", "sliced"):
+                    continue
+                t, span = measure_tail_ag(fo, cfg, hz, sched)
+                row[sched + "_us"] = round(t, 2)
+                row["last_arrival_us"] = round(span, 1)
+            row["tail_over_chunk_gemm"] = round(row["flashoverlap_us"] / cg, 3)
+            tails[key] = row
+            log(f"tail {key}: {row}")
+        row = {s_ + "_us": round(measure_tail_rs(fo, c3, hz, s_), 2) for s_ in ("flashoverlap", "naive")}
+        tails["cfg3_gemm_rs_reduce"] = row
+        log(f"tail cfg3: {row}")
+        row = {s_ + "_us": round(measure_tail_dp(fo, wl.CFG4, hz, s_), 1) for s_ in ("flashoverlap", "naive")}
+        tails["cfg4_dp_reduce"] = row
+        log(f"tail cfg4: {row}")
+        out["tails_50GBps_links"] = tails
     if args.copy_calibration:
         copy_calibration()
     if not args.quick and not args.no_cpu:
