@@ -41,12 +41,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int NT = 256;   // threads per k-group (4 waves, one per SIMD)
+constexpr int NT = 256;   // threads in 4 waves, one per SIMD
 constexpr uint32_t kBufDword3 = 0x00020000u;   // raw buffer, 32-bit data format (gfx9)
 
 // Tile of BM x BN outputs; k staged through an LDS ring of STAGES buffers,
 // BK at a time (BK = 32 or 64: one or two MFMA k-steps per stage).  The
-// waves of one k-group form a WGM x WGN grid over the tile.
+// compute waves form a WGM x WGN grid over the tile.
 template <int BM, int BN, int BK, int STAGES, int WGM = 2, int WGN = 2>
 struct Cfg {
   static constexpr int WTM = BM / WGM, WTN = BN / WGN;   // wave tile
@@ -443,22 +443,18 @@ __device__ __forceinline__ void wait_later(int later) {
   wait_vm<0>();
 }
 
-// Compute waves: KG k-groups of WGM x WGN waves over the tile.  With KG = 2
-// group g multiplies k-step g of every stage into its own accumulators
-// (BK = 32 KG); the groups' tiles are summed in LDS before the store.
-// Without PC every 4 waves form a copy group that also issues the stage
-// copies (round v goes to copy group v % NCG).  With PC four extra producer
-// waves issue every copy and wait for it, so a compute wave never stalls
-// behind a full load queue: the two kinds of wave share each SIMD.
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int KG, bool PC>
+// Compute waves: a WGM x WGN grid of waves over the tile.  Without PC every 4
+// waves form a copy group that also issues the stage copies (round v goes to
+// copy group v % NCG).  With PC four extra producer waves issue every copy
+// and wait for it, so a compute wave never stalls behind a full load queue:
+// the two kinds of wave share each SIMD.
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool PC>
 __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
   using C = Cfg<BM, BN, BK, STAGES, WGM, WGN>;
-  constexpr int NCW = WGM * WGN * KG;          // compute waves
+  constexpr int NCW = WGM * WGN;               // compute waves
   constexpr int NTT = 64 * NCW + (PC ? NT : 0);
   constexpr int NCG = PC ? 1 : NTT / NT;       // copy groups of 4 waves
   static_assert(NTT % NT == 0, "whole copy groups");
-  static_assert(KG == 1 || C::KS == KG, "one k-step per k-group");
-  static_assert(!PC || KG == 1, "producer waves feed one k-group");
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
   __shared__ Unit s_unit;
   __shared__ int s_last;
@@ -469,9 +465,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
   const bool prod = !PC || wave < 4;                                     // issues stage copies
   const bool cons = !PC || wave >= 4;                                    // multiplies
   const int cwave = PC ? (wave >= 4 ? wave - 4 : 0) : wave;              // index among compute waves
-  const int grp = __builtin_amdgcn_readfirstlane(cwave / (WGM * WGN));  // k-group
-  const int gw = cwave % (WGM * WGN);                                    // wave in its k-group
-  const int wm = gw / WGN, wn = gw % WGN;
+  const int wm = cwave / WGN, wn = cwave % WGN;
   const int cg = __builtin_amdgcn_readfirstlane(wave >> 2);             // copy group
   const int cw = wave & 3;                                               // wave in its copy group
   const int gtid = tid & (NT - 1);                                       // thread in its copy group
@@ -563,30 +557,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
       constexpr int buf = decltype(bufc)::value;
       const char *A = lds + buf * C::STAGE;
       const char *B = A + C::A_BYTES;
-      if constexpr (KG > 1) {
-        // this group's k-step of the stage: read its fragments, then the MFMAs
-        const int ch = grp * 4 + (lane >> 4);
-        const int swz = ((ch ^ C::swz(lane & 15)) << 4);
-        bf16x8 af[C::FM], bfr[C::FN];
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-          af[i] = *reinterpret_cast<const bf16x8 *>(A + (wm * C::WTM + i * 16 + (lane & 15)) * C::ROWB + swz);
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8 *>(B + (wn * C::WTN + j * 16 + (lane & 15)) * C::ROWB + swz);
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j) {
-            if (first)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            else
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-          }
-        __builtin_amdgcn_sched_group_barrier(0x100, C::FM + C::FN, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, C::FM * C::FN, 0);
-        return;
-      } else if constexpr (PC && C::KS == 2) {
+      if constexpr (PC && C::KS == 2) {
         // Both k-steps with few live fragments: k-step 0's MFMAs go column by
         // column; after column j its W fragment is dead and k-step 1's W
         // fragment j is read in its place, and k-step 1's X fragments are read
@@ -745,24 +716,17 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
       const bool wt = !to_out || a.done_flags != nullptr;
 #pragma unroll
       for (int h = 0; h < HALVES; ++h) {
-        // the last k-group stores its tile, then each other group adds its
-        // own in turn (group KG-1 + ... + group 0, a fixed order)
+        __syncthreads();
+        if (cons && (HALVES == 1 || wm == h)) {
 #pragma unroll
-        for (int g = KG - 1; g >= 0; --g) {
-          __syncthreads();
-          if (cons && grp == g && (HALVES == 1 || wm == h)) {
+          for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-            for (int i = 0; i < C::FM; ++i)
+            for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-              for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                  const int r = (HALVES == 1 ? wm * C::WTM : 0) + i * 16 + (lane >> 4) * 4 + v;
-                  float *q = stg + r * SROW + wn * C::WTN + j * 16 + (lane & 15);
-                  if (g == KG - 1) *q = acc[i][j][v];
-                  else *q = *q + acc[i][j][v];
-                }
-          }
+              for (int v = 0; v < 4; ++v) {
+                const int r = (HALVES == 1 ? wm * C::WTM : 0) + i * 16 + (lane >> 4) * 4 + v;
+                stg[r * SROW + wn * C::WTN + j * 16 + (lane & 15)] = acc[i][j][v];
+              }
         }
         __syncthreads();
         for (int cidx = tid; cidx < HROWS * CPR; cidx += NTT) {
@@ -847,18 +811,18 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
 
 template <int BM, int BN, int BK, int STAGES>
 __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
-  gemm_body<BM, BN, BK, STAGES, 2, 2, 1, false>(a);
+  gemm_body<BM, BN, BK, STAGES, 2, 2, false>(a);
 }
 
-// Two k-groups: two waves per SIMD.  The register cap leaves VGPRs free on
-// every SIMD, so a one-wave kernel of a copy-engine emulator still fits
-// beside the persistent grid.  On gfx950 the compiler counts this attribute
-// in pairs of the unified VGPR/AGPR file: 120 caps each wave at 240, so two
-// waves leave 32 of each lane's 512 registers free.
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, int KG, bool PC>
+// Eight waves: two per SIMD.  The register cap leaves VGPRs free on every
+// SIMD, so a one-wave kernel of a copy-engine emulator still fits beside the
+// persistent grid.  On gfx950 the compiler counts this attribute in pairs of
+// the unified VGPR/AGPR file: 120 caps each wave at 240, so two waves leave
+// 32 of each lane's 512 registers free.
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool PC>
 __global__ void __launch_bounds__(2 * NT, 1) __attribute__((amdgpu_num_vgpr(120)))
 gemm_kernel_w8(GemmArgs a) {
-  gemm_body<BM, BN, BK, STAGES, WGM, WGN, KG, PC>(a);
+  gemm_body<BM, BN, BK, STAGES, WGM, WGN, PC>(a);
 }
 
 namespace {
@@ -926,11 +890,11 @@ size_t partial_slot_bytes(const TileCfg &t) { return (size_t)t.bm * t.bn * sizeo
 
 hipError_t launch_gemm(const GemmArgs &a, const TileCfg &t, hipStream_t stream) {
   if (t.bm == 256 && t.bn == 256)
-    hipLaunchKernelGGL((gemm_kernel_w8<256, 256, 32, 4, 2, 4, 1, false>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel_w8<256, 256, 32, 4, 2, 4, false>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
   else if (t.bm == 256 && t.bn == 160)
     hipLaunchKernelGGL((gemm_kernel<256, 160, 64, 3>), dim3(a.grid), dim3(NT), 0, stream, a);
   else if (t.bm == 128 && t.bn == 224)
-    hipLaunchKernelGGL((gemm_kernel_w8<128, 224, 64, 3, 2, 2, 1, true>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel_w8<128, 224, 64, 3, 2, 2, true>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
   else if (t.bm == 128 && t.bn == 128)
     hipLaunchKernelGGL((gemm_kernel<128, 128, 64, 4>), dim3(a.grid), dim3(NT), 0, stream, a);
   else
