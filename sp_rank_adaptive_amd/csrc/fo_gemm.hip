@@ -143,6 +143,27 @@ __device__ __forceinline__ uint32_t group_units(const GemmArgs &a, int c, int g)
   return (uint32_t)(a.gtiles[g] * a.split[c]);
 }
 
+// Without arrival flags every chunk is present from the start, so each
+// workgroup's first unit is assigned statically: the q-th workgroup of XCD g
+// takes the q-th unit of group g in priority order, with no atomic.  The
+// claim counter of (c, g) then counts the units after these: this returns
+// how many units of (c, g) the static assignment covers.
+__device__ __forceinline__ uint32_t static_units(const GemmArgs &a, int c, int g) {
+  if (a.arrived != nullptr) return 0;
+  const int wgs = (a.grid - g + XCDS - 1) / XCDS;   // workgroups on XCD g
+  int off = 0;
+  for (int sidx = 0; sidx < a.R; ++sidx) {
+    const int cc = a.order[sidx];
+    const int nu = (int)group_units(a, cc, g);
+    if (cc == c) {
+      const int left = wgs - off;
+      return left <= 0 ? 0u : (uint32_t)(left < nu ? left : nu);
+    }
+    off += nu;
+  }
+  return 0u;
+}
+
 // Group g of a chunk is rectangle (g / gn, g % gn) of the chunk's tile grid,
 // cut into gm row bands and gn column bands; its tiles are numbered row by
 // row.  Rectangle g is the XCD g queue, so an XCD streams a few X row blocks
@@ -170,11 +191,31 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
   const int R = a.R;
   uint64_t wait_from = 0;
   Unit r{-1, 0, 0, 0, 0, 0};
-  // First claim of a workgroup: its own XCD's group, the q-th unit in
-  // priority order over the landed chunks, taken as if no unit were claimed
-  // yet (true at the start of a call), so only the flags are read before the
-  // fetch-add; if the fetch-add shows the group exhausted, the general claim
-  // below takes over.
+  // First claim of a workgroup: the q-th unit of its own XCD's group in
+  // priority order (q = its rank on the XCD).  Without flags it is taken
+  // statically (see static_units).  With flags it is the q-th unit over the
+  // landed chunks, taken as if no unit were claimed yet (true at the start
+  // of a call), so only the flags are read before the fetch-add; if that
+  // shows the group exhausted, the general claim below takes over.
+  if (rank_hint >= 0 && a.arrived == nullptr) {
+    uint32_t q = (uint32_t)rank_hint;
+    rank_hint = -1;
+    for (int sidx = 0; sidx < R; ++sidx) {
+      const int c = a.order[sidx];
+      const uint32_t nu = group_units(a, c, xg);
+      if (q < nu) {
+        const int S = a.split[c];
+        const int tl = (int)q / S;
+        r.c = c;
+        r.sp = (int)q - tl * S;
+        group_tile(a, xg, tl, r.tm, r.tn);
+        r.first = (xg == 0 && q == 0);
+        r.red = 0;
+        return r;
+      }
+      q -= nu;
+    }
+  }
   if (rank_hint >= 0 && !a.strict) {
     bool ok = false;
     if (lane < R) {
@@ -231,7 +272,7 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
       if (pidx < R * XCDS) {
         const int sidx = pidx / XCDS, g = pidx % XCDS;
         const int c = a.order[sidx];
-        const uint32_t cnt = load_relaxed(a.ws32 + WS_CLAIM + c * XCDS + g);
+        const uint32_t cnt = load_relaxed(a.ws32 + WS_CLAIM + c * XCDS + g) + static_units(a, c, g);
         const uint32_t tot = group_units(a, c, g);
         lv = cnt < tot ? tot - cnt : 0;
       }
@@ -333,7 +374,7 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
       }
       uint32_t u = 0;
       if (lane == 0) u = fetch_add_relaxed(a.ws32 + WS_CLAIM + c * XCDS + pick_g, 1u);
-      u = __builtin_amdgcn_readfirstlane(u);
+      u = __builtin_amdgcn_readfirstlane(u) + static_units(a, c, pick_g);
       if (u < group_units(a, c, pick_g)) {
         const int S = a.split[c];
         const int tl = (int)u / S;
