@@ -484,6 +484,17 @@ __device__ __forceinline__ void wait_later(int later) {
   wait_vm<0>();
 }
 
+// The kernel's argument block behind a pointer the compiler cannot see
+// through, taken once per unit: without it the compiler hoists every argument
+// field the unit loop may read into registers for the whole kernel (and spills
+// them), where the tiles need those registers for accumulators and fragments.
+// The fields are reloaded with scalar loads from the argument segment.
+__device__ __forceinline__ const GemmArgs &unit_args() {
+  auto p = (const __attribute__((address_space(4))) GemmArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return *(const GemmArgs *)p;
+}
+
 // Compute waves: a WGM x WGN grid of waves over the tile.  Without PC every 4
 // waves form a copy group that also issues the stage copies (round v goes to
 // copy group v % NCG).  With PC four extra producer waves issue every copy
@@ -522,6 +533,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
   if (blockIdx.x == 0 && tid == 0 && a.stamps) store_u64_relaxed(a.stamps + 2 * a.R, now_ticks());
 
   for (;;) {
+    const GemmArgs &a = unit_args();
     if (wave == 0) {
       const Unit u = claim_unit(a, st, xg, rank_hint);
       if (lane == 0) s_unit = u;

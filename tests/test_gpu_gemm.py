@@ -92,6 +92,39 @@ def test_ag_gemm_ragged_shapes(fo, orc, m, n, k, R):
             check_tolerance(host(y), ref, what="gauss")
 
 
+# every compiled tile layout (FO_TILE=BMxBN picks one)
+TILES = ["256x256", "256x160", "128x224", "128x128"]
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_every_tile_layout_ragged_int_exact(fo, orc, tile, monkeypatch):
+    """Each layout on ragged shapes (partial row/column tiles, k not a
+    multiple of the stage depth, odd n for the scalar store path, one and
+    two k stages), unsplit and split, AG and GEMM-RS, fp32 and bf16 out."""
+    monkeypatch.setenv("FO_TILE", tile)
+    R = 2
+    for m, n, k in [(600, 522, 200), (520, 264, 8), (520, 264, 40), (1040, 520, 1000)]:
+        log(f"case: tile {tile} {m}x{n}x{k} R={R}")
+        xb = wl.bf16_operand((m, k), "int", 1.0, 1200 + k)
+        wb = wl.bf16_operand((n, k), "int", 1.0, 1201 + n)
+        ref = orc.gemm(xb, wb)
+        x, w = dev_bf16(xb), dev_bf16(wb)
+        ws = torch.zeros(4 * fo.fo_workspace_bytes(m, n, k, R), dtype=torch.uint8, device="cuda")
+        for split in (None, [3, 1], [1, 2]):
+            kw = {} if split is None else {"split": split}
+            y, _ = run_ag(fo, x, w, R, ws=ws, **kw)
+            check_exact(host(y), ref, f"{tile} {m}x{n}x{k} split {split}")
+        part = torch.full((m, n), float("nan"), device="cuda")
+        done = torch.zeros(R, dtype=torch.int32, device="cuda")
+        e = EP.next()
+        fo.fo_gemm_rs(x, w, part, done, fo.Schedule(nchunks=R, epoch=e), ws)
+        torch.cuda.synchronize()
+        assert (host(done) == e).all()
+        check_exact(host(part), ref, f"{tile} {m}x{n}x{k} gemm_rs")
+        y, _ = run_ag(fo, x, w, R, y_dtype=torch.bfloat16, ws=ws)
+        assert np.array_equal(host(y), orc.f64_to_bf16(ref)), f"{tile} bf16 out"
+
+
 def test_ag_gemm_bf16_output(fo, orc):
     c = wl.CFG1
     xb, wb, x, w = gemm_case(c, "gauss")
