@@ -107,7 +107,8 @@ typedef struct fo_schedule {
                                   arrived == NULL, otherwise the last peer in
                                   `order` (the chunk expected to land last) is
                                   split so its tiles fill the GPU.             */
-  int32_t         max_workgroups; /* 0 = auto                                  */
+  int32_t         max_workgroups; /* 0 = auto.  fo_chunk_reduce may exceed it
+                                     so no workgroup owns more than 1 GiB.     */
   int32_t         reserved;
 } fo_schedule;
 
@@ -155,9 +156,10 @@ fo_status fo_gemm_rs(const void *x, const void *w, float *partial, uint32_t *don
  *   dst   device, n elements of dst_dtype (FO_F32 or FO_BF16).
  * dst = srcs[local] + srcs[order'[0]] + srcs[order'[1]] + ... in fp32, added
  * left to right, where order' is `order` without `local`.  With s->arrived,
- * a source is read only after its flag shows the epoch; each pass adds the
- * longest run of pending sources (in that order) that have all landed, so the
- * bits never depend on arrival timing.
+ * a source is read only after its flag shows the epoch (with system-scope
+ * coherent loads, so a copy engine may have written it during the call); each
+ * pass adds the longest run of pending sources (in that order) that have all
+ * landed, so the bits never depend on arrival timing.
  * Intermediate fp32 sums of a multi-pass reduce are kept in dst when dst is
  * fp32 (dst may equal srcs[local]: in place) and in srcs[local] when dst is
  * bf16 (srcs[local] is then overwritten).  n % 4 == 0 and 16-byte aligned
@@ -170,8 +172,10 @@ fo_status fo_chunk_reduce(void *dst, fo_dtype dst_dtype, const float *const *src
  * 0..count-1 in array order: wait until issue_ns[i] after the call's start
  * t0, copy bytes[i] from src[i] to dst[i] on a DMA (SDMA) engine, wait until
  * release_ns[i] after t0 and after the copy, then record the device wall clock
- * in stamps[1 + chunk_id[i]] and store arrived[chunk_id[i]] = epoch with
- * release semantics.  stamps[0] receives t0.
+ * in stamps[1 + chunk_id[i]] and store arrived[chunk_id[i]] = epoch, written
+ * through to memory (the copy has completed before the store, in stream
+ * order; a consumer acquires before reading the chunk).  stamps[0] receives
+ * t0.
  *   dst, src, bytes, issue_ns, release_ns, chunk_id: host arrays [count];
  *   issue_ns may be NULL (each copy is issued at its release time).
  *   arrived: device [R]; stamps: device [1 + max chunk id + 1], optional. */

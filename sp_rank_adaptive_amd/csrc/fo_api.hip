@@ -346,9 +346,13 @@ fo_status fo_chunk_reduce(void *dst, fo_dtype dst_dtype, const float *const *src
   // arrival flags, wave slots stay free for the emulator's one-wave kernels.
   int grid = s->max_workgroups > 0 ? s->max_workgroups : I->cus * 4;
   const int64_t min_per = 256 * 2;   // one full step of the workgroup
+  // a workgroup's range is addressed with 32-bit byte offsets (at most 1 GiB
+  // per workgroup; the grid grows past max_workgroups if it must)
+  const int64_t max_per = ((int64_t)1 << 30) / 16;
   int64_t per = (a.n4 + grid - 1) / grid;
   if (per < min_per) per = min_per;
   per = (per + 255) / 256 * 256;
+  if (per > max_per) per = max_per;
   a.per_wg4 = per;
   grid = (int)((a.n4 + per - 1) / per);
   hipError_t e = launch_reduce(a, grid, static_cast<hipStream_t>(stream));

@@ -6,7 +6,8 @@
 // from a staging region of the same HBM on a DMA engine, enqueued between these
 // kernels on a side stream.  A timer kernel holds the stream until the copy's
 // issue time; a flag kernel waits for the chunk's release time, records the
-// device wall clock and stores the chunk's epoch flag with release semantics.
+// device wall clock and stores the chunk's epoch flag, written through to
+// memory.
 // Each kernel is a single wave that sleeps between clock reads.
 #include "fo_device.hpp"
 #include "fo_internal.hpp"
@@ -31,7 +32,12 @@ __global__ void __launch_bounds__(64) emu_flag_kernel(const uint64_t *t0_slot, u
   const uint64_t t0 = __hip_atomic_load(t0_slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   sleep_until(t0, release_ticks);
   if (stamp_slot) store_u64_relaxed(stamp_slot, now_ticks());
-  store_release(flag, epoch);
+  // The chunk's bytes were written by the copy engine, which finished before
+  // this kernel started: there is nothing of this kernel's own to release.  A
+  // release store would write back this XCD's whole L2 (dirty lines of the
+  // concurrent GEMM included) before the flag becomes visible, delaying it by
+  // microseconds; the flag store itself is written through to memory.
+  __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   sleep_until(t0, next_issue_ticks);
 }
 

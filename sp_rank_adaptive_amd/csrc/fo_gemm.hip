@@ -388,20 +388,32 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
       continue;   // lost the race for the last unit: look again
     }
     if (has_work == 0 && red_left == 0) { r.c = -1; return r; }   // every unit claimed
-    // work left only in chunks that have not landed: wait
-    if (load_relaxed(a.ws32 + WS_ABORT)) { r.c = -2; return r; }
-    const uint64_t t = now_ticks();
-    if (wait_from == 0) wait_from = t;
-    if (t - wait_from > a.timeout_ticks) {
-      if (lane == 0) {
-        if (a.status) __hip_atomic_store(a.status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_SYSTEM);
-        __hip_atomic_store(a.ws32 + WS_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Work is left only in chunks that have not landed (or, in STRICT mode,
+    // behind one), and only a landing can change that: other workgroups'
+    // claims only remove work.  So until the landed set changes, only the
+    // flags and the abort word are read, one line each, rather than every
+    // claim counter: hundreds of waiting workgroups would otherwise queue on
+    // the counters' memory channel and delay the claims after a landing.
+    if (wait_from == 0) wait_from = now_ticks();
+    for (;;) {
+      if (load_relaxed(a.ws32 + WS_ABORT)) { r.c = -2; return r; }
+      if (now_ticks() - wait_from > a.timeout_ticks) {
+        if (lane == 0) {
+          if (a.status) __hip_atomic_store(a.status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_SYSTEM);
+          __hip_atomic_store(a.ws32 + WS_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        r.c = -2;
+        return r;
       }
-      r.c = -2;
-      return r;
+      __builtin_amdgcn_s_sleep(4);
+      bool now_ok = false;
+      if (lane < R) {
+        const int c = a.order[lane];
+        now_ok = a.arrived == nullptr || c == a.local || epoch_reached(load_relaxed(a.arrived + c), a.epoch);
+      }
+      if (__ballot(now_ok) != landed) break;
     }
-    __builtin_amdgcn_s_sleep(4);
   }
 }
 

@@ -21,7 +21,19 @@ constexpr int RT = 256;  // threads per workgroup
 constexpr int RU = 2;    // vectors per thread per step
 constexpr int KB = 8;    // sources whose loads are issued together
 
-template <bool OUT_BF16>
+// 16 bytes of a source that a copy engine wrote after this grid started, read
+// coherently at system scope (cache policy sc0 sc1, plus the streaming hint):
+// a line of it that an XCD's L2 still holds from before the copy is not
+// returned.  Every byte of a source is read once, so nothing is lost by not
+// caching it, and no workgroup needs an acquire fence, which would invalidate
+// its XCD's whole L2 (once per workgroup, several microseconds in total).
+__device__ __forceinline__ f32x4 load_landed(__amdgpu_buffer_rsrc_t rs, int64_t byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)byte_off, 0, 1 | 2 | 16));
+}
+
+// PEER: sources are gated by arrival flags (read with load_landed);
+// otherwise every source was written before the launch.
+template <bool OUT_BF16, bool PEER>
 __global__ void __launch_bounds__(RT) reduce_kernel(ReduceArgs a) {
   __shared__ int s_avail;
   const int tid = threadIdx.x;
@@ -40,10 +52,7 @@ __global__ void __launch_bounds__(RT) reduce_kernel(ReduceArgs a) {
         while (av < a.R && (av == 0 || a.arrived == nullptr ||
                             epoch_reached(load_relaxed(a.arrived + a.chunk_of[av]), a.epoch)))
           ++av;
-        if (av > added) {
-          if (a.arrived) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
-          break;
-        }
+        if (av > added) break;
         const uint64_t t = now_ticks();
         if (wait_from == 0) wait_from = t;
         if (t - wait_from > a.timeout_ticks) {
@@ -83,10 +92,21 @@ __global__ void __launch_bounds__(RT) reduce_kernel(ReduceArgs a) {
         for (int k = 0; k < KB; ++k) {
           if (s0 + k < av) {
             const f32x4 *p = reinterpret_cast<const f32x4 *>(a.src[s0 + k]);
+            if constexpr (PEER) {
+              // this workgroup's range of the source; offsets past it read zero
+              const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                  (void *)(p + beg), (short)0, (int)((end - beg) * 16), 0x00020000);
 #pragma unroll
-            for (int q = 0; q < RU; ++q) {
-              const int64_t i = base + (int64_t)q * RT;
-              if (full || i < end) t[k][q] = __builtin_nontemporal_load(p + i);
+              for (int q = 0; q < RU; ++q) {
+                const int64_t i = base + (int64_t)q * RT;
+                if (full || i < end) t[k][q] = load_landed(rs, (i - beg) * 16);
+              }
+            } else {
+#pragma unroll
+              for (int q = 0; q < RU; ++q) {
+                const int64_t i = base + (int64_t)q * RT;
+                if (full || i < end) t[k][q] = __builtin_nontemporal_load(p + i);
+              }
             }
           }
         }
@@ -126,10 +146,15 @@ __global__ void __launch_bounds__(RT) reduce_kernel(ReduceArgs a) {
 }
 
 hipError_t launch_reduce(const ReduceArgs &a, int grid, hipStream_t stream) {
-  if (a.dst_bf16)
-    hipLaunchKernelGGL(reduce_kernel<true>, dim3(grid), dim3(RT), 0, stream, a);
+  const bool peer = a.arrived != nullptr;
+  if (a.dst_bf16 && peer)
+    hipLaunchKernelGGL((reduce_kernel<true, true>), dim3(grid), dim3(RT), 0, stream, a);
+  else if (a.dst_bf16)
+    hipLaunchKernelGGL((reduce_kernel<true, false>), dim3(grid), dim3(RT), 0, stream, a);
+  else if (peer)
+    hipLaunchKernelGGL((reduce_kernel<false, true>), dim3(grid), dim3(RT), 0, stream, a);
   else
-    hipLaunchKernelGGL(reduce_kernel<false>, dim3(grid), dim3(RT), 0, stream, a);
+    hipLaunchKernelGGL((reduce_kernel<false, false>), dim3(grid), dim3(RT), 0, stream, a);
   return hipGetLastError();
 }
 
