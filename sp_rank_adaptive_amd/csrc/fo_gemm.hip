@@ -1,6 +1,6 @@
 // Persistent chunked GEMM for gfx950: bf16 MFMA (16x16x32), fp32 accumulate,
-// LDS-staged double-buffered tiles fed by a register prefetch pipeline, work
-// claimed chunk by chunk as the chunks' epoch flags show them landed.
+// operand tiles copied straight into an LDS ring by the buffer-load DMA path,
+// work claimed chunk by chunk as the chunks' epoch flags show them landed.
 //
 // This is the partitioned computation of FlashOverlap (euno.news
 // "Methodology" step 2: the GEMM is split into sub-tasks on the same row
@@ -12,8 +12,12 @@
 // stays local is produced last (Flash-RS).
 //
 // Layout and schedule
-//  - One workgroup = 4 waves (one per SIMD) computing a BM x BN output tile;
-//    each wave owns a (BM/2) x (BN/2) quadrant of 16x16 MFMA blocks.
+//  - One persistent workgroup per CU computes BM x BN output tiles.  Its
+//    compute waves form a WGM x WGN grid, each wave owning a block of 16x16
+//    MFMA tiles: 4 waves (one per SIMD) or 8 (two per SIMD, under a register
+//    cap that leaves room for a one-wave kernel beside the grid).  In the
+//    producer/consumer layout 4 of the 8 waves only issue and wait for the
+//    copies while the other 4 only read fragments and multiply.
 //  - Operand tiles of BM x BK (X rows) and BN x BK (W rows = output columns)
 //    sit in an LDS ring of STAGES buffers with a 16-byte XOR swizzle, so the
 //    fragment reads of 8 consecutive rows hit distinct bank groups.
@@ -41,7 +45,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int NT = 256;   // threads in 4 waves, one per SIMD
+constexpr int NT = 256;   // threads of 4 waves (one copy group)
 constexpr uint32_t kBufDword3 = 0x00020000u;   // raw buffer, 32-bit data format (gfx9)
 
 // Tile of BM x BN outputs; k staged through an LDS ring of STAGES buffers,
@@ -78,10 +82,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
-// 16 bytes per lane from a buffer resource straight into LDS: lane L's bytes
-// land at m0 + 16 L.  Issued from asm so the compiler does not wait for
-// every outstanding copy before each LDS read; waits are explicit
-// (wait_vm) and a workgroup barrier follows them before any read.
 // 16-byte store written through every cache level to memory (system-scope
 // cache policy).  Output that another agent or XCD consumes is stored this
 // way, so a unit only has to wait for its own stores to be acknowledged
@@ -96,6 +96,10 @@ __device__ __forceinline__ void wait_stores() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// 16 bytes per lane from a buffer resource straight into LDS: lane L's bytes
+// land at m0 + 16 L.  Issued from asm so the compiler does not wait for
+// every outstanding copy before each LDS read; waits are explicit
+// (wait_vm) and a workgroup barrier follows them before any read.
 __device__ __forceinline__ void dma16(uint32_t m0, int voff, __amdgpu_buffer_rsrc_t rs, int soff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(rs),
@@ -485,8 +489,6 @@ __device__ __forceinline__ void reduce_unit(const GemmArgs &a, int c, int tile, 
   }
 }
 
-// Wait for this wave's copies of stage j when `later` stages issued after it
-// may stay in flight (VR copies per stage and wave).
 // Wait for this wave's copies of stage j when `later` stages issued after it
 // may stay in flight (VR copies per stage and wave).
 template <int VR, int STAGES>
