@@ -509,17 +509,22 @@ __device__ __forceinline__ const GemmArgs &unit_args() {
   return *(const GemmArgs *)p;
 }
 
-// Compute waves: a WGM x WGN grid of waves over the tile.  Without PC every 4
-// waves form a copy group that also issues the stage copies (round v goes to
-// copy group v % NCG).  With PC four extra producer waves issue every copy
-// and wait for it, so a compute wave never stalls behind a full load queue:
-// the two kinds of wave share each SIMD.
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool PC>
+// Compute waves: a WGM x WGN grid of waves over the tile.  Copies:
+//  - default: every 4 waves form a copy group that also issues the stage
+//    copies (round v goes to copy group v % NCG);
+//  - PC: four extra producer waves issue every copy and wait for it, so a
+//    compute wave never stalls behind a full load queue; the two kinds of
+//    wave share each SIMD;
+//  - HP (8 compute waves): waves 0-3 issue every copy and also multiply,
+//    waves 4-7 only multiply.  A wave that issues a burst of copies stalls
+//    until the load queue takes them; the other wave on its SIMD then keeps
+//    the matrix core busy, where in the default layout both would stall.
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool PC, bool HP = false>
 __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
   using C = Cfg<BM, BN, BK, STAGES, WGM, WGN>;
   constexpr int NCW = WGM * WGN;               // compute waves
   constexpr int NTT = 64 * NCW + (PC ? NT : 0);
-  constexpr int NCG = PC ? 1 : NTT / NT;       // copy groups of 4 waves
+  constexpr int NCG = (PC || HP) ? 1 : NTT / NT;   // copy groups of 4 waves
   static_assert(NTT % NT == 0, "whole copy groups");
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
   __shared__ Unit s_unit;
@@ -528,7 +533,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const bool prod = !PC || wave < 4;                                     // issues stage copies
+  const bool prod = !(PC || HP) || wave < 4;                             // issues stage copies
   const bool cons = !PC || wave >= 4;                                    // multiplies
   const int cwave = PC ? (wave >= 4 ? wave - 4 : 0) : wave;              // index among compute waves
   const int wm = cwave / WGN, wn = cwave % WGN;
@@ -886,10 +891,10 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
 // persistent grid.  On gfx950 the compiler counts this attribute in pairs of
 // the unified VGPR/AGPR file: 120 caps each wave at 240, so two waves leave
 // 32 of each lane's 512 registers free.
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool PC>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool PC, bool HP = false>
 __global__ void __launch_bounds__(2 * NT, 1) __attribute__((amdgpu_num_vgpr(120)))
 gemm_kernel_w8(GemmArgs a) {
-  gemm_body<BM, BN, BK, STAGES, WGM, WGN, PC>(a);
+  gemm_body<BM, BN, BK, STAGES, WGM, WGN, PC, HP>(a);
 }
 
 namespace {
@@ -900,9 +905,9 @@ struct Cand {
 };
 
 // Tile configurations compiled into the library (the launcher below maps
-// each to its wave layout): 256 x 256 as 8 waves in a 2 x 4 grid; 128 x 224
-// as 4 producer waves + 2 x 2 compute waves; 256 x 160 and 128 x 128 as
-// 2 x 2 waves.
+// each to its wave layout): 256 x 256 as 8 waves in a 2 x 4 grid, half of
+// them also issuing the copies (HP); 128 x 224 as 4 producer waves + 2 x 2
+// compute waves; 256 x 160 and 128 x 128 as 2 x 2 waves.
 // The 256 x 160 kernel holds almost every register of a SIMD.
 constexpr Cand kCands[] = {{256, 256, 32, 4, true}, {256, 160, 64, 3, false},
                            {128, 224, 64, 3, true}, {128, 128, 64, 4, true}};
@@ -957,7 +962,7 @@ size_t partial_slot_bytes(const TileCfg &t) { return (size_t)t.bm * t.bn * sizeo
 
 hipError_t launch_gemm(const GemmArgs &a, const TileCfg &t, hipStream_t stream) {
   if (t.bm == 256 && t.bn == 256)
-    hipLaunchKernelGGL((gemm_kernel_w8<256, 256, 32, 4, 2, 4, false>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel_w8<256, 256, 32, 4, 2, 4, false, true>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
   else if (t.bm == 256 && t.bn == 160)
     hipLaunchKernelGGL((gemm_kernel<256, 160, 64, 3>), dim3(a.grid), dim3(NT), 0, stream, a);
   else if (t.bm == 128 && t.bn == 224)
