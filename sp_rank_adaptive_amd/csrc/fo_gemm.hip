@@ -771,7 +771,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
       constexpr int SROW = (BM / 2 * (BN + 4) * 4 <= C::LDS) ? BN + 4 : BN;
       constexpr int HALVES = (BM * SROW * 4 <= C::LDS) ? 1 : 2;
       static_assert(BM / HALVES * SROW * 4 <= C::LDS, "epilogue staging");
-      static_assert(HALVES == 1 || HALVES == WGM, "a staging pass holds whole wave rows");
+      static_assert(WGM % HALVES == 0, "a staging pass holds whole wave rows");
+      constexpr int WPP = WGM / HALVES;                             // wave rows per pass
       constexpr int HROWS = BM / HALVES;
       constexpr int CPR = BN / 4;                                   // 16-byte pieces per row
       float *stg = reinterpret_cast<float *>(lds);
@@ -789,14 +790,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
 #pragma unroll
       for (int h = 0; h < HALVES; ++h) {
         __syncthreads();
-        if (cons && (HALVES == 1 || wm == h)) {
+        if (cons && wm / WPP == h) {
 #pragma unroll
           for (int i = 0; i < C::FM; ++i)
 #pragma unroll
             for (int j = 0; j < C::FN; ++j)
 #pragma unroll
               for (int v = 0; v < 4; ++v) {
-                const int r = (HALVES == 1 ? wm * C::WTM : 0) + i * 16 + (lane >> 4) * 4 + v;
+                const int r = (wm % WPP) * C::WTM + i * 16 + (lane >> 4) * 4 + v;
                 stg[r * SROW + wn * C::WTN + j * 16 + (lane & 15)] = acc[i][j][v];
               }
         }
@@ -905,11 +906,11 @@ struct Cand {
 };
 
 // Tile configurations compiled into the library (the launcher below maps
-// each to its wave layout): 256 x 256 as 8 waves in a 2 x 4 grid, half of
-// them also issuing the copies (HP); 128 x 224 as 4 producer waves + 2 x 2
-// compute waves; 256 x 160 and 128 x 128 as 2 x 2 waves.
-// The 256 x 160 kernel holds almost every register of a SIMD.
-constexpr Cand kCands[] = {{256, 256, 32, 4, true}, {256, 160, 64, 3, false},
+// each to its wave layout): 256 x 256 as 8 waves in a 2 x 4 grid and 256 x 160
+// as 8 waves in a 4 x 2 grid, half of them also issuing the copies (HP);
+// 128 x 224 as 4 producer waves + 2 x 2 compute waves; 128 x 128 as 2 x 2
+// waves.
+constexpr Cand kCands[] = {{256, 256, 32, 4, true}, {256, 160, 64, 3, true},
                            {128, 224, 64, 3, true}, {128, 128, 64, 4, true}};
 
 // Relative cost of a tile shape per output element: operand bytes staged per
@@ -964,7 +965,7 @@ hipError_t launch_gemm(const GemmArgs &a, const TileCfg &t, hipStream_t stream) 
   if (t.bm == 256 && t.bn == 256)
     hipLaunchKernelGGL((gemm_kernel_w8<256, 256, 32, 4, 2, 4, false, true>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
   else if (t.bm == 256 && t.bn == 160)
-    hipLaunchKernelGGL((gemm_kernel<256, 160, 64, 3>), dim3(a.grid), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel_w8<256, 160, 64, 3, 4, 2, false, true>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
   else if (t.bm == 128 && t.bn == 224)
     hipLaunchKernelGGL((gemm_kernel_w8<128, 224, 64, 3, 2, 2, true>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
   else if (t.bm == 128 && t.bn == 128)
