@@ -528,7 +528,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
   static_assert(NTT % NT == 0, "whole copy groups");
   __shared__ __attribute__((aligned(16))) char lds[C::LDS];
   __shared__ Unit s_unit;
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -906,11 +905,12 @@ struct Cand {
 };
 
 // Tile configurations compiled into the library (the launcher below maps
-// each to its wave layout): 256 x 256 as 8 waves in a 2 x 4 grid and 256 x 160
-// as 8 waves in a 4 x 2 grid, half of them also issuing the copies (HP);
+// each to its wave layout): 256 x 256 (k staged 64 at a time in two 64 KiB
+// buffers, so every operand row piece is a whole 128-byte line) and 256 x 160,
+// both as 8 waves in a 4 x 2 grid, half of them also issuing the copies (HP);
 // 128 x 224 as 4 producer waves + 2 x 2 compute waves; 128 x 128 as 2 x 2
 // waves.
-constexpr Cand kCands[] = {{256, 256, 32, 4, true}, {256, 160, 64, 3, true},
+constexpr Cand kCands[] = {{256, 256, 64, 2, true}, {256, 160, 64, 3, true},
                            {128, 224, 64, 3, true}, {128, 128, 64, 4, true}};
 
 // Relative cost of a tile shape per output element: operand bytes staged per
@@ -963,7 +963,7 @@ size_t partial_slot_bytes(const TileCfg &t) { return (size_t)t.bm * t.bn * sizeo
 
 hipError_t launch_gemm(const GemmArgs &a, const TileCfg &t, hipStream_t stream) {
   if (t.bm == 256 && t.bn == 256)
-    hipLaunchKernelGGL((gemm_kernel_w8<256, 256, 32, 4, 2, 4, false, true>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel_w8<256, 256, 64, 2, 4, 2, false, true>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
   else if (t.bm == 256 && t.bn == 160)
     hipLaunchKernelGGL((gemm_kernel_w8<256, 160, 64, 3, 4, 2, false, true>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
   else if (t.bm == 128 && t.bn == 224)
