@@ -252,6 +252,22 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
   a.total_units = (int32_t)total_units;
   a.grid = (int32_t)(total_units < grid_cap ? total_units : grid_cap);
   if (a.grid < 1) a.grid = 1;
+  // Without arrival flags and reduce units each workgroup's first unit is
+  // assigned statically (the q-th workgroup of XCD g takes the q-th unit of
+  // group g); when that covers every unit, a workgroup leaves after its
+  // first unit without claiming again.
+  a.static_all = 0;
+  if (a.arrived == nullptr) {
+    bool all = true;
+    for (int c = 0; c < R && all; ++c) all = a.red_units[c] == 0;
+    for (int g = 0; g < XCDS && all; ++g) {
+      int64_t units_g = 0;
+      for (int c = 0; c < R; ++c) units_g += (int64_t)a.gtiles[g] * a.split[c];
+      const int64_t wgs_g = (a.grid - g + XCDS - 1) / XCDS;
+      all = units_g <= (wgs_g > 0 ? wgs_g : 0);
+    }
+    a.static_all = all ? 1 : 0;
+  }
 
   hipError_t e = launch_gemm(a, p.tile, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) { record(e); return FO_ERR_HIP; }

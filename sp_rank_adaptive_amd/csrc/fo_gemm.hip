@@ -201,6 +201,7 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
   // landed chunks, taken as if no unit were claimed yet (true at the start
   // of a call), so only the flags are read before the fetch-add; if that
   // shows the group exhausted, the general claim below takes over.
+  if (rank_hint < 0 && a.static_all) return r;   // every unit was assigned statically
   if (rank_hint >= 0 && a.arrived == nullptr) {
     uint32_t q = (uint32_t)rank_hint;
     rank_hint = -1;
@@ -519,7 +520,7 @@ __device__ __forceinline__ const GemmArgs &unit_args() {
 //    waves 4-7 only multiply.  A wave that issues a burst of copies stalls
 //    until the load queue takes them; the other wave on its SIMD then keeps
 //    the matrix core busy, where in the default layout both would stall.
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool PC, bool HP = false>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool PC, bool HP = false, bool RV = false>
 __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
   using C = Cfg<BM, BN, BK, STAGES, WGM, WGN>;
   constexpr int NCW = WGM * WGN;               // compute waves
@@ -592,18 +593,23 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
     // uniform offset.  Rows past the chunk end or past n read as zero (buffer
     // size), and so does k past the split's end (per-thread offset moved past
     // the buffer).
-    const int tr = gtid / C::CH;
-    const int tch = (gtid % C::CH) ^ C::swz(tr);
     const int nra = (int)((rowlim - row0 < BM) ? rowlim - row0 : BM);
     const int nrb = (int)((N - col0 < BN) ? N - col0 : BN);
     const __amdgpu_buffer_rsrc_t rsa = uniform_rsrc(a.x + row0 * K, (int)(nra * K * 2));
     const __amdgpu_buffer_rsrc_t rsb = uniform_rsrc(a.w + col0 * K, (int)(nrb * K * 2));
-    const int voff = (int)((tr * K + tch * 8) * 2);
     const uint32_t lds0 = lds_addr(lds) + (uint32_t)(__builtin_amdgcn_readfirstlane(cw) * 1024);
 
     auto issue = [&](int stage) {
       const int kk = (int)(k0 + (int64_t)stage * BK);          // uniform
-      const int vo = (kk + tch * 8 < k1) ? voff : 0x40000000;   // k past the end reads zero
+      // RV: the per-lane offset is recomputed from the thread index at each
+      // issue.  In a layout whose k-loop needs nearly every register, the
+      // offset kept live across the loop gets spilled, and its reload waits
+      // for every copy in flight before the next stage's copies go out.
+      int t = threadIdx.x;
+      if constexpr (RV) asm volatile("" : "+v"(t));
+      const int rtr = (t & (NT - 1)) / C::CH;
+      const int rtch = ((t & (NT - 1)) % C::CH) ^ C::swz(rtr);
+      const int vo = (kk + rtch * 8 < k1) ? (int)((rtr * K + rtch * 8) * 2) : 0x40000000;   // k past the end reads zero
       const uint32_t base = lds0 + (uint32_t)((stage % STAGES) * C::STAGE);
 #pragma unroll
       for (int v = 0; v < C::V; ++v) {
@@ -844,9 +850,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
           store_release(a.done_flags + c, a.epoch);
         }
       }
-      const uint32_t t = fetch_add_relaxed(a.ws32 + WS_TOTAL_DONE, 1u);
-      if (t == (uint32_t)(a.total_units - 1) && a.stamps)
-        store_u64_relaxed(a.stamps + 2 * a.R + 1, now_ticks());
+      if (a.stamps) {
+        const uint32_t t = fetch_add_relaxed(a.ws32 + WS_TOTAL_DONE, 1u);
+        if (t == (uint32_t)(a.total_units - 1)) store_u64_relaxed(a.stamps + 2 * a.R + 1, now_ticks());
+      }
     }
   }
 
@@ -891,10 +898,10 @@ __global__ void __launch_bounds__(NT, 1) gemm_kernel(GemmArgs a) {
 // persistent grid.  On gfx950 the compiler counts this attribute in pairs of
 // the unified VGPR/AGPR file: 120 caps each wave at 240, so two waves leave
 // 32 of each lane's 512 registers free.
-template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool PC, bool HP = false>
+template <int BM, int BN, int BK, int STAGES, int WGM, int WGN, bool PC, bool HP = false, bool RV = false>
 __global__ void __launch_bounds__(2 * NT, 1) __attribute__((amdgpu_num_vgpr(120)))
 gemm_kernel_w8(GemmArgs a) {
-  gemm_body<BM, BN, BK, STAGES, WGM, WGN, PC, HP>(a);
+  gemm_body<BM, BN, BK, STAGES, WGM, WGN, PC, HP, RV>(a);
 }
 
 namespace {
@@ -963,7 +970,7 @@ size_t partial_slot_bytes(const TileCfg &t) { return (size_t)t.bm * t.bn * sizeo
 
 hipError_t launch_gemm(const GemmArgs &a, const TileCfg &t, hipStream_t stream) {
   if (t.bm == 256 && t.bn == 256)
-    hipLaunchKernelGGL((gemm_kernel_w8<256, 256, 64, 2, 4, 2, false, true>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
+    hipLaunchKernelGGL((gemm_kernel_w8<256, 256, 64, 2, 4, 2, false, true, true>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
   else if (t.bm == 256 && t.bn == 160)
     hipLaunchKernelGGL((gemm_kernel_w8<256, 160, 64, 3, 4, 2, false, true>), dim3(a.grid), dim3(2 * NT), 0, stream, a);
   else if (t.bm == 128 && t.bn == 224)

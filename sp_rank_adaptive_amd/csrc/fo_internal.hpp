@@ -44,6 +44,7 @@ struct GemmArgs {
   int32_t strict;
   int32_t total_units;
   int32_t grid;
+  int32_t static_all;         // 1: the static first units cover every unit
   const uint32_t *arrived;    // device [R] or null
   uint32_t *done_flags;       // device [R] or null
   uint32_t epoch;
