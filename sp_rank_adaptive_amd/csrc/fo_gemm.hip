@@ -65,7 +65,12 @@ struct Cfg {
   static constexpr int A_BYTES = BM * ROWB;
   static constexpr int B_BYTES = BN * ROWB;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LDS = STAGES * STAGE;
+  static constexpr int LDS_RING = STAGES * STAGE;
+  // The epilogue stages fp32 output rows padded by 4 floats (16 bytes), half
+  // a tile at a time when the whole tile does not fit; the LDS block is the
+  // larger of the ring and that staging area.
+  static constexpr int EPI_HALF = BM / 2 * (BN + 4) * 4;
+  static constexpr int LDS = LDS_RING > EPI_HALF ? LDS_RING : EPI_HALF;
   static_assert(BK == 32 || BK == 64, "BK");
   static_assert(STAGES >= 2 && STAGES <= 4, "STAGES");
   static_assert(BM % 32 == 0 && BN % 32 == 0, "tile");
