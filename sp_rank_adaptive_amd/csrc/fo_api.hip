@@ -252,21 +252,32 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
   a.total_units = (int32_t)total_units;
   a.grid = (int32_t)(total_units < grid_cap ? total_units : grid_cap);
   if (a.grid < 1) a.grid = 1;
-  // Without arrival flags and reduce units each workgroup's first unit is
-  // assigned statically (the q-th workgroup of XCD g takes the q-th unit of
-  // group g); when that covers every unit, a workgroup leaves after its
-  // first unit without claiming again.
-  a.static_all = 0;
+  // Without arrival flags and reduce units, every unit is assigned
+  // statically when that is balanced: no workgroup gets a second unit (2), or
+  // every XCD group holds the same number of units and every XCD the same
+  // number of workgroups (1: round-robin over the XCD's workgroups).
+  a.static_rr = 0;
+  a.all_unsplit = 1;
+  for (int c = 0; c < R; ++c) a.all_unsplit = a.all_unsplit && a.split[c] == 1;
+  for (int g = 0; g < XCDS; ++g) {
+    int64_t units_g = 0;
+    for (int c = 0; c < R; ++c) units_g += (int64_t)a.gtiles[g] * a.split[c];
+    a.gunits[g] = (int32_t)units_g;
+  }
   if (a.arrived == nullptr) {
-    bool all = true;
-    for (int c = 0; c < R && all; ++c) all = a.red_units[c] == 0;
-    for (int g = 0; g < XCDS && all; ++g) {
+    bool ok = true;
+    for (int c = 0; c < R && ok; ++c) ok = a.red_units[c] == 0;
+    bool equal = (a.grid % XCDS) == 0, single = true;
+    int64_t units0 = -1;
+    for (int g = 0; g < XCDS && ok; ++g) {
       int64_t units_g = 0;
       for (int c = 0; c < R; ++c) units_g += (int64_t)a.gtiles[g] * a.split[c];
       const int64_t wgs_g = (a.grid - g + XCDS - 1) / XCDS;
-      all = units_g <= (wgs_g > 0 ? wgs_g : 0);
+      if (units0 < 0) units0 = units_g;
+      equal = equal && units_g == units0;
+      single = single && units_g <= wgs_g;
     }
-    a.static_all = all ? 1 : 0;
+    a.static_rr = !ok ? 0 : single ? 2 : equal ? 1 : 0;
   }
 
   hipError_t e = launch_gemm(a, p.tile, static_cast<hipStream_t>(stream));

@@ -138,6 +138,7 @@ __device__ __forceinline__ void static_for(F &&f) {
 
 struct ClaimState {
   uint64_t acquired;   // bit c: this workgroup has done the acquire for chunk c
+  int taken;           // units taken so far (static round-robin)
 };
 
 struct Unit {
@@ -206,7 +207,48 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
   // landed chunks, taken as if no unit were claimed yet (true at the start
   // of a call), so only the flags are read before the fetch-add; if that
   // shows the group exhausted, the general claim below takes over.
-  if (rank_hint < 0 && a.static_all) return r;   // every unit was assigned statically
+  // Static round-robin (no arrival flags, no reduce units, XCD groups of
+  // equal size): the q-th workgroup of XCD g takes units q, q + W, q + 2W, ...
+  // of group g in priority order (W = workgroups on the XCD), with no atomic.
+  // Claims by hundreds of workgroups at once would otherwise queue on the
+  // counters' cache lines.  When no workgroup gets a second unit
+  // (static_rr == 2) the first unit comes from the static first claim below
+  // and the next claim ends the workgroup.
+  if (a.static_rr == 2 && rank_hint < 0) return r;   // one unit per workgroup: done
+  if (a.static_rr == 1) {
+    const int wgs = (a.grid - xg + XCDS - 1) / XCDS;
+    uint32_t q = (uint32_t)((int)(blockIdx.x / XCDS) + st.taken * wgs);
+    ++st.taken;
+    rank_hint = -1;
+    if (q >= (uint32_t)a.gunits[xg]) return r;   // this workgroup's share is done
+    if (a.all_unsplit) {
+      // every chunk holds gtiles[g] units in group g: no walk over the order
+      const int gt = a.gtiles[xg];
+      const int sidx = (int)q / gt, tl = (int)q - sidx * gt;
+      r.c = a.order[sidx];
+      r.sp = 0;
+      group_tile(a, xg, tl, r.tm, r.tn);
+      r.first = (xg == 0 && tl == 0);
+      r.red = 0;
+      return r;
+    }
+    for (int sidx = 0; sidx < R; ++sidx) {
+      const int c = a.order[sidx];
+      const uint32_t nu = group_units(a, c, xg);
+      if (q < nu) {
+        const int S = a.split[c];
+        const int tl = (int)q / S;
+        r.c = c;
+        r.sp = (int)q - tl * S;
+        group_tile(a, xg, tl, r.tm, r.tn);
+        r.first = (xg == 0 && q == 0);
+        r.red = 0;
+        return r;
+      }
+      q -= nu;
+    }
+    return r;
+  }
   if (rank_hint >= 0 && a.arrived == nullptr) {
     uint32_t q = (uint32_t)rank_hint;
     rank_hint = -1;
@@ -548,7 +590,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
   const int64_t K = a.k, N = a.n;
   const int xg = (int)(blockIdx.x % XCDS);
 
-  ClaimState st{0ull};
+  ClaimState st{0ull, 0};
   int rank_hint = (int)(blockIdx.x / XCDS);   // this workgroup's rank inside its XCD
   // The stage buffers are written only by the copy engine (asm below): hand
   // the buffer to an opaque asm so the compiler cannot assume it is never

@@ -44,7 +44,9 @@ struct GemmArgs {
   int32_t strict;
   int32_t total_units;
   int32_t grid;
-  int32_t static_all;         // 1: the static first units cover every unit
+  int32_t static_rr;          // every unit assigned statically: 1 round-robin per XCD, 2 one per workgroup
+  int32_t all_unsplit;        // 1: no chunk is split
+  int32_t gunits[XCDS];       // units per work-queue group over all chunks
   const uint32_t *arrived;    // device [R] or null
   uint32_t *done_flags;       // device [R] or null
   uint32_t epoch;
