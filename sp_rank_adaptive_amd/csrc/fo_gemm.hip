@@ -509,7 +509,8 @@ __device__ __forceinline__ void put4(char *base, int64_t ld, int64_t row, int64_
 template <int BM, int BN, int NTT>
 __device__ __forceinline__ void reduce_unit(const GemmArgs &a, int c, int tile, int slice, int64_t row0,
                                          int64_t rowlim, int64_t col0) {
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));   // computed per unit, not kept live across the loop
   const int64_t N = a.n;
   const int S = a.split[c];
   const size_t pbase = (size_t)a.part_base[c] + (size_t)tile * S;
@@ -819,6 +820,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
     // its workspace slot (row-major BM x BN); the split that completes the
     // tile publishes it for the reduce units.
     {
+      // Lane indices of the epilogue come from an opaque copy of the thread
+      // index, so they are computed here, per unit, rather than hoisted to
+      // the kernel's start and kept live (spilled) across the k-loop.
+      int etid = threadIdx.x;
+      asm volatile("" : "+v"(etid));
+      const int elane = etid & 63, ewave = etid >> 6;
+      const int ecw = PC ? (ewave >= 4 ? ewave - 4 : 0) : ewave;
+      const bool econs = !PC || ewave >= 4;
+      const int ewm = ecw / WGN, ewn = ecw % WGN;
       // padded fp32 row (spreads the staging writes over banks) when it fits
       constexpr int SROW = (BM / 2 * (BN + 4) * 4 <= C::LDS) ? BN + 4 : BN;
       constexpr int HALVES = (BM * SROW * 4 <= C::LDS) ? 1 : 2;
@@ -842,19 +852,19 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
 #pragma unroll
       for (int h = 0; h < HALVES; ++h) {
         __syncthreads();
-        if (cons && wm / WPP == h) {
+        if (econs && ewm / WPP == h) {
 #pragma unroll
           for (int i = 0; i < C::FM; ++i)
 #pragma unroll
             for (int j = 0; j < C::FN; ++j)
 #pragma unroll
               for (int v = 0; v < 4; ++v) {
-                const int r = (wm % WPP) * C::WTM + i * 16 + (lane >> 4) * 4 + v;
-                stg[r * SROW + wn * C::WTN + j * 16 + (lane & 15)] = acc[i][j][v];
+                const int r = (ewm % WPP) * C::WTM + i * 16 + (elane >> 4) * 4 + v;
+                stg[r * SROW + ewn * C::WTN + j * 16 + (elane & 15)] = acc[i][j][v];
               }
         }
         __syncthreads();
-        for (int cidx = tid; cidx < HROWS * CPR; cidx += NTT) {
+        for (int cidx = etid; cidx < HROWS * CPR; cidx += NTT) {
           const int r = cidx / CPR, cc = cidx - (cidx / CPR) * CPR;
           const int64_t row = rbase + h * HROWS + r;
           const int64_t col = cbase + cc * 4;
@@ -870,7 +880,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
         // of the partials (see the reduce unit).
         wait_stores();
         __syncthreads();
-        if (tid == 0) {
+        if (etid == 0) {
           const uint32_t old = fetch_add_relaxed(a.ws32 + WS_TILE_CTR + a.ctr_base[c] + tile, 1u);
           if (old == (uint32_t)(S - 1)) {
             const uint32_t idx = fetch_add_relaxed(a.ws32 + WS_RED_READY + c, 1u);
