@@ -180,17 +180,19 @@ def side_stream():
     return _SIDE[0]
 
 
-def _emulate(fo, dsts, srcs, order, nbytes, flags, e, es, side, link_bw):
+def _emulate(fo, dsts, srcs, order, nbytes, flags, e, es, side, link_bw, copy=True):
     """Enqueue ring arrivals of `order` on the side stream: chunk s lands at
-    s * B / BW, its copy issued B / BW earlier."""
+    s * B / BW, its copy issued B / BW earlier.  copy=False: the data are
+    already in place and only the flags are released at those times."""
     import torch
     rel = wl.ring_release_ns(nbytes, len(order), link_bw)
-    iss = [r - nbytes / link_bw * 1e9 for r in rel]
+    iss = [r - nbytes / link_bw * 1e9 for r in rel] if copy else list(rel)
     with torch.cuda.stream(side):
-        fo.fo_emulate_arrivals(dsts, srcs, rel, order, flags, e, es, issue_ns=iss, stream=side)
+        fo.fo_emulate_arrivals(dsts, srcs, rel, order, flags, e, es, issue_ns=iss,
+                               nbytes=None if copy else [0] * len(order), stream=side)
 
 
-def measure_tail_ag(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LINK_BW):
+def measure_tail_ag(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LINK_BW, copy=True, split=None):
     """Exposed tail of the AG-GEMM under emulated ring arrivals (us): time
     from the last chunk's landing to the last output written.
       flashoverlap: one persistent launch, ready-first claims over the flags;
@@ -218,7 +220,7 @@ def measure_tail_ag(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LIN
         e = 100 + rep
         torch.cuda.synchronize()
         _emulate(fo, [x[q * mc:(q + 1) * mc] for q in order], [staging[q * mc:(q + 1) * mc] for q in order],
-                 order, nbytes, flags, e, es, side, link_bw)
+                 order, nbytes, flags, e, es, side, link_bw, copy)
         if schedule == "naive":
             ev = torch.cuda.Event()
             ev.record(side)
@@ -239,7 +241,7 @@ def measure_tail_ag(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LIN
         else:
             mode = fo.FO_SCHED_STRICT if schedule == "strict" else fo.FO_SCHED_READY_FIRST
             fo.fo_ag_gemm(x, w, y, fo.Schedule(nchunks=cfg.R, epoch=e, arrived=flags, stamps=gs, mode=mode,
-                                               timeout_ns=5_000_000_000), ws)
+                                               timeout_ns=5_000_000_000, split=split), ws)
             done_idx = 2 * cfg.R + 1
         torch.cuda.synchronize()
         e_st = es.cpu().numpy().astype(np.int64)
@@ -251,7 +253,7 @@ def measure_tail_ag(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LIN
     return float(np.median(tails)), float(np.median(spans))
 
 
-def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LINK_BW):
+def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LINK_BW, copy=True, span=False):
     """Exposed tail of GEMM-RS + chunk reduce-add: the 7 incoming fp32
     partials of the local shard land by emulated ring arrivals; the tail is
     the time from the last landing to the bf16 shard written.
@@ -265,7 +267,7 @@ def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LIN
     done = torch.zeros(cfg.R, dtype=torch.int32, device="cuda")
     inc = wl.incoming_partials(cfg, "gauss")
     staging = [None if a is None else torch.from_numpy(a).cuda() for a in inc]
-    inbox = [None if a is None else torch.empty_like(a) for a in staging]
+    inbox = [None if a is None else (torch.empty_like(a) if copy else a.clone()) for a in staging]
     shard = torch.empty((mc, cfg.n), dtype=torch.bfloat16, device="cuda")
     order = wl.ring_arrival_order(cfg.R, cfg.local)
     nbytes = mc * cfg.n * 4
@@ -275,13 +277,13 @@ def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LIN
     ws = torch.zeros(fo.fo_workspace_bytes(cfg.m, cfg.n, cfg.k, cfg.R), dtype=torch.uint8, device="cuda")
     side = side_stream()
     main = torch.cuda.current_stream()
-    tails = []
+    tails, spans = [], []
     for rep in range(reps + 1):   # the first repetition is a warm-up
         e = 200 + rep
         rs_st.zero_()
         torch.cuda.synchronize()
         _emulate(fo, [inbox[q] for q in order], [staging[q] for q in order], order, nbytes, flags, e, es,
-                 side, link_bw)
+                 side, link_bw, copy)
         if schedule == "naive":
             ev = torch.cuda.Event()
             ev.record(side)
@@ -296,7 +298,50 @@ def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LIN
         last_arrival = max(e_st[1 + q] for q in order)
         if rep > 0:
             tails.append(ticks_to_us(int(rs_st[1].item()) - last_arrival, hz))
+            spans.append(ticks_to_us(last_arrival - e_st[0], hz))
+    if span:
+        return float(np.median(tails)), float(np.median(spans))
     return float(np.median(tails))
+
+
+def link_sweep(fo, hz, bws=(50e9, 153e9, 400e9, 1000e9)):
+    """End-to-end time (first release to output complete) and exposed tail at
+    several per-link bandwidths.  The data are copied in before the timed
+    window and only the flags are released at the modelled ring times, so
+    the sweep is not limited by the copy engine's own rate."""
+    out = {}
+    c2, c3 = wl.CFG2, wl.CFG3
+    for bw in bws:
+        row = {}
+        # the schedule model's split, and every split of the last-landing chunk
+        mc = c2.m // c2.R
+        order = wl.ring_arrival_order(c2.R, c2.local)
+        arr = [0] * c2.R
+        for q, t in zip(order, wl.ring_release_ns(mc * c2.k * 2, c2.R - 1, bw)):
+            arr[q] = int(t)
+        _, plan_split, pred = fo.fo_plan_ag_schedule(c2.m, c2.n, c2.k, c2.R, c2.local, arr)
+        last = order[-1]
+        for i, sk in enumerate((1, 2, 4, 8)):
+            sp = [1] * c2.R
+            sp[last] = sk
+            t, spn = measure_tail_ag(fo, c2, hz, "flashoverlap", link_bw=bw, copy=False, split=sp)
+            row[f"cfg2_split{sk}_total_us"] = round(t + spn, 2)
+            row[f"cfg2_split{sk}_predicted_us"] = round(pred[i] / 1e3, 2)
+        row["cfg2_planned_split"] = plan_split[last]
+        row["cfg2_planned_total_us"] = row[f"cfg2_split{plan_split[last]}_total_us"]
+        for sched in ("flashoverlap", "naive", "sliced"):
+            t, sp = measure_tail_ag(fo, c2, hz, sched, link_bw=bw, copy=False)
+            row[f"cfg2_{sched}_total_us"] = round(t + sp, 2)
+            row[f"cfg2_{sched}_tail_us"] = round(t, 2)
+        row["cfg2_last_arrival_us"] = round(sp, 2)
+        for sched in ("flashoverlap", "naive"):
+            t, sp = measure_tail_rs(fo, c3, hz, sched, link_bw=bw, copy=False, span=True)
+            row[f"cfg3_{sched}_total_us"] = round(t + sp, 2)
+            row[f"cfg3_{sched}_tail_us"] = round(t, 2)
+        row["cfg3_last_arrival_us"] = round(sp, 2)
+        out[f"{bw / 1e9:g}GBps"] = row
+        log(f"link sweep {bw / 1e9:g} GB/s: {row}")
+    return out
 
 
 def measure_tail_dp(fo, cfg, hz, schedule="flashoverlap", reps=1, link_bw=wl.LINK_BW):
@@ -422,6 +467,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="skip tails, cfg4/cfg5 and the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--link-sweep", action="store_true",
+                    help="also sweep the per-link bandwidth (end-to-end time and tail per schedule)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB copy (for scaling profiled byte counters)")
     args = ap.parse_args()
@@ -527,6 +574,8 @@ def main():
         tails["cfg4_dp_reduce"] = row
         log(f"tail cfg4: {row}")
         out["tails_50GBps_links"] = tails
+    if args.link_sweep:
+        out["link_sweep_flags_only"] = link_sweep(fo, hz)
     if args.copy_calibration:
         copy_calibration()
     if not args.quick and not args.no_cpu:

@@ -185,6 +185,38 @@ fo_status fo_emulate_arrivals(void *const *dst, const void *const *src,
                               int32_t count, uint32_t *arrived, uint32_t epoch,
                               uint64_t *stamps, void *stream);
 
+/* Schedule model for fo_ag_gemm (host only; euno.news "Methodology" step 3:
+ * the scheduler models the dependency graph of pieces and sub-tasks;
+ * technical summary §2: work on incoming data first, the local slice last).
+ * Given when each peer chunk is expected to land, returns the priority order
+ * (peers by landing time, ties in ring order local-1, local-2, ...; the
+ * local chunk last) and the split vector (1 everywhere except the chunk that
+ * lands last, split 1, 2, 4 or 8 ways along k).  A simulation of the
+ * kernel's ready-first claims over `num_workgroups` workgroups (processor
+ * sharing of the GPU's rate among running units) predicts how many
+ * workgroups are idle when that chunk becomes claimable.  The chunk is split
+ * only when at least three quarters are idle, and then by the largest factor
+ * whose units (tiles x split) the idle workgroups can all take at once:
+ * split units queued behind busy workgroups cost more than they save.  The
+ * result is meant for fo_schedule.order and .split.
+ *   arrival_ns      host [R]: expected landing time of chunk c after t0
+ *                   (the local chunk's entry is ignored).
+ *   gemm_tflops     sustained rate of one launch with every workgroup busy;
+ *                   <= 0 selects 900.
+ *   num_workgroups  workgroups of the launch; <= 0 = one per CU of the
+ *                   current device (needs a device).
+ *   order_out, split_out  host [R].
+ *   predicted_ns    host [4], optional: the simulation's completion (ns
+ *                   after t0) with the last chunk split 1, 2, 4, 8 ways; -1
+ *                   where that split is not possible (k too short, or
+ *                   R == 1).  It undercounts split costs on a busy GPU.
+ * Errors: NULL, SHAPE, SCHEDULE (local out of range, negative arrival), HIP
+ * (no device when num_workgroups <= 0). */
+fo_status fo_plan_ag_schedule(int64_t m, int64_t n, int64_t k, int32_t nchunks, int32_t local,
+                              const int64_t *arrival_ns, double gemm_tflops,
+                              int32_t num_workgroups, int32_t *order_out, int32_t *split_out,
+                              int64_t *predicted_ns);
+
 /* Device facts used to interpret stamps and size launches. */
 fo_status fo_device_info(int32_t *num_cus, int32_t *lds_bytes_per_cu,
                          uint64_t *wall_clock_hz);

@@ -27,7 +27,7 @@ FO_SCHED_READY_FIRST, FO_SCHED_STRICT = 0, 1
 FO_MAX_CHUNKS = 64
 
 EXPORTS = ("fo_workspace_bytes", "fo_ag_gemm", "fo_gemm_rs", "fo_chunk_reduce",
-           "fo_emulate_arrivals", "fo_device_info", "fo_status_string",
+           "fo_emulate_arrivals", "fo_plan_ag_schedule", "fo_device_info", "fo_status_string",
            "fo_last_hip_error")
 
 
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.fo_chunk_reduce.argtypes = [P, i32, P, i64, S, P]
     L.fo_emulate_arrivals.restype = i32
     L.fo_emulate_arrivals.argtypes = [P, P, P, P, P, P, i32, P, u32, P, P]
+    L.fo_plan_ag_schedule.restype = i32
+    L.fo_plan_ag_schedule.argtypes = [i64, i64, i64, i32, i32, P, ctypes.c_double, i32, P, P, P]
     L.fo_device_info.restype = i32
     L.fo_device_info.argtypes = [P, P, P]
     L.fo_status_string.restype = ctypes.c_char_p
@@ -160,6 +162,20 @@ def fo_last_hip_error() -> str:
 
 def fo_workspace_bytes(m: int, n: int, k: int, nchunks: int) -> int:
     return int(lib().fo_workspace_bytes(m, n, k, nchunks))
+
+
+def fo_plan_ag_schedule(m, n, k, nchunks, local, arrival_ns, gemm_tflops=0.0, num_workgroups=0):
+    """Schedule model for fo_ag_gemm: (order, split, predicted_ns) where
+    predicted_ns[i] is the predicted completion with the last-landing chunk
+    split (1, 2, 4, 8)[i] ways (-1 where not possible)."""
+    R = int(nchunks)
+    arr = (ctypes.c_int64 * R)(*[int(v) for v in arrival_ns])
+    order = (ctypes.c_int32 * R)()
+    split = (ctypes.c_int32 * R)()
+    pred = (ctypes.c_int64 * 4)()
+    _check(lib().fo_plan_ag_schedule(int(m), int(n), int(k), R, int(local), arr, float(gemm_tflops),
+                                     int(num_workgroups), order, split, pred), "fo_plan_ag_schedule")
+    return list(order), list(split), list(pred)
 
 
 def fo_device_info():
