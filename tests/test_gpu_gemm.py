@@ -219,11 +219,33 @@ def test_ag_gemm_full_size_sampled_rows(fo, orc):
         log(f"case: cfg{cfg.cfg} gauss {cfg.m}x{cfg.n}x{cfg.k} R={cfg.R}")
         xb, wb, x, w = gemm_case(cfg, "gauss")
         y, _ = run_ag(fo, x, w, cfg.R)
+        assert not torch.isnan(y).any()   # every tile written (y starts as NaN)
         rows = np.sort(np.random.Generator(np.random.PCG64(7 + cfg.cfg)).choice(cfg.m, 48, replace=False))
         mc = cfg.m // cfg.R
         rows = np.unique(np.concatenate([rows, [0, mc - 1, mc, cfg.m - 1]]))
         ref = orc.gemm(xb[rows], wb)
         check_tolerance(host(y)[rows], ref, what=f"cfg{cfg.cfg}")
+
+
+@pytest.mark.parametrize("grid", [8, 12, 96, 100, 256])
+def test_claim_paths_cover_every_unit_int_exact(fo, orc, grid):
+    # Static round-robin (no flags, 8 | grid, balanced groups), the static
+    # first claim followed by dynamic claims (grid not a multiple of 8), and
+    # dynamic claims over preset flags: every output element is written once
+    # (the output starts as NaN) and equals the oracle exactly.
+    m, n, k, R = 1024, 448, 512, 4
+    xb = wl.bf16_operand((m, k), "int", 0.0, 12001)
+    wb = wl.bf16_operand((n, k), "int", 0.0, 12002)
+    x, w = dev_bf16(xb), dev_bf16(wb)
+    ref = orc.gemm(xb, wb)
+    log(f"case: claim paths {m}x{n}x{k} R={R} grid={grid}")
+    y, ws = run_ag(fo, x, w, R, max_workgroups=grid)
+    assert not torch.isnan(y).any()
+    check_exact(host(y), ref, f"no flags, grid {grid}")
+    flags = torch.full((R,), EP.e + 1, dtype=torch.int32, device="cuda")
+    y2, _ = run_ag(fo, x, w, R, ws=ws, max_workgroups=grid, arrived=flags)
+    assert not torch.isnan(y2).any()
+    check_exact(host(y2), ref, f"preset flags, grid {grid}")
 
 
 def test_ag_gemm_full_size_int_sampled_rows(fo, orc):
