@@ -180,16 +180,18 @@ def side_stream():
     return _SIDE[0]
 
 
-def _emulate(fo, dsts, srcs, order, nbytes, flags, e, es, side, link_bw, copy=True):
+def _emulate(fo, dsts, srcs, order, nbytes, flags, e, es, side, link_bw, copy=True, gate=None):
     """Enqueue ring arrivals of `order` on the side stream: chunk s lands at
     s * B / BW, its copy issued B / BW earlier.  copy=False: the data are
-    already in place and only the flags are released at those times."""
+    already in place and only the flags are released at those times.  gate:
+    a device word (the consumer kernel's start stamp); the timeline starts
+    once it is nonzero."""
     import torch
     rel = wl.ring_release_ns(nbytes, len(order), link_bw)
     iss = [r - nbytes / link_bw * 1e9 for r in rel] if copy else list(rel)
     with torch.cuda.stream(side):
         fo.fo_emulate_arrivals(dsts, srcs, rel, order, flags, e, es, issue_ns=iss,
-                               nbytes=None if copy else [0] * len(order), stream=side)
+                               nbytes=None if copy else [0] * len(order), stream=side, gate=gate)
 
 
 def measure_tail_ag(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LINK_BW, copy=True, split=None):
@@ -216,12 +218,23 @@ def measure_tail_ag(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LIN
     main = torch.cuda.current_stream()
     wait_value = _hip_wait_value() if schedule == "sliced" else None
     tails, spans = [], []
+    start_idx = 2 * cfg.R
     for rep in range(reps + 1):   # the first repetition is a warm-up
         e = 100 + rep
+        gs.zero_()
         torch.cuda.synchronize()
-        _emulate(fo, [x[q * mc:(q + 1) * mc] for q in order], [staging[q * mc:(q + 1) * mc] for q in order],
-                 order, nbytes, flags, e, es, side, link_bw, copy)
+        emulate = lambda gate=None: _emulate(fo, [x[q * mc:(q + 1) * mc] for q in order],
+                                             [staging[q * mc:(q + 1) * mc] for q in order],
+                                             order, nbytes, flags, e, es, side, link_bw, copy, gate)
+        # For consumers that wait on the flags themselves the emulator is
+        # enqueued first with its timeline gated on the consumer kernel's
+        # start stamp: its timer kernel is resident and waiting when the
+        # consumer starts, so t0 follows the kernel start within about a
+        # microsecond, as in a layer whose kernel runs while the transfers
+        # start.  Ungated, the host's enqueue time decides which starts first
+        # (tens of microseconds either way).
         if schedule == "naive":
+            emulate()
             ev = torch.cuda.Event()
             ev.record(side)
             main.wait_event(ev)
@@ -229,6 +242,8 @@ def measure_tail_ag(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LIN
             done_idx = 2 * cfg.R + 1
         elif schedule == "sliced":
             one = torch.zeros(4, dtype=torch.int64, device="cuda")
+            start_idx = None
+            emulate(one[2:3])
             for q in [cfg.local] + order:
                 if q != cfg.local:
                     st = wait_value(main.cuda_stream, flags[q:q + 1].data_ptr(), e, 0, 0xFFFFFFFF)
@@ -236,20 +251,26 @@ def measure_tail_ag(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LIN
                         raise RuntimeError(f"hipStreamWaitValue32 failed ({st})")
                 rows = slice(q * mc, (q + 1) * mc)
                 fo.fo_ag_gemm(x[rows], w, y[rows], fo.Schedule(nchunks=1, epoch=e, stamps=one), ws)
-            gs = one
+            gs_used = one
             done_idx = 3
         else:
             mode = fo.FO_SCHED_STRICT if schedule == "strict" else fo.FO_SCHED_READY_FIRST
+            emulate(gs[start_idx:start_idx + 1])
             fo.fo_ag_gemm(x, w, y, fo.Schedule(nchunks=cfg.R, epoch=e, arrived=flags, stamps=gs, mode=mode,
                                                timeout_ns=5_000_000_000, split=split), ws)
             done_idx = 2 * cfg.R + 1
+        if schedule != "sliced":
+            gs_used = gs
         torch.cuda.synchronize()
         e_st = es.cpu().numpy().astype(np.int64)
-        g_st = gs.cpu().numpy().astype(np.int64)
+        g_st = gs_used.cpu().numpy().astype(np.int64)
         last_arrival = max(e_st[1 + q] for q in order)
+        # the run starts at the emulator's t0 or at the consumer kernel's own
+        # start, whichever is earlier
+        t_start = e_st[0] if schedule == "naive" else min(e_st[0], g_st[2 if start_idx is None else start_idx])
         if rep > 0:
             tails.append(ticks_to_us(g_st[done_idx] - last_arrival, hz))
-            spans.append(ticks_to_us(last_arrival - e_st[0], hz))
+            spans.append(ticks_to_us(last_arrival - t_start, hz))
     return float(np.median(tails)), float(np.median(spans))
 
 
@@ -277,18 +298,25 @@ def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LIN
     ws = torch.zeros(fo.fo_workspace_bytes(cfg.m, cfg.n, cfg.k, cfg.R), dtype=torch.uint8, device="cuda")
     side = side_stream()
     main = torch.cuda.current_stream()
+    gs = torch.zeros(2 * cfg.R + 2, dtype=torch.int64, device="cuda")
     tails, spans = [], []
     for rep in range(reps + 1):   # the first repetition is a warm-up
         e = 200 + rep
         rs_st.zero_()
+        gs.zero_()
         torch.cuda.synchronize()
-        _emulate(fo, [inbox[q] for q in order], [staging[q] for q in order], order, nbytes, flags, e, es,
-                 side, link_bw, copy)
+        emulate = lambda gate=None: _emulate(fo, [inbox[q] for q in order], [staging[q] for q in order], order,
+                                             nbytes, flags, e, es, side, link_bw, copy, gate)
         if schedule == "naive":
+            emulate()
             ev = torch.cuda.Event()
             ev.record(side)
             main.wait_event(ev)
-        fo.fo_gemm_rs(x, w, part, done, fo.Schedule(nchunks=cfg.R, epoch=e), ws)
+        else:
+            # the emulator's timeline starts with the GEMM-RS kernel (see
+            # measure_tail_ag)
+            emulate(gs[2 * cfg.R:2 * cfg.R + 1])
+        fo.fo_gemm_rs(x, w, part, done, fo.Schedule(nchunks=cfg.R, epoch=e, stamps=gs), ws)
         srcs = [part[cfg.local * mc:(cfg.local + 1) * mc] if q == cfg.local else inbox[q] for q in range(cfg.R)]
         arrived = None if schedule == "naive" else flags
         fo.fo_chunk_reduce(shard, srcs, fo.Schedule(nchunks=cfg.R, epoch=e, arrived=arrived, stamps=rs_st,
@@ -296,9 +324,11 @@ def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LIN
         torch.cuda.synchronize()
         e_st = es.cpu().numpy().astype(np.int64)
         last_arrival = max(e_st[1 + q] for q in order)
+        g0 = int(gs[2 * cfg.R].item())
+        t_start = e_st[0] if schedule == "naive" else min(e_st[0], g0)
         if rep > 0:
             tails.append(ticks_to_us(int(rs_st[1].item()) - last_arrival, hz))
-            spans.append(ticks_to_us(last_arrival - e_st[0], hz))
+            spans.append(ticks_to_us(last_arrival - t_start, hz))
     if span:
         return float(np.median(tails)), float(np.median(spans))
     return float(np.median(tails))

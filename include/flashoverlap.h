@@ -185,6 +185,20 @@ fo_status fo_emulate_arrivals(void *const *dst, const void *const *src,
                               int32_t count, uint32_t *arrived, uint32_t epoch,
                               uint64_t *stamps, void *stream);
 
+/* fo_emulate_arrivals whose timeline starts when a device word becomes
+ * nonzero: the timer kernel first waits (at most gate_timeout_ns, 0 = 10 s)
+ * until *gate != 0, then records t0; issue and release times count from
+ * there.  With gate = the consumer kernel's start stamp (stamps[2R] of a
+ * GEMM call, zeroed before the call) the emulated peers start sending when
+ * the consumer starts, however long the host takes to enqueue the arrivals.
+ * gate NULL behaves as fo_emulate_arrivals.  Errors as fo_emulate_arrivals. */
+fo_status fo_emulate_arrivals_gated(const uint64_t *gate, uint64_t gate_timeout_ns,
+                                    void *const *dst, const void *const *src,
+                                    const size_t *bytes, const int64_t *issue_ns,
+                                    const int64_t *release_ns, const int32_t *chunk_id,
+                                    int32_t count, uint32_t *arrived, uint32_t epoch,
+                                    uint64_t *stamps, void *stream);
+
 /* Schedule model for fo_ag_gemm (host only; euno.news "Methodology" step 3:
  * the scheduler models the dependency graph of pieces and sub-tasks;
  * technical summary §2: work on incoming data first, the local slice last).
@@ -193,12 +207,11 @@ fo_status fo_emulate_arrivals(void *const *dst, const void *const *src,
  * local chunk last) and the split vector (1 everywhere except the chunk that
  * lands last, split 1, 2, 4 or 8 ways along k).  A simulation of the
  * kernel's ready-first claims over `num_workgroups` workgroups (processor
- * sharing of the GPU's rate among running units) predicts how many
- * workgroups are idle when that chunk becomes claimable.  The chunk is split
- * only when at least three quarters are idle, and then by the largest factor
- * whose units (tiles x split) the idle workgroups can all take at once:
- * split units queued behind busy workgroups cost more than they save.  The
- * result is meant for fo_schedule.order and .split.
+ * sharing of the GPU's rate among running units) predicts the completion for
+ * each split; the earliest wins, a larger split by more than 0.5 us.  A chunk
+ * landing on an idle GPU is split so every workgroup shares its tiles; one
+ * landing while the workgroups are busy is not, since its split units would
+ * queue behind them.  The result is meant for fo_schedule.order and .split.
  *   arrival_ns      host [R]: expected landing time of chunk c after t0
  *                   (the local chunk's entry is ignored).
  *   gemm_tflops     sustained rate of one launch with every workgroup busy;
@@ -206,10 +219,9 @@ fo_status fo_emulate_arrivals(void *const *dst, const void *const *src,
  *   num_workgroups  workgroups of the launch; <= 0 = one per CU of the
  *                   current device (needs a device).
  *   order_out, split_out  host [R].
- *   predicted_ns    host [4], optional: the simulation's completion (ns
- *                   after t0) with the last chunk split 1, 2, 4, 8 ways; -1
- *                   where that split is not possible (k too short, or
- *                   R == 1).  It undercounts split costs on a busy GPU.
+ *   predicted_ns    host [4], optional: the predicted completion (ns after
+ *                   t0) with the last chunk split 1, 2, 4, 8 ways; -1 where
+ *                   that split is not possible (k too short, or R == 1).
  * Errors: NULL, SHAPE, SCHEDULE (local out of range, negative arrival), HIP
  * (no device when num_workgroups <= 0). */
 fo_status fo_plan_ag_schedule(int64_t m, int64_t n, int64_t k, int32_t nchunks, int32_t local,

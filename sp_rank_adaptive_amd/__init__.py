@@ -27,7 +27,7 @@ FO_SCHED_READY_FIRST, FO_SCHED_STRICT = 0, 1
 FO_MAX_CHUNKS = 64
 
 EXPORTS = ("fo_workspace_bytes", "fo_ag_gemm", "fo_gemm_rs", "fo_chunk_reduce",
-           "fo_emulate_arrivals", "fo_plan_ag_schedule", "fo_device_info", "fo_status_string",
+           "fo_emulate_arrivals", "fo_emulate_arrivals_gated", "fo_plan_ag_schedule", "fo_device_info", "fo_status_string",
            "fo_last_hip_error")
 
 
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.fo_chunk_reduce.argtypes = [P, i32, P, i64, S, P]
     L.fo_emulate_arrivals.restype = i32
     L.fo_emulate_arrivals.argtypes = [P, P, P, P, P, P, i32, P, u32, P, P]
+    L.fo_emulate_arrivals_gated.restype = i32
+    L.fo_emulate_arrivals_gated.argtypes = [P, ctypes.c_uint64, P, P, P, P, P, P, i32, P, u32, P, P]
     L.fo_plan_ag_schedule.restype = i32
     L.fo_plan_ag_schedule.argtypes = [i64, i64, i64, i32, i32, P, ctypes.c_double, i32, P, P, P]
     L.fo_device_info.restype = i32
@@ -238,8 +240,10 @@ def fo_chunk_reduce(dst, srcs, sched: Schedule, stream=None, *, raise_on_error=T
 
 
 def fo_emulate_arrivals(dsts, srcs, release_ns, chunk_ids, arrived, epoch, stamps,
-                        issue_ns=None, nbytes=None, stream=None) -> int:
-    """Enqueue emulated peer arrivals (SDMA copies + timed epoch flags)."""
+                        issue_ns=None, nbytes=None, stream=None, gate=None, gate_timeout_ns=0) -> int:
+    """Enqueue emulated peer arrivals (SDMA copies + timed epoch flags).
+    gate: a device uint64 word (tensor element pointer or int); the timeline
+    starts once it is nonzero (fo_emulate_arrivals_gated)."""
     cnt = len(dsts)
     if nbytes is None:
         nbytes = [t.numel() * t.element_size() for t in srcs]
@@ -249,7 +253,12 @@ def fo_emulate_arrivals(dsts, srcs, release_ns, chunk_ids, arrived, epoch, stamp
     rel = (ctypes.c_int64 * cnt)(*[int(v) for v in release_ns])
     iss = None if issue_ns is None else (ctypes.c_int64 * cnt)(*[int(v) for v in issue_ns])
     cid = (ctypes.c_int32 * cnt)(*[int(v) for v in chunk_ids])
-    st = lib().fo_emulate_arrivals(d, s, b, iss, rel, cid, cnt, _ptr(arrived), epoch,
-                                   _ptr(stamps), _stream(stream))
-    _check(st, "fo_emulate_arrivals")
+    if gate is None:
+        st = lib().fo_emulate_arrivals(d, s, b, iss, rel, cid, cnt, _ptr(arrived), epoch,
+                                       _ptr(stamps), _stream(stream))
+        _check(st, "fo_emulate_arrivals")
+    else:
+        st = lib().fo_emulate_arrivals_gated(_ptr(gate), int(gate_timeout_ns), d, s, b, iss, rel, cid, cnt,
+                                             _ptr(arrived), epoch, _ptr(stamps), _stream(stream))
+        _check(st, "fo_emulate_arrivals_gated")
     return st

@@ -391,6 +391,15 @@ fo_status fo_emulate_arrivals(void *const *dst, const void *const *src, const si
                               const int64_t *issue_ns, const int64_t *release_ns,
                               const int32_t *chunk_id, int32_t count, uint32_t *arrived,
                               uint32_t epoch, uint64_t *stamps, void *stream) {
+  return fo_emulate_arrivals_gated(nullptr, 0, dst, src, bytes, issue_ns, release_ns, chunk_id, count,
+                                   arrived, epoch, stamps, stream);
+}
+
+fo_status fo_emulate_arrivals_gated(const uint64_t *gate, uint64_t gate_timeout_ns, void *const *dst,
+                                    const void *const *src, const size_t *bytes,
+                                    const int64_t *issue_ns, const int64_t *release_ns,
+                                    const int32_t *chunk_id, int32_t count, uint32_t *arrived,
+                                    uint32_t epoch, uint64_t *stamps, void *stream) {
   if (count < 0) return FO_ERR_SHAPE;
   if (count == 0) return FO_OK;
   if (!dst || !src || !bytes || !release_ns || !chunk_id || !arrived || !stamps) return FO_ERR_NULL;
@@ -405,7 +414,9 @@ fo_status fo_emulate_arrivals(void *const *dst, const void *const *src, const si
   if (!I) return FO_ERR_HIP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   auto issue_at = [&](int i) -> uint64_t { return (uint64_t)(issue_ns ? issue_ns[i] : release_ns[i]); };
-  hipError_t e = launch_emu_start(stamps, ns_to_ticks(issue_at(0), I->wall_hz), st);
+  const uint64_t gate_ns = gate_timeout_ns ? gate_timeout_ns : kDefaultTimeoutNs;
+  hipError_t e = launch_emu_start(stamps, ns_to_ticks(issue_at(0), I->wall_hz), gate,
+                                  ns_to_ticks(gate_ns, I->wall_hz), st);
   for (int i = 0; i < count && e == hipSuccess; ++i) {
     if (bytes[i]) e = hipMemcpyAsync(dst[i], src[i], bytes[i], hipMemcpyDeviceToDeviceNoCU, st);
     if (e != hipSuccess) break;

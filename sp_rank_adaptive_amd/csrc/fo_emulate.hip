@@ -18,8 +18,17 @@ __device__ __forceinline__ void sleep_until(uint64_t t0, uint64_t offset) {
   while (now_ticks() - t0 < offset) __builtin_amdgcn_s_sleep(16);
 }
 
-__global__ void __launch_bounds__(64) emu_start_kernel(uint64_t *t0_slot, uint64_t wait_ticks) {
+// With a gate, the timeline starts once *gate is nonzero (the consumer
+// kernel's start stamp, say), waiting at most gate_ticks.
+__global__ void __launch_bounds__(64) emu_start_kernel(uint64_t *t0_slot, uint64_t wait_ticks,
+                                                       const uint64_t *gate, uint64_t gate_ticks) {
   if (threadIdx.x != 0) return;
+  if (gate) {
+    const uint64_t g0 = now_ticks();
+    while (__hip_atomic_load(gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == 0 &&
+           now_ticks() - g0 < gate_ticks)
+      __builtin_amdgcn_s_sleep(2);
+  }
   const uint64_t t0 = now_ticks();
   store_u64_relaxed(t0_slot, t0);
   sleep_until(t0, wait_ticks);
@@ -41,8 +50,9 @@ __global__ void __launch_bounds__(64) emu_flag_kernel(const uint64_t *t0_slot, u
   sleep_until(t0, next_issue_ticks);
 }
 
-hipError_t launch_emu_start(uint64_t *t0_slot, uint64_t wait_ticks, hipStream_t s) {
-  hipLaunchKernelGGL(emu_start_kernel, dim3(1), dim3(64), 0, s, t0_slot, wait_ticks);
+hipError_t launch_emu_start(uint64_t *t0_slot, uint64_t wait_ticks, const uint64_t *gate,
+                            uint64_t gate_ticks, hipStream_t s) {
+  hipLaunchKernelGGL(emu_start_kernel, dim3(1), dim3(64), 0, s, t0_slot, wait_ticks, gate, gate_ticks);
   return hipGetLastError();
 }
 

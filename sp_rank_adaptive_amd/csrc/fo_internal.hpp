@@ -91,7 +91,8 @@ hipError_t launch_gemm(const GemmArgs &a, const TileCfg &t, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs &a, int grid, hipStream_t stream);
 
 // Emulator kernels.
-hipError_t launch_emu_start(uint64_t *t0_slot, uint64_t wait_ticks, hipStream_t s);
+hipError_t launch_emu_start(uint64_t *t0_slot, uint64_t wait_ticks, const uint64_t *gate,
+                            uint64_t gate_ticks, hipStream_t s);
 hipError_t launch_emu_flag(const uint64_t *t0_slot, uint64_t release_ticks,
                            uint64_t next_issue_ticks, uint32_t *flag, uint32_t epoch,
                            uint64_t *stamp_slot, hipStream_t s);

@@ -22,8 +22,9 @@
 // (4096 x 1792 x 4096 in 8 chunks): about 900 TFLOP/s with every workgroup
 // busy, one chunk alone about 1.8 times faster per workgroup, and about 5 us
 // from a flag store to the first claim of that chunk.  Over ring arrivals at
-// 50, 153, 400 and 1000 GB/s per link the split it picks ran within 2% of the
-// best measured split.
+// 50, 153, 400 and 1000 GB/s per link (peers starting with the consumer
+// kernel) it predicted completions within 1-10% and picked the best measured
+// split at each bandwidth.
 #include "fo_internal.hpp"
 
 #include <algorithm>
@@ -40,6 +41,7 @@ constexpr double kHbmBytesPerNs = 5000.0;       // 5 TB/s, shared
 constexpr double kWgBytesPerNsMax = 60.0;       // one workgroup alone
 constexpr double kUnitFixedNs = 1500.0;         // claim and bookkeeping per unit
 constexpr double kClaimQueueNs = 10.0;          // per workgroup claiming at the same instant
+constexpr double kSplitMarginNs = 500.0;        // a larger split must win by more
 
 struct Sim {
   int grid = 0, tiles = 0, kt_total = 0;
@@ -69,8 +71,7 @@ int effective_split(int sk, int kt_total) {
 // grows with the number of workgroups claiming at that instant (they queue on
 // the same claim counters).  A reduce unit waits, holding its workgroup, until
 // every split of its tile has finished.
-double simulate(const Sim &s, int R, const int *order, const double *avail, const int *split,
-                double probe_t = -1, int *busy_at_probe = nullptr) {
+double simulate(const Sim &s, int R, const int *order, const double *avail, const int *split) {
   struct Chunk {
     int units = 0, next = 0, red_units = 0, red_next = 0, S = 1;
     std::vector<int> tile_left;          // splits of the tile still running
@@ -101,14 +102,7 @@ double simulate(const Sim &s, int R, const int *order, const double *avail, cons
   double t = 0, done = 0;
   int left_total = 0;
   for (int c = 0; c < R; ++c) left_total += ch[c].units + ch[c].red_units;
-  bool probed = false;
   while (left_total > 0) {
-    if (busy_at_probe && !probed && t >= probe_t) {
-      int busy = 0;
-      for (const Wg &g : wg) busy += g.state == RUN || g.state == WAIT_TILE;
-      *busy_at_probe = busy;
-      probed = true;
-    }
     // claims by idle workgroups: those that find work queue on the counters
     int idle = 0, claimable = 0;
     for (const Wg &g : wg) idle += g.state == IDLE;
@@ -232,35 +226,27 @@ extern "C" fo_status fo_plan_ag_schedule(int64_t m, int64_t n, int64_t k, int32_
   // Predicted completion for every split of the last-landing chunk.
   std::vector<int> split(R, 1);
   const int cands[4] = {1, 2, 4, 8};
-  int busy_at_last = 0;
+  double pred_by[4] = {-1, -1, -1, -1};
   for (int i = 0; i < 4; ++i) {
     const int want = cands[i];
     const int sk = effective_split(std::min(want, kPlanMaxSplit), s.kt_total);
     double pred = -1;
     if ((tail >= 0 && sk == want) || (tail < 0 && want == 1)) {
       if (tail >= 0) split[tail] = sk;
-      pred = simulate(s, R, order_out, avail.data(), split.data(), tail >= 0 ? avail[tail] : -1,
-                      want == 1 ? &busy_at_last : nullptr);
+      pred = simulate(s, R, order_out, avail.data(), split.data());
       if (tail >= 0) split[tail] = 1;
     }
+    pred_by[i] = pred;
     if (predicted_ns) predicted_ns[i] = pred < 0 ? -1 : (int64_t)pred;
   }
-  // Split decision.  The simulation undercounts what split units cost while
-  // the GPU is busy (measured on MI355X: with every workgroup busy at the
-  // last landing, splits of 2-8 ran 45-65% slower than no split, where it
-  // predicts them equal), so the split is taken from the predicted number of
-  // idle workgroups when the last chunk becomes claimable: only when at least
-  // three quarters of them are idle, and then the largest split whose units
-  // (tiles x split) they can all take at once.
+  // Split decision: the earliest predicted completion; a larger split must
+  // win by more than kSplitMarginNs.
   for (int c = 0; c < R; ++c) split_out[c] = 1;
   if (tail >= 0) {
-    const int idle = grid - busy_at_last;
+    double best = pred_by[0];
     int best_s = 1;
-    if (4 * idle >= 3 * grid)
-      for (int i = 1; i < 4; ++i) {
-        const int want = cands[i];
-        if (effective_split(want, s.kt_total) == want && (int64_t)s.tiles * want <= idle) best_s = want;
-      }
+    for (int i = 1; i < 4; ++i)
+      if (pred_by[i] >= 0 && pred_by[i] < best - kSplitMarginNs) { best = pred_by[i]; best_s = cands[i]; }
     split_out[tail] = best_s;
   }
   return FO_OK;

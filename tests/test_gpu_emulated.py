@@ -30,6 +30,18 @@ def fo():
 
 
 _EP = [5000]
+_SIDE = []
+
+
+def side_stream():
+    """One side stream for every emulated arrival in this process, created
+    on first use (the first stream the process creates, as in bench.py), so
+    it does not share a hardware queue with the stream the kernels run on:
+    a consumer enqueued before a gated emulator would otherwise wait for
+    flags that the emulator, queued behind it, cannot set."""
+    if not _SIDE:
+        _SIDE.append(torch.cuda.Stream())
+    return _SIDE[0]
 
 
 def epoch():
@@ -38,9 +50,11 @@ def epoch():
 
 
 def ag_with_emulated_peers(fo, xb, wb, R, local, arrival, gap_ns, mode=None, reps=3,
-                           split=None):
+                           split=None, gated=False):
     """Runs fo_ag_gemm with peers landing in `arrival` order, gap_ns apart;
-    returns the outputs of every repetition and the stamps of the last."""
+    returns the outputs of every repetition and the stamps of the last.
+    gated: the emulator's timeline starts at the GEMM kernel's start stamp
+    (fo_emulate_arrivals_gated); its timer kernel waits for it."""
     m, k = xb.shape
     n = wb.shape[0]
     mc = m // R
@@ -52,19 +66,24 @@ def ag_with_emulated_peers(fo, xb, wb, R, local, arrival, gap_ns, mode=None, rep
     gs = torch.zeros(2 * R + 2, dtype=torch.int64, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     ws = torch.zeros(fo.fo_workspace_bytes(m, n, k, R), dtype=torch.uint8, device="cuda")
-    side = torch.cuda.Stream()
+    side = side_stream()
     outs = []
     for rep in range(reps):
         e = epoch()
         for q in arrival:                        # poison every peer destination
             x[q * mc:(q + 1) * mc].fill_(float("nan"))
         y = torch.full((m, n), float("nan"), device="cuda")
+        gs.zero_()
         torch.cuda.synchronize()
         rel = [gap_ns * (i + 1) for i in range(len(arrival))]
-        with torch.cuda.stream(side):
-            fo.fo_emulate_arrivals([x[q * mc:(q + 1) * mc] for q in arrival],
-                                   [staging[q * mc:(q + 1) * mc] for q in arrival],
-                                   rel, arrival, flags, e, es, stream=side)
+
+        def emulate(gate=None):
+            with torch.cuda.stream(side):
+                fo.fo_emulate_arrivals([x[q * mc:(q + 1) * mc] for q in arrival],
+                                       [staging[q * mc:(q + 1) * mc] for q in arrival],
+                                       rel, arrival, flags, e, es, stream=side, gate=gate)
+
+        emulate(gs[2 * R:2 * R + 1] if gated else None)
         kw = {} if mode is None else {"mode": mode}
         fo.fo_ag_gemm(x, w, y, fo.Schedule(nchunks=R, local=local, arrived=flags, epoch=e,
                                            stamps=gs, status=status, split=split,
@@ -89,6 +108,26 @@ def test_ag_gemm_emulated_poisoned_int_exact(fo, orc):
     t = [es[1 + q] for q in arrival]
     assert all(b >= a for a, b in zip(t, t[1:])) and t[0] > es[0]
     # the last output was written after the last landing
+    assert gs[2 * R + 1] >= max(t)
+
+
+def test_ag_gemm_emulated_gated_timeline_int_exact(fo, orc):
+    """The emulated peers start sending when the GEMM kernel starts (the
+    emulator waits for its start stamp): poisoned destinations, integer
+    inputs exact, and the emulator's t0 comes after the kernel's start
+    stamp."""
+    m, n, k, R, local = 1024, 448, 512, 8, 0
+    xb = wl.bf16_operand((m, k), "int", 1.0, 3011)
+    wb = wl.bf16_operand((n, k), "int", 1.0, 3012)
+    ref = orc.gemm(xb, wb)
+    arrival = wl.ring_arrival_order(R, local)
+    log("case: gated emulator timeline, poisoned destinations, 5 us apart")
+    outs, es, gs = ag_with_emulated_peers(fo, xb, wb, R, local, arrival, 5_000, gated=True)
+    for y in outs:
+        check_exact(y, ref, "gated emulated AG-GEMM")
+    assert gs[2 * R] > 0 and es[0] >= gs[2 * R]
+    t = [es[1 + q] for q in arrival]
+    assert all(b >= a for a, b in zip(t, t[1:])) and t[0] > es[0]
     assert gs[2 * R + 1] >= max(t)
 
 
@@ -135,7 +174,7 @@ def test_reduce_emulated_poisoned(fo, orc):
     flags = torch.zeros(R, dtype=torch.int32, device="cuda")
     es = torch.zeros(R + 2, dtype=torch.int64, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    side = torch.cuda.Stream()
+    side = side_stream()
     for rep in range(3):
         e = epoch()
         dst = [staging[local].clone() if q == local else torch.full((n,), float("nan"), device="cuda")
