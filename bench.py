@@ -595,6 +595,17 @@ def main():
                 row[sched + "_us"] = round(t, 2)
                 row["last_arrival_us"] = round(span, 1)
             row["tail_over_chunk_gemm"] = round(row["flashoverlap_us"] / cg, 3)
+            # the schedule model's order and split for these ring arrivals
+            order = wl.ring_arrival_order(cfg.R, cfg.local)
+            arr = [0] * cfg.R
+            for q, t_ in zip(order, wl.ring_release_ns((cfg.m // cfg.R) * cfg.k * 2, cfg.R - 1, wl.LINK_BW)):
+                arr[q] = int(t_)
+            p_order, p_split, _ = fo.fo_plan_ag_schedule(cfg.m, cfg.n, cfg.k, cfg.R, cfg.local, arr)
+            assert p_order == order + [cfg.local]   # the default priority
+            t, _ = measure_tail_ag(fo, cfg, hz, "flashoverlap", split=p_split)
+            row["planned_split"] = p_split[order[-1]]
+            row["planned_us"] = round(t, 2)
+            row["planned_tail_over_chunk_gemm"] = round(t / cg, 3)
             tails[key] = row
             log(f"tail {key}: {row}")
         row = {s_ + "_us": round(measure_tail_rs(fo, c3, hz, s_), 2) for s_ in ("flashoverlap", "naive")}

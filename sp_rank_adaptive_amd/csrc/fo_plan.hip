@@ -16,15 +16,18 @@
 // The model simulates the kernel's ready-first claims.  One simulated
 // workgroup per launch workgroup takes, whenever it is free, the first unit
 // in priority order whose chunk has landed; the units of a split chunk are
-// followed by its reduce units.  Running units share the whole GPU's rate,
-// up to what one workgroup reaches alone (processor sharing).  The constants
-// are calibrated on MI355X measurements of the TP=8 MLP up-projection share
-// (4096 x 1792 x 4096 in 8 chunks): about 900 TFLOP/s with every workgroup
-// busy, one chunk alone about 1.8 times faster per workgroup, and about 5 us
-// from a flag store to the first claim of that chunk.  Over ring arrivals at
-// 50, 153, 400 and 1000 GB/s per link (peers starting with the consumer
-// kernel) it predicted completions within 1-10% and picked the best measured
-// split at each bandwidth.
+// followed by its reduce units.  A running unit's rate falls linearly from
+// what one workgroup reaches alone to an equal share of the whole GPU's rate
+// as more workgroups run (rates are recomputed at every event).  The
+// constants are calibrated on MI355X measurements of the TP=8 MLP
+// up-projection share (4096 x 1792 x 4096 in 8 chunks): about 900 TFLOP/s
+// with every workgroup busy, one chunk alone about 1.8 times faster per
+// workgroup, and about 5 us from a flag store to the first claim of that
+// chunk.  Over ring arrivals at 50, 153, 400 and 1000 GB/s per link (peers
+// starting with the consumer kernel) its completions came within 3% of the
+// measured ones, and its split was the best measured one or within 2% of it;
+// on the long-sequence QKV share (16384 x 1280 x 8192 in 16 chunks, 50 GB/s)
+// it also picks the best measured split.
 #include "fo_internal.hpp"
 
 #include <algorithm>
@@ -156,7 +159,10 @@ double simulate(const Sim &s, int R, const int *order, const double *avail, cons
       t = next_avail;
       continue;
     }
-    const double speed = std::min(1.0, s.rate_all / active / s.rate_one);
+    // a workgroup's rate falls linearly from the alone rate (one running)
+    // to an equal share of the whole GPU's (all running)
+    const double busy_frac = (double)active / s.grid;
+    const double speed = (1.0 + (kAloneSpeedup - 1.0) * (1.0 - busy_frac)) / kAloneSpeedup;
     double dt = -1;
     for (const Wg &g : wg)
       if (g.state == RUN && (dt < 0 || g.work / speed < dt)) dt = g.work / speed;

@@ -128,3 +128,13 @@ def test_validation():
     # the local chunk's entry is ignored, even when negative
     loc = (ctypes.c_int64 * 4)(-1, 1, 2, 3)
     assert L.fo_plan_ag_schedule(args["m"], args["n"], args["k"], 4, 0, loc, 0.0, GRID, o, s, None) == fo.FO_OK
+
+
+def test_long_sequence_share_at_slow_links():
+    # the QKV share (16 chunks of 1024 x 8192, 256x160 tiles) at 50 GB/s: the
+    # GPU is idle at the last landing and 8 splits of its 32 tiles fill it
+    cfg = wl.CFG5
+    arr, order = ring_arrivals(cfg, 50e9)
+    o, split, pred = fo.fo_plan_ag_schedule(cfg.m, cfg.n, cfg.k, cfg.R, cfg.local, arr, num_workgroups=GRID)
+    assert o == order + [cfg.local]
+    assert split[order[-1]] == 8 and chosen_is_earliest(8, pred)
