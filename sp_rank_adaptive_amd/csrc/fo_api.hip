@@ -264,7 +264,7 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
     for (int c = 0; c < R; ++c) units_g += (int64_t)a.gtiles[g] * a.split[c];
     a.gunits[g] = (int32_t)units_g;
   }
-  if (a.arrived == nullptr) {
+  {
     bool ok = true;
     for (int c = 0; c < R && ok; ++c) ok = a.red_units[c] == 0;
     bool equal = (a.grid % XCDS) == 0, single = true;
@@ -277,7 +277,13 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
       equal = equal && units_g == units0;
       single = single && units_g <= wgs_g;
     }
-    a.static_rr = !ok ? 0 : single ? 2 : equal ? 1 : 0;
+    if (a.arrived == nullptr) a.static_rr = !ok ? 0 : single ? 2 : equal ? 1 : 0;
+    // With flags and no group holding more units than its XCD has
+    // workgroups, a workgroup whose first claim got a unit leaves after it:
+    // the units number at most the workgroups, so every unit not taken by a
+    // first claim leaves a workgroup whose first claim failed, and those keep
+    // claiming until no work is left.
+    a.one_unit = (a.arrived != nullptr && ok && single) ? 1 : 0;
   }
 
   hipError_t e = launch_gemm(a, p.tile, static_cast<hipStream_t>(stream));

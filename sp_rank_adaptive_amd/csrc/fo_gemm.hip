@@ -215,6 +215,7 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
   // (static_rr == 2) the first unit comes from the static first claim below
   // and the next claim ends the workgroup.
   if (a.static_rr == 2 && rank_hint < 0) return r;   // one unit per workgroup: done
+  if (a.one_unit && st.taken == 1) return r;          // first claim got a unit: done
   if (a.static_rr == 1) {
     const int wgs = (a.grid - xg + XCDS - 1) / XCDS;
     uint32_t q = (uint32_t)((int)(blockIdx.x / XCDS) + st.taken * wgs);
@@ -293,6 +294,7 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
       if (u < group_units(a, pick, xg)) {
         const int S = a.split[pick];
         const int tl = (int)u / S;
+        st.taken = 1;
         r.c = pick;
         r.sp = (int)u - tl * S;
         group_tile(a, xg, tl, r.tm, r.tn);

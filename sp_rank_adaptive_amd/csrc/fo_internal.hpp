@@ -46,6 +46,7 @@ struct GemmArgs {
   int32_t grid;
   int32_t static_rr;          // every unit assigned statically: 1 round-robin per XCD, 2 one per workgroup
   int32_t all_unsplit;        // 1: no chunk is split
+  int32_t one_unit;           // flags: a workgroup whose first claim succeeds leaves after it
   int32_t gunits[XCDS];       // units per work-queue group over all chunks
   const uint32_t *arrived;    // device [R] or null
   uint32_t *done_flags;       // device [R] or null
