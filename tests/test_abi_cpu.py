@@ -169,6 +169,15 @@ def test_emulate_validation(L):
     assert em(d, s, b, iss, rel, cid, 1, A, 1, A, None) == fo.FO_ERR_SCHEDULE
     bad = (ctypes.c_int32 * 1)(64)
     assert em(d, s, b, None, rel, bad, 1, A, 1, A, None) == fo.FO_ERR_SCHEDULE
+    # the gated form validates the same way before anything is enqueued
+    eg = L.fo_emulate_arrivals_gated
+    for gate in (None, A):
+        assert eg(gate, 0, d, s, b, None, rel, cid, 0, A, 1, A, None) == fo.FO_OK
+        assert eg(gate, 0, d, s, b, None, rel, cid, -1, A, 1, A, None) == fo.FO_ERR_SHAPE
+        assert eg(gate, 0, d, s, b, None, rel, cid, 1, None, 1, A, None) == fo.FO_ERR_NULL
+        assert eg(gate, 0, d, s, b, None, rel, cid, 1, A, 0, A, None) == fo.FO_ERR_SCHEDULE
+        assert eg(gate, 0, d, s, b, iss, rel, cid, 1, A, 1, A, None) == fo.FO_ERR_SCHEDULE
+        assert eg(gate, 0, d, s, b, None, rel, bad, 1, A, 1, A, None) == fo.FO_ERR_SCHEDULE
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
