@@ -152,6 +152,13 @@ class _Null:
         return False
 
 
+def _spread(out, values):
+    """p10 and p90 of the repetitions, into the dict `out` when one is given."""
+    if out is not None:
+        out["p10"], out["p90"] = (round(float(v), 2) for v in np.percentile(values, [10, 90]))
+        out["reps"] = len(values)
+
+
 def ticks_to_us(t, hz):
     return float(t) * 1e6 / hz
 
@@ -194,7 +201,8 @@ def _emulate(fo, dsts, srcs, order, nbytes, flags, e, es, side, link_bw, copy=Tr
                                nbytes=None if copy else [0] * len(order), stream=side, gate=gate)
 
 
-def measure_tail_ag(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LINK_BW, copy=True, split=None):
+def measure_tail_ag(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LINK_BW, copy=True, split=None,
+                    spread=None):
     """Exposed tail of the AG-GEMM under emulated ring arrivals (us): time
     from the last chunk's landing to the last output written.
       flashoverlap: one persistent launch, ready-first claims over the flags;
@@ -271,10 +279,12 @@ def measure_tail_ag(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LIN
         if rep > 0:
             tails.append(ticks_to_us(g_st[done_idx] - last_arrival, hz))
             spans.append(ticks_to_us(last_arrival - t_start, hz))
+    _spread(spread, tails)
     return float(np.median(tails)), float(np.median(spans))
 
 
-def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LINK_BW, copy=True, span=False):
+def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LINK_BW, copy=True, span=False,
+                    spread=None):
     """Exposed tail of GEMM-RS + chunk reduce-add: the 7 incoming fp32
     partials of the local shard land by emulated ring arrivals; the tail is
     the time from the last landing to the bf16 shard written.
@@ -329,6 +339,7 @@ def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=3, link_bw=wl.LIN
         if rep > 0:
             tails.append(ticks_to_us(int(rs_st[1].item()) - last_arrival, hz))
             spans.append(ticks_to_us(last_arrival - t_start, hz))
+    _spread(spread, tails)
     if span:
         return float(np.median(tails)), float(np.median(spans))
     return float(np.median(tails))
@@ -374,7 +385,7 @@ def link_sweep(fo, hz, bws=(50e9, 153e9, 400e9, 1000e9)):
     return out
 
 
-def measure_tail_dp(fo, cfg, hz, schedule="flashoverlap", reps=1, link_bw=wl.LINK_BW):
+def measure_tail_dp(fo, cfg, hz, schedule="flashoverlap", reps=10, link_bw=wl.LINK_BW, spread=None):
     """Exposed tail of the DP gradient reduce-add (in place into the local
     shard): the 7 peer chunks land by emulated arrivals in a seeded order; the
     tail is the time from the last landing to the reduce's completion."""
@@ -409,6 +420,7 @@ def measure_tail_dp(fo, cfg, hz, schedule="flashoverlap", reps=1, link_bw=wl.LIN
             tails.append(ticks_to_us(int(st[1].item()) - last_arrival, hz))
     del srcs, staging
     torch.cuda.empty_cache()
+    _spread(spread, tails)
     return float(np.median(tails))
 
 
@@ -591,9 +603,12 @@ def main():
             for sched in ("flashoverlap", "strict", "naive", "sliced"):
                 if cfg is wl.CFG5 and sched in ("strict", "sliced"):
                     continue
-                t, span = measure_tail_ag(fo, cfg, hz, sched)
+                sp = {}
+                t, span = measure_tail_ag(fo, cfg, hz, sched, spread=sp)
                 row[sched + "_us"] = round(t, 2)
+                row[sched + "_p10_p90_us"] = [sp["p10"], sp["p90"]]
                 row["last_arrival_us"] = round(span, 1)
+                row["reps"] = sp["reps"]
             row["tail_over_chunk_gemm"] = round(row["flashoverlap_us"] / cg, 3)
             # the schedule model's order and split for these ring arrivals
             order = wl.ring_arrival_order(cfg.R, cfg.local)
@@ -602,16 +617,28 @@ def main():
                 arr[q] = int(t_)
             p_order, p_split, _ = fo.fo_plan_ag_schedule(cfg.m, cfg.n, cfg.k, cfg.R, cfg.local, arr)
             assert p_order == order + [cfg.local]   # the default priority
-            t, _ = measure_tail_ag(fo, cfg, hz, "flashoverlap", split=p_split)
+            sp = {}
+            t, _ = measure_tail_ag(fo, cfg, hz, "flashoverlap", split=p_split, spread=sp)
             row["planned_split"] = p_split[order[-1]]
             row["planned_us"] = round(t, 2)
+            row["planned_p10_p90_us"] = [sp["p10"], sp["p90"]]
             row["planned_tail_over_chunk_gemm"] = round(t / cg, 3)
             tails[key] = row
             log(f"tail {key}: {row}")
-        row = {s_ + "_us": round(measure_tail_rs(fo, c3, hz, s_), 2) for s_ in ("flashoverlap", "naive")}
+        row = {}
+        for s_ in ("flashoverlap", "naive"):
+            sp = {}
+            row[s_ + "_us"] = round(measure_tail_rs(fo, c3, hz, s_, spread=sp), 2)
+            row[s_ + "_p10_p90_us"] = [sp["p10"], sp["p90"]]
+            row["reps"] = sp["reps"]
         tails["cfg3_gemm_rs_reduce"] = row
         log(f"tail cfg3: {row}")
-        row = {s_ + "_us": round(measure_tail_dp(fo, wl.CFG4, hz, s_), 1) for s_ in ("flashoverlap", "naive")}
+        row = {}
+        for s_ in ("flashoverlap", "naive"):
+            sp = {}
+            row[s_ + "_us"] = round(measure_tail_dp(fo, wl.CFG4, hz, s_, spread=sp), 1)
+            row[s_ + "_p10_p90_us"] = [sp["p10"], sp["p90"]]
+            row["reps"] = sp["reps"]
         tails["cfg4_dp_reduce"] = row
         log(f"tail cfg4: {row}")
         out["tails_50GBps_links"] = tails
