@@ -289,6 +289,7 @@ def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LI
     partials of the local shard land by emulated ring arrivals; the tail is
     the time from the last landing to the bf16 shard written.
       flashoverlap: GEMM-RS, then a reduce that adds partials as they land;
+      fused: one fo_gemm_rs_reduce launch whose shard units wait for them;
       naive: wait for every partial, then GEMM-RS and the reduce."""
     import torch
     xb, wb = wl.gemm_inputs(cfg, "gauss")
@@ -326,18 +327,25 @@ def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LI
             # the emulator's timeline starts with the GEMM-RS kernel (see
             # measure_tail_ag)
             emulate(gs[2 * cfg.R:2 * cfg.R + 1])
-        fo.fo_gemm_rs(x, w, part, done, fo.Schedule(nchunks=cfg.R, epoch=e, stamps=gs), ws)
-        srcs = [part[cfg.local * mc:(cfg.local + 1) * mc] if q == cfg.local else inbox[q] for q in range(cfg.R)]
-        arrived = None if schedule == "naive" else flags
-        fo.fo_chunk_reduce(shard, srcs, fo.Schedule(nchunks=cfg.R, epoch=e, arrived=arrived, stamps=rs_st,
-                                                    timeout_ns=5_000_000_000))
+        if schedule == "fused":
+            fo.fo_gemm_rs_reduce(x, w, part, done, shard, inbox,
+                                 fo.Schedule(nchunks=cfg.R, epoch=e, arrived=flags, stamps=gs,
+                                             timeout_ns=5_000_000_000), ws)
+        else:
+            fo.fo_gemm_rs(x, w, part, done, fo.Schedule(nchunks=cfg.R, epoch=e, stamps=gs), ws)
+            srcs = [part[cfg.local * mc:(cfg.local + 1) * mc] if q == cfg.local else inbox[q]
+                    for q in range(cfg.R)]
+            arrived = None if schedule == "naive" else flags
+            fo.fo_chunk_reduce(shard, srcs, fo.Schedule(nchunks=cfg.R, epoch=e, arrived=arrived, stamps=rs_st,
+                                                        timeout_ns=5_000_000_000))
         torch.cuda.synchronize()
         e_st = es.cpu().numpy().astype(np.int64)
         last_arrival = max(e_st[1 + q] for q in order)
         g0 = int(gs[2 * cfg.R].item())
         t_start = e_st[0] if schedule == "naive" else min(e_st[0], g0)
+        t_done = int(gs[2 * cfg.R + 1].item()) if schedule == "fused" else int(rs_st[1].item())
         if rep > 0:
-            tails.append(ticks_to_us(int(rs_st[1].item()) - last_arrival, hz))
+            tails.append(ticks_to_us(t_done - last_arrival, hz))
             spans.append(ticks_to_us(last_arrival - t_start, hz))
     _spread(spread, tails)
     if span:
@@ -375,7 +383,7 @@ def link_sweep(fo, hz, bws=(50e9, 153e9, 400e9, 1000e9)):
             row[f"cfg2_{sched}_total_us"] = round(t + sp, 2)
             row[f"cfg2_{sched}_tail_us"] = round(t, 2)
         row["cfg2_last_arrival_us"] = round(sp, 2)
-        for sched in ("flashoverlap", "naive"):
+        for sched in ("flashoverlap", "fused", "naive"):
             t, sp = measure_tail_rs(fo, c3, hz, sched, link_bw=bw, copy=False, span=True)
             row[f"cfg3_{sched}_total_us"] = round(t + sp, 2)
             row[f"cfg3_{sched}_tail_us"] = round(t, 2)
@@ -461,6 +469,29 @@ def gemm_rate(fo, cfg, reps=20):
     torch.cuda.synchronize()
     ms = float(np.median(tm.ms()))
     return 2.0 * cfg.m * cfg.n * cfg.k / (ms * 1e-3) / 1e12, ms
+
+
+def fused_rs_us(fo, path, reps=50):
+    """cfg3 all present: one fo_gemm_rs_reduce launch against fo_gemm_rs +
+    fo_chunk_reduce on the same buffers (HIP events; means over reps)."""
+    import torch
+    c3 = path.c3
+    stream = torch.cuda.current_stream()
+    inc = [None if q == c3.local else path.inc[q] for q in range(c3.R)]
+    tf, tu = Timer(stream), Timer(stream)
+    for i in range(reps + 3):
+        path.epoch += 1
+        e = path.epoch
+        with (tf if i >= 3 else _Null()):
+            fo.fo_gemm_rs_reduce(path.x3, path.w3, path.part, path.done3, path.shard, inc,
+                                 fo.Schedule(nchunks=c3.R, epoch=e), path.ws3)
+        path.epoch += 1
+        e = path.epoch
+        with (tu if i >= 3 else _Null()):
+            fo.fo_gemm_rs(path.x3, path.w3, path.part, path.done3, fo.Schedule(nchunks=c3.R, epoch=e), path.ws3)
+            fo.fo_chunk_reduce(path.shard, path.srcs, fo.Schedule(nchunks=c3.R, epoch=e))
+    torch.cuda.synchronize()
+    return float(np.mean(tf.ms())) * 1e3, float(np.mean(tu.ms())) * 1e3
 
 
 def reduce_rate(fo, cfg, reps=10):
@@ -588,6 +619,9 @@ def main():
             "flops_per_launch": d_flops,
         },
     }
+    f_us, u_us = fused_rs_us(fo, path)
+    out["gemm_rs_reduce_fused_cfg3"] = {"us": round(f_us, 2), "unfused_rs_plus_reduce_us": round(u_us, 2)}
+    log(f"fused GEMM-RS + reduce {f_us:.1f} us against {u_us:.1f} us unfused")
     if not args.quick:
         for cfg in (wl.CFG5,):
             tf, ms = gemm_rate(fo, cfg)
@@ -626,7 +660,7 @@ def main():
             tails[key] = row
             log(f"tail {key}: {row}")
         row = {}
-        for s_ in ("flashoverlap", "naive"):
+        for s_ in ("flashoverlap", "fused", "naive"):
             sp = {}
             row[s_ + "_us"] = round(measure_tail_rs(fo, c3, hz, s_, spread=sp), 2)
             row[s_ + "_p10_p90_us"] = [sp["p10"], sp["p90"]]

@@ -151,6 +151,34 @@ fo_status fo_gemm_rs(const void *x, const void *w, float *partial, uint32_t *don
                      const fo_schedule *s, void *ws, size_t ws_bytes,
                      void *stream);
 
+/* Chunked GEMM-RS with the reduce of the local chunk fused in (technical
+ * summary §2, Flash-RS: the partial that stays local is produced last, and
+ * the final receive is absorbed by that last step).  Computes exactly what
+ * fo_gemm_rs computes (partial and done flags, same bits) and, in the same
+ * launch,
+ *   shard = partial[rows of local] + incoming[order'[0]] + incoming[order'[1]]
+ *           + ...
+ * in fp32 left to right, where order' is the priority order without local:
+ * the order and bits of fo_chunk_reduce(shard, srcs with srcs[local] =
+ * partial rows of local, srcs[q] = incoming[q]).  Each tile of the local
+ * chunk is split into row slices that any workgroup sums once the tile is
+ * written and every incoming partial has landed.
+ *   shard     device [m/R][n], shard_dtype FO_F32 or FO_BF16 (nearest even).
+ *   incoming  host [R] array of device fp32 [m/R][n] pointers; incoming[local]
+ *             is ignored.  With s->arrived, incoming[q] is read only after
+ *             arrived[q] shows the epoch (system-coherent loads: a copy
+ *             engine may write it during the call); the GEMM itself is not
+ *             gated.  The launch holds its workgroups until every partial has
+ *             landed, so use it when they land before the local chunk's
+ *             tiles finish; otherwise fo_gemm_rs + fo_chunk_reduce.
+ * n % 4 == 0 and (m/R) * n * 4 < 2^31 are required; split factors other
+ * than 1 are rejected.  Errors as fo_gemm_rs, plus DTYPE, ALIAS (shard
+ * overlapping partial, x or w). */
+fo_status fo_gemm_rs_reduce(const void *x, const void *w, float *partial, uint32_t *done,
+                            void *shard, fo_dtype shard_dtype, const float *const *incoming,
+                            int64_t m, int64_t n, int64_t k, const fo_schedule *s,
+                            void *ws, size_t ws_bytes, void *stream);
+
 /* Chunk reduce-add (technical summary §1 DP reduce-scatter, §2 Flash-RS).
  *   srcs  host [R] array of device fp32 pointers, n elements each.
  *   dst   device, n elements of dst_dtype (FO_F32 or FO_BF16).

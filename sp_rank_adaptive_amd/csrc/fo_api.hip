@@ -132,9 +132,16 @@ GemmPlan plan_gemm(int64_t m, int64_t n, int64_t k, int R, int grid, bool leave_
   return p;
 }
 
+// The fused reduce of fo_gemm_rs_reduce.
+struct FusedRs {
+  void *shard;
+  bool shard_bf16;
+  const float *const *incoming;   // host [R] of device pointers
+};
+
 fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t *done,
                    bool rs_mode, int64_t m, int64_t n, int64_t k, const fo_schedule *s,
-                   void *ws, size_t ws_bytes, void *stream) {
+                   void *ws, size_t ws_bytes, void *stream, const FusedRs *fz = nullptr) {
   if (!x || !w || !y || !s) return FO_ERR_NULL;
   fo_status st = check_schedule(s);
   if (st != FO_OK) return st;
@@ -143,7 +150,31 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
   if (m / R > (int64_t)1 << 30 || n > (int64_t)1 << 30) return FO_ERR_SHAPE;
   if (k % 8 != 0 || !aligned16(x) || !aligned16(w)) return FO_ERR_ALIGN;
   if (!aligned16(y) && !y_bf16) return FO_ERR_ALIGN;
-  if (rs_mode && s->arrived) return FO_ERR_SCHEDULE;
+  if (rs_mode && s->arrived && !fz) return FO_ERR_SCHEDULE;
+  if (fz) {
+    if (!fz->shard || !fz->incoming) return FO_ERR_NULL;
+    for (int c = 0; c < R; ++c)
+      if (c != s->local && !fz->incoming[c]) return FO_ERR_NULL;
+    if (n % 4 != 0 || !aligned16(fz->shard)) return FO_ERR_ALIGN;
+    for (int c = 0; c < R; ++c)
+      if (c != s->local && !aligned16(fz->incoming[c])) return FO_ERR_ALIGN;
+    if ((m / R) * n * 4 >= ((int64_t)1 << 31)) return FO_ERR_SHAPE;
+    if (s->split)
+      for (int c = 0; c < R; ++c)
+        if (s->split[c] != 1) return FO_ERR_SCHEDULE;
+    const size_t shard_bytes = (size_t)(m / R) * n * (fz->shard_bf16 ? 2 : 4);
+    if (overlaps(fz->shard, shard_bytes, y, (size_t)m * n * 4) ||
+        overlaps(fz->shard, shard_bytes, x, (size_t)m * k * 2) ||
+        overlaps(fz->shard, shard_bytes, w, (size_t)n * k * 2))
+      return FO_ERR_ALIAS;
+    // incoming partials are read while the launch writes the partials and
+    // the shard
+    const size_t inc_bytes = (size_t)(m / R) * n * 4;
+    for (int c = 0; c < R; ++c)
+      if (c != s->local && (overlaps(fz->incoming[c], inc_bytes, fz->shard, shard_bytes) ||
+                            overlaps(fz->incoming[c], inc_bytes, y, (size_t)m * n * 4)))
+        return FO_ERR_ALIAS;
+  }
   const size_t ybytes = (size_t)m * n * (y_bf16 ? 2 : 4);
   if (overlaps(y, ybytes, x, (size_t)m * k * 2) || overlaps(y, ybytes, w, (size_t)n * k * 2))
     return FO_ERR_ALIAS;
@@ -193,7 +224,7 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
   }
   a.local = s->local;
   a.strict = s->mode == FO_SCHED_STRICT ? 1 : 0;
-  a.arrived = s->arrived;
+  a.arrived = fz ? nullptr : s->arrived;   // fused: the flags gate the incoming partials only
   a.done_flags = done;
   a.epoch = s->epoch;
   a.timeout_ticks = ns_to_ticks(s->timeout_ns ? s->timeout_ns : kDefaultTimeoutNs, I->wall_hz);
@@ -208,7 +239,7 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
   for (int c = 0; c < R; ++c) split[c] = 1;
   if (s->split) {
     for (int c = 0; c < R; ++c) split[c] = s->split[c];
-  } else if (s->arrived && R > 1) {
+  } else if (s->arrived && R > 1 && !rs_mode) {
     // the last peer in priority order is the chunk expected to land last
     int tail = -1;
     for (int i = R - 1; i >= 0; --i)
@@ -244,6 +275,27 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
       a.part_base[c] = -1;
     }
     total_units += a.units[c] + a.red_units[c];
+  }
+  if (fz) {
+    // the local chunk's tiles get shard units (RED_SLICES row slices each)
+    // and a ready list; the incoming partials are summed in priority order
+    const int c = s->local;
+    a.fused = 1;
+    a.shard = fz->shard;
+    a.shard_bf16 = fz->shard_bf16 ? 1 : 0;
+    a.inc_arrived = s->arrived;
+    a.red_units[c] = p.tiles * RED_SLICES;
+    a.ctr_base[c] = (int32_t)ctr_used;
+    ctr_used += (size_t)p.tiles;
+    total_units += a.red_units[c];
+    a.ninc = 0;
+    for (int i = 0; i < R; ++i) {
+      const int q = a.order[i];
+      if (q == c) continue;
+      a.inc[a.ninc] = fz->incoming[q];
+      a.inc_chunk[a.ninc] = q;
+      ++a.ninc;
+    }
   }
   a.ready_off = p.ready_off;
   if (part_used > 0 && ws_bytes < p.partial_offset + part_used * partial_slot_bytes(p.tile))
@@ -285,6 +337,17 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
     // claiming until no work is left.
     a.one_unit = (a.arrived != nullptr && ok && single) ? 1 : 0;
   }
+  if (fz) {
+    // shard units are assigned statically (workgroup b takes b, b + grid,
+    // ...) only when every workgroup's static first claim is a GEMM unit, so
+    // no dynamic claim of a shard unit can happen
+    bool exact = true;
+    for (int g = 0; g < XCDS; ++g) {
+      const int64_t wgs_g = (a.grid - g + XCDS - 1) / XCDS;
+      exact = exact && (int64_t)a.gunits[g] == wgs_g;
+    }
+    a.fused_static = exact ? 1 : 0;
+  }
 
   hipError_t e = launch_gemm(a, p.tile, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) { record(e); return FO_ERR_HIP; }
@@ -324,6 +387,15 @@ fo_status fo_gemm_rs(const void *x, const void *w, float *partial, uint32_t *don
                      int64_t n, int64_t k, const fo_schedule *s, void *ws, size_t ws_bytes,
                      void *stream) {
   return run_gemm(x, w, partial, false, done, true, m, n, k, s, ws, ws_bytes, stream);
+}
+
+fo_status fo_gemm_rs_reduce(const void *x, const void *w, float *partial, uint32_t *done,
+                            void *shard, fo_dtype shard_dtype, const float *const *incoming,
+                            int64_t m, int64_t n, int64_t k, const fo_schedule *s, void *ws,
+                            size_t ws_bytes, void *stream) {
+  if (shard_dtype != FO_F32 && shard_dtype != FO_BF16) return FO_ERR_DTYPE;
+  const FusedRs fz{shard, shard_dtype == FO_BF16, incoming};
+  return run_gemm(x, w, partial, false, done, true, m, n, k, s, ws, ws_bytes, stream, &fz);
 }
 
 fo_status fo_chunk_reduce(void *dst, fo_dtype dst_dtype, const float *const *srcs, int64_t n,

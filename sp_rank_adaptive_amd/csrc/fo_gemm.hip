@@ -187,6 +187,53 @@ __device__ __forceinline__ void group_tile(const GemmArgs &a, int g, int tl, int
   tn = clo + tl - (tl / ncols) * ncols;
 }
 
+// Reduce unit v of chunk c: wait (wave 0, all lanes) until the v / RED_SLICES-th
+// tile of the chunk is published on its ready list, then fill r.  A split
+// tile is published once all its splits are written; the tile counter reads S
+// only after all S splits counted themselves, and reading it, then an acquire
+// fence, orders this unit's reads of the partials after every split's
+// stores.  An unsplit tile (the fused shard units) is published by its only
+// unit after its written-through stores; the shard unit reads it with
+// coherent loads and needs no fence.  On abort or timeout r.c = -2.
+__device__ __forceinline__ void take_reduce_unit(const GemmArgs &a, int c, uint32_t v, Unit &r) {
+  const int lane = threadIdx.x & 63;
+  uint32_t e = 0;
+  if (lane == 0) {
+    const uint32_t *slot = a.ws32 + a.ready_off + a.ctr_base[c] + v / RED_SLICES;
+    const uint64_t t0 = now_ticks();
+    while ((e = load_relaxed(slot)) == 0u) {
+      if (load_relaxed(a.ws32 + WS_ABORT) || now_ticks() - t0 > a.timeout_ticks) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  e = __builtin_amdgcn_readfirstlane(e);
+  if (e == 0u) {   // abort or timeout while waiting
+    if (lane == 0) {
+      if (a.status) __hip_atomic_store(a.status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(a.ws32 + WS_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    r.c = -2;
+    return;
+  }
+  const int tile = (int)e - 1;
+  if (a.split[c] > 1) {
+    if (lane == 0) {
+      const uint32_t *ctr = a.ws32 + WS_TILE_CTR + a.ctr_base[c] + tile;
+      const uint64_t t0 = now_ticks();   // bounded like every other wait
+      while (load_relaxed_agent(ctr) < (uint32_t)a.split[c] && now_ticks() - t0 <= a.timeout_ticks)
+        __builtin_amdgcn_s_sleep(1);
+    }
+    fence_acquire_agent();
+  }
+  r.c = c;
+  r.tm = tile / a.tiles_n;
+  r.tn = tile - r.tm * a.tiles_n;
+  r.sp = (int)(v % RED_SLICES);
+  r.first = 0;
+  r.red = 1;
+}
+
 // Wave 0 of a workgroup picks the next unit (all 64 lanes call this).
 // One round trip reads every arrival flag and every claim counter in
 // parallel across the lanes; then a scan in priority order takes the first
@@ -214,6 +261,16 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
   // counters' cache lines.  When no workgroup gets a second unit
   // (static_rr == 2) the first unit comes from the static first claim below
   // and the next claim ends the workgroup.
+  // Fused shard units with one GEMM unit per workgroup: after its static
+  // first unit, workgroup b takes shard units b, b + grid, ... of the local
+  // chunk (no claim counter).
+  if (a.fused_static && rank_hint < 0) {
+    const uint32_t v = blockIdx.x + (uint32_t)st.taken * (uint32_t)a.grid;
+    ++st.taken;
+    if (v >= (uint32_t)a.red_units[a.local]) return r;
+    take_reduce_unit(a, a.local, v, r);
+    return r;
+  }
   if (a.static_rr == 2 && rank_hint < 0) return r;   // one unit per workgroup: done
   if (a.one_unit && st.taken == 1) return r;          // first claim got a unit: done
   if (a.static_rr == 1) {
@@ -387,43 +444,7 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
         if (lane == 0) v = fetch_add_relaxed(a.ws32 + WS_RED_CLAIM + c, 1u);
         v = __builtin_amdgcn_readfirstlane(v);
         if (v >= (uint32_t)a.red_units[c]) continue;   // all taken: look again
-        // wait for the v / RED_SLICES-th tile of the chunk to be published
-        uint32_t e = 0;
-        if (lane == 0) {
-          const uint32_t *slot = a.ws32 + a.ready_off + a.ctr_base[c] + v / RED_SLICES;
-          const uint64_t t0 = now_ticks();
-          while ((e = load_relaxed(slot)) == 0u) {
-            if (load_relaxed(a.ws32 + WS_ABORT) || now_ticks() - t0 > a.timeout_ticks) break;
-            __builtin_amdgcn_s_sleep(2);
-          }
-        }
-        e = __builtin_amdgcn_readfirstlane(e);
-        if (e == 0u) {   // abort or timeout while waiting
-          if (lane == 0) {
-            if (a.status) __hip_atomic_store(a.status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_SYSTEM);
-            __hip_atomic_store(a.ws32 + WS_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-          r.c = -2;
-          return r;
-        }
-        const int tile = (int)e - 1;
-        // The tile counter reads S only after all S splits counted themselves;
-        // reading it, then an acquire fence, orders this unit's reads of the
-        // partials after every split's release fence.
-        if (lane == 0) {
-          const uint32_t *ctr = a.ws32 + WS_TILE_CTR + a.ctr_base[c] + tile;
-          const uint64_t t0 = now_ticks();   // bounded like every other wait
-          while (load_relaxed_agent(ctr) < (uint32_t)a.split[c] && now_ticks() - t0 <= a.timeout_ticks)
-            __builtin_amdgcn_s_sleep(1);
-        }
-        fence_acquire_agent();
-        r.c = c;
-        r.tm = tile / a.tiles_n;
-        r.tn = tile - r.tm * a.tiles_n;
-        r.sp = (int)(v % RED_SLICES);
-        r.first = 0;
-        r.red = 1;
+        take_reduce_unit(a, c, v, r);
         return r;
       }
       uint32_t u = 0;
@@ -540,6 +561,97 @@ __device__ __forceinline__ void reduce_unit(const GemmArgs &a, int c, int tile, 
   }
 }
 
+// Shard unit (fo_gemm_rs_reduce): row slice `slice` of tile `tile` of the
+// local chunk, whose partial is in memory (written through by its unit).
+// Waits until every incoming partial has landed, then sums the local partial
+// and the incoming ones in summation order (fp32, left to right: the order
+// fo_chunk_reduce uses, so the bits match the unfused pair) and stores the
+// shard rows (fp32, or bf16 rounded to nearest even).  The partial and the
+// incoming partials are read with system-coherent loads: a copy engine or
+// another XCD wrote them during the launch.  Returns false after a timeout
+// (status set, the launch aborted).
+template <int BM, int BN, int NTT>
+__device__ __forceinline__ bool shard_unit(const GemmArgs &a, int slice, int64_t row0, int64_t rowlim,
+                                           int64_t col0) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));   // computed per unit, not kept live across the loop
+  if (a.inc_arrived) {
+    const uint64_t t0 = now_ticks();
+    for (;;) {
+      bool ok = true;
+      if (tid < a.ninc) ok = epoch_reached(load_relaxed(a.inc_arrived + a.inc_chunk[tid]), a.epoch);
+      if (__syncthreads_and(ok)) break;
+      int out = 0;
+      if (tid == 0) out = (now_ticks() - t0 > a.timeout_ticks) || load_relaxed(a.ws32 + WS_ABORT) != 0u;
+      if (__syncthreads_or(out)) {
+        if (tid == 0) {
+          if (a.status) __hip_atomic_store(a.status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_SYSTEM);
+          __hip_atomic_store(a.ws32 + WS_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return false;
+      }
+      __builtin_amdgcn_s_sleep(4);
+    }
+  }
+  const int64_t N = a.n;
+  const int bytes = (int)((int64_t)a.mc * N * 4);              // one chunk of fp32 rows (< 2 GiB)
+  const int64_t lrow0 = row0 - (int64_t)a.local * a.mc;        // first row inside the local chunk
+  const __amdgpu_buffer_rsrc_t rp =
+      uniform_rsrc(reinterpret_cast<const float *>(a.y) + (int64_t)a.local * a.mc * N, bytes);
+  constexpr int ROWS = BM / RED_SLICES;
+  constexpr int PPR = BN / 4;                       // 16-byte pieces per row
+  constexpr int PER = (ROWS * PPR + NTT - 1) / NTT; // pieces per thread
+  constexpr int KB = 8;                             // sources whose loads are issued together
+  const int r0 = slice * ROWS;
+  int off[PER];
+  bool ok[PER];
+  f32x4 v[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int pc = tid + q * NTT;
+    const int rr = r0 + pc / PPR, cc = pc - (pc / PPR) * PPR;
+    const int64_t col = col0 + cc * 4;
+    ok[q] = pc < ROWS * PPR && row0 + rr < rowlim && col < N;
+    off[q] = ok[q] ? (int)(((lrow0 + rr) * N + col) * 4) : 0;
+    if (ok[q]) v[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, off[q], 0, 1 | 2 | 16));
+  }
+  // the loads of up to KB sources are issued together, then added in
+  // summation order
+  for (int s0 = 0; s0 < a.ninc; s0 += KB) {
+    f32x4 t[KB][PER];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      if (s0 + k < a.ninc) {
+        const __amdgpu_buffer_rsrc_t ri = uniform_rsrc(a.inc[s0 + k], bytes);
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+          if (ok[q]) t[k][q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ri, off[q], 0, 1 | 2 | 16));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < KB; ++k)
+      if (s0 + k < a.ninc) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+          if (ok[q]) v[q] += t[k][q];
+      }
+  }
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    if (!ok[q]) continue;
+    const int64_t idx = off[q] / 4;
+    if (a.shard_bf16) {
+      const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[q][0]) | ((uint32_t)f32_to_bf16_rne(v[q][1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_rne(v[q][2]) | ((uint32_t)f32_to_bf16_rne(v[q][3]) << 16);
+      *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.shard) + idx) = u32x2{lo, hi};
+    } else {
+      __builtin_nontemporal_store(v[q], reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.shard) + idx));
+    }
+  }
+  return true;
+}
+
 // Wait for this wave's copies of stage j when `later` stages issued after it
 // may stay in flight (VR copies per stage and wave).
 template <int VR, int STAGES>
@@ -629,7 +741,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
     const int KT = (int)((k1 - k0 + BK - 1) / BK);
 
     if (un.red) {
-      reduce_unit<BM, BN, NTT>(a, c, tile, un.sp, row0, rowlim, col0);
+      if (a.fused && c == a.local)
+        shard_unit<BM, BN, NTT>(a, un.sp, row0, rowlim, col0);
+      else
+        reduce_unit<BM, BN, NTT>(a, c, tile, un.sp, row0, rowlim, col0);
     } else {
 
     // Stage layout in LDS: BM rows of X then BN rows of W, ROWB bytes each,
@@ -850,7 +965,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
       const bool bf = to_out && a.y_bf16;
       // split partials (read by reduce units on any XCD) and GEMM-RS output
       // (read by the consumer of the done flags) are written through
-      const bool wt = !to_out || a.done_flags != nullptr;
+      const bool wt = !to_out || a.done_flags != nullptr || a.fused;
 #pragma unroll
       for (int h = 0; h < HALVES; ++h) {
         __syncthreads();
@@ -873,6 +988,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
           if (row >= rlim || col >= clim) continue;
           const f32x4 val = *reinterpret_cast<const f32x4 *>(stg + r * SROW + cc * 4);
           put4(dbase, ld, row, col, clim, bf, vec_ok, wt, val);
+        }
+      }
+      if (to_out && a.fused && c == a.local) {
+        // fused: publish the local tile for the shard units once its
+        // written-through stores are acknowledged
+        wait_stores();
+        __syncthreads();
+        if (etid == 0) {
+          const uint32_t idx = fetch_add_relaxed(a.ws32 + WS_RED_READY + c, 1u);
+          store_relaxed_agent(a.ws32 + a.ready_off + a.ctr_base[c] + idx, (uint32_t)(tile + 1));
         }
       }
       if (!to_out) {

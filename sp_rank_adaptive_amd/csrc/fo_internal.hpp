@@ -47,6 +47,16 @@ struct GemmArgs {
   int32_t static_rr;          // every unit assigned statically: 1 round-robin per XCD, 2 one per workgroup
   int32_t all_unsplit;        // 1: no chunk is split
   int32_t one_unit;           // flags: a workgroup whose first claim succeeds leaves after it
+  // Fused reduce of the local chunk (fo_gemm_rs_reduce): the local chunk's
+  // reduce units sum its partial and the incoming partials into the shard.
+  int32_t fused;                      // 1: red_units[local] are shard units
+  int32_t fused_static;               // 1: shard units assigned statically (b, b + grid, ...)
+  int32_t shard_bf16;
+  int32_t ninc;                       // incoming partials, in summation order
+  void *shard;                        // [mc][n]
+  const uint32_t *inc_arrived;        // device [R] flags of the incoming partials, or null
+  const float *inc[FO_MAX_CHUNKS];    // incoming partials [mc][n] fp32
+  int32_t inc_chunk[FO_MAX_CHUNKS];   // chunk id of inc[i] (its flag)
   int32_t gunits[XCDS];       // units per work-queue group over all chunks
   const uint32_t *arrived;    // device [R] or null
   uint32_t *done_flags;       // device [R] or null

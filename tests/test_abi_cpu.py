@@ -130,6 +130,43 @@ def test_gemm_rs_validation(L):
     assert L.fo_gemm_rs(A, A, A2, None, 256, 512, 500, ctypes.byref(s), WS, 1 << 30, None) == fo.FO_ERR_ALIGN
 
 
+def test_gemm_rs_reduce_validation(L):
+    R, m, n, k = 4, 256, 512, 512
+    mc = m // R
+    inc_ok = [A2 + 0x1000000 * (q + 1) for q in range(R)]
+    shard = A2 + 0x8000000
+
+    def fz(part=A2, sh=shard, dt=fo.FO_F32, inc=inc_ok, nn=n, s=None, x=A, wsb=1 << 30):
+        if s is None:
+            s, fz.keep = sched()
+        arr = None if inc is None else (ctypes.c_void_p * R)(*inc)
+        return L.fo_gemm_rs_reduce(x, A + 0x100000, part, None, sh, dt, arr, m, nn, k,
+                                   ctypes.byref(s), WS, wsb, None)
+    assert fz(x=None) == fo.FO_ERR_NULL
+    assert fz(sh=None) == fo.FO_ERR_NULL
+    assert fz(inc=None) == fo.FO_ERR_NULL
+    nul = list(inc_ok)
+    nul[1] = None
+    assert fz(inc=nul) == fo.FO_ERR_NULL
+    nul[0] = None                                   # the local chunk's entry is ignored:
+    nul[1] = inc_ok[1]                              # the call gets as far as the workspace
+    assert fz(inc=nul, wsb=16) == fo.FO_ERR_WORKSPACE
+    assert fz(dt=7) == fo.FO_ERR_DTYPE
+    assert fz(nn=510) == fo.FO_ERR_ALIGN              # n % 4
+    assert fz(sh=shard + 4) == fo.FO_ERR_ALIGN
+    mis = list(inc_ok)
+    mis[2] += 4
+    assert fz(inc=mis) == fo.FO_ERR_ALIGN
+    s, keep = sched(split=[1, 2, 1, 1])             # the fused launch takes no split
+    assert fz(s=s) == fo.FO_ERR_SCHEDULE
+    assert fz(sh=A2 + 64) == fo.FO_ERR_ALIAS          # shard inside the partials
+    over = list(inc_ok)
+    over[3] = shard + mc * n * 4 - 16                 # incoming overlaps the shard
+    assert fz(inc=over) == fo.FO_ERR_ALIAS
+    over[3] = A2 + 4096                               # incoming inside the partials
+    assert fz(inc=over) == fo.FO_ERR_ALIAS
+
+
 def test_chunk_reduce_validation(L):
     R = 4
     n = 1024
