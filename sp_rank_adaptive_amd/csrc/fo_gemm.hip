@@ -372,12 +372,18 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
     }
     const uint64_t landed = __ballot(ok);
     const uint64_t red_left = __ballot(redp);
-    // GEMM units left per (order position, group), 8 positions per batch
-    uint64_t gmask[FO_MAX_CHUNKS / 8];
-    uint32_t left[FO_MAX_CHUNKS / 8];
+    // GEMM units left per (order position, group), 8 positions per batch of
+    // 64 lanes; each batch is looked at as it is read (no arrays indexed at
+    // run time: the compiler would keep them in registers across the whole
+    // persistent loop).  has_work covers every batch read so far; the walk
+    // stops early only at a pick or at a chunk with work left, so has_work is
+    // nonzero whenever the walk did not reach the end.
     const int nb = (R + 7) / 8;
     uint64_t has_work = 0;
-    for (int b = 0; b < nb; ++b) {
+    int pick_s = -1, pick_g = -1, pick_red = 0;
+    bool stop = false;
+#pragma nounroll
+    for (int b = 0; b < nb && !stop; ++b) {
       const int pidx = b * 64 + lane;
       uint32_t lv = 0;
       if (pidx < R * XCDS) {
@@ -387,45 +393,44 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
         const uint32_t tot = group_units(a, c, g);
         lv = cnt < tot ? tot - cnt : 0;
       }
-      left[b] = lv;
-      gmask[b] = __ballot(lv > 0);
-      for (uint64_t mm = gmask[b]; mm; mm &= mm - 1) has_work |= 1ull << (b * 8 + __builtin_ctzll(mm) / XCDS);
-    }
-    int pick_s = -1, pick_g = -1, pick_red = 0;
-    for (int sidx = 0; sidx < R; ++sidx) {
-      const int b = sidx / 8;
-      const uint64_t gm = (gmask[b] >> ((sidx % 8) * XCDS)) & 0xFFull;
-      const bool redw = ((red_left >> sidx) & 1) && gm == 0;
-      if (!gm && !redw) continue;
-      const bool is_landed = (landed >> sidx) & 1;
-      if (!is_landed) {
-        if (a.strict) break;   // strict: the first chunk with work decides
-        continue;
-      }
-      if (gm) {
-        // first claim of a workgroup: the q-th workgroup of an XCD skips the
-        // first q units its XCD's group has left (in priority order over
-        // landed chunks), so the XCD's workgroups start on distinct units
-        if (rank_hint >= 0 && !a.strict && ((gm >> xg) & 1)) {
-          const uint32_t own = __shfl(left[b], (sidx % 8) * XCDS + xg);
-          if ((uint32_t)rank_hint >= own) { rank_hint -= (int)own; continue; }
+      const uint64_t gmb = __ballot(lv > 0);
+      for (uint64_t mm = gmb; mm; mm &= mm - 1) has_work |= 1ull << (b * 8 + __builtin_ctzll(mm) / XCDS);
+      const int s_end = R < b * 8 + 8 ? R : b * 8 + 8;
+      for (int sidx = b * 8; sidx < s_end; ++sidx) {
+        const uint64_t gm = (gmb >> ((sidx % 8) * XCDS)) & 0xFFull;
+        const bool redw = ((red_left >> sidx) & 1) && gm == 0;
+        if (!gm && !redw) continue;
+        const bool is_landed = (landed >> sidx) & 1;
+        if (!is_landed) {
+          if (a.strict) { stop = true; break; }   // strict: the first chunk with work decides
+          continue;
         }
-        pick_s = sidx;
-        if ((gm >> xg) & 1) {
-          pick_g = xg;
-        } else {
-          uint32_t best = 0;
-          for (uint64_t g2 = gm; g2; g2 &= g2 - 1) {
-            const int g = __builtin_ctzll(g2);
-            const uint32_t lv = __shfl(left[b], (sidx % 8) * XCDS + g);
-            if (lv > best) { best = lv; pick_g = g; }
+        if (gm) {
+          // first claim of a workgroup: the q-th workgroup of an XCD skips the
+          // first q units its XCD's group has left (in priority order over
+          // landed chunks), so the XCD's workgroups start on distinct units
+          if (rank_hint >= 0 && !a.strict && ((gm >> xg) & 1)) {
+            const uint32_t own = __shfl(lv, (sidx % 8) * XCDS + xg);
+            if ((uint32_t)rank_hint >= own) { rank_hint -= (int)own; continue; }
           }
+          pick_s = sidx;
+          if ((gm >> xg) & 1) {
+            pick_g = xg;
+          } else {
+            uint32_t best = 0;
+            for (uint64_t g2 = gm; g2; g2 &= g2 - 1) {
+              const int g = __builtin_ctzll(g2);
+              const uint32_t lg = __shfl(lv, (sidx % 8) * XCDS + g);
+              if (lg > best) { best = lg; pick_g = g; }
+            }
+          }
+        } else {
+          pick_s = sidx;
+          pick_red = 1;
         }
-      } else {
-        pick_s = sidx;
-        pick_red = 1;
+        stop = true;
+        break;
       }
-      break;
     }
     if (pick_s < 0 && rank_hint >= 0) {   // fewer units than workgroups: normal claim
       rank_hint = -1;
@@ -563,37 +568,23 @@ __device__ __forceinline__ void reduce_unit(const GemmArgs &a, int c, int tile, 
 
 // Shard unit (fo_gemm_rs_reduce): row slice `slice` of tile `tile` of the
 // local chunk, whose partial is in memory (written through by its unit).
-// Waits until every incoming partial has landed, then sums the local partial
-// and the incoming ones in summation order (fp32, left to right: the order
-// fo_chunk_reduce uses, so the bits match the unfused pair) and stores the
-// shard rows (fp32, or bf16 rounded to nearest even).  The partial and the
-// incoming partials are read with system-coherent loads: a copy engine or
-// another XCD wrote them during the launch.  Returns false after a timeout
-// (status set, the launch aborted).
+// Sums the local partial and the incoming partials in summation order (fp32,
+// left to right: the order fo_chunk_reduce uses, so the bits match the
+// unfused pair) and stores the shard rows (fp32, or bf16 rounded to nearest
+// even).  Each wave keeps its running sums in registers and adds, whenever it
+// finds some, the longest run of pending sources whose flags show the epoch:
+// only the sources that land last are left to read after the last landing,
+// and all of them are read together when they are already there.  The
+// partial and the incoming partials are read with system-coherent loads: a
+// copy engine or another XCD wrote them during the launch.  Returns false
+// after a timeout (status set, the launch aborted).  No barrier: the waves of
+// the workgroup run through it independently.
 template <int BM, int BN, int NTT>
 __device__ __forceinline__ bool shard_unit(const GemmArgs &a, int slice, int64_t row0, int64_t rowlim,
                                            int64_t col0) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));   // computed per unit, not kept live across the loop
-  if (a.inc_arrived) {
-    const uint64_t t0 = now_ticks();
-    for (;;) {
-      bool ok = true;
-      if (tid < a.ninc) ok = epoch_reached(load_relaxed(a.inc_arrived + a.inc_chunk[tid]), a.epoch);
-      if (__syncthreads_and(ok)) break;
-      int out = 0;
-      if (tid == 0) out = (now_ticks() - t0 > a.timeout_ticks) || load_relaxed(a.ws32 + WS_ABORT) != 0u;
-      if (__syncthreads_or(out)) {
-        if (tid == 0) {
-          if (a.status) __hip_atomic_store(a.status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_SYSTEM);
-          __hip_atomic_store(a.ws32 + WS_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        return false;
-      }
-      __builtin_amdgcn_s_sleep(4);
-    }
-  }
+  const int lane = tid & 63;
   const int64_t N = a.n;
   const int bytes = (int)((int64_t)a.mc * N * 4);              // one chunk of fp32 rows (< 2 GiB)
   const int64_t lrow0 = row0 - (int64_t)a.local * a.mc;        // first row inside the local chunk
@@ -614,28 +605,58 @@ __device__ __forceinline__ bool shard_unit(const GemmArgs &a, int slice, int64_t
     const int64_t col = col0 + cc * 4;
     ok[q] = pc < ROWS * PPR && row0 + rr < rowlim && col < N;
     off[q] = ok[q] ? (int)(((lrow0 + rr) * N + col) * 4) : 0;
+    v[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (ok[q]) v[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, off[q], 0, 1 | 2 | 16));
   }
-  // the loads of up to KB sources are issued together, then added in
-  // summation order
-  for (int s0 = 0; s0 < a.ninc; s0 += KB) {
-    f32x4 t[KB][PER];
-#pragma unroll
-    for (int k = 0; k < KB; ++k) {
-      if (s0 + k < a.ninc) {
-        const __amdgpu_buffer_rsrc_t ri = uniform_rsrc(a.inc[s0 + k], bytes);
-#pragma unroll
-        for (int q = 0; q < PER; ++q)
-          if (ok[q]) t[k][q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ri, off[q], 0, 1 | 2 | 16));
+  const uint64_t t0 = now_ticks();
+  int s = 0;
+  while (s < a.ninc) {
+    // sources s .. e-1 have landed (lane i looks at source i's flag)
+    int e = a.ninc;
+    if (a.inc_arrived) {
+      bool landed = true;
+      if (lane < a.ninc) landed = epoch_reached(load_relaxed(a.inc_arrived + a.inc_chunk[lane]), a.epoch);
+      const uint64_t pending = ~__ballot(landed) >> s;
+      if (pending) e = s + __builtin_ctzll(pending);
+      if (e == s) {
+        bool out = false;
+        if (lane == 0) out = (now_ticks() - t0 > a.timeout_ticks) || load_relaxed(a.ws32 + WS_ABORT) != 0u;
+        if (__ballot(out)) {
+          if (lane == 0) {
+            if (a.status) __hip_atomic_store(a.status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_SYSTEM);
+            __hip_atomic_store(a.ws32 + WS_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          return false;
+        }
+        __builtin_amdgcn_s_sleep(4);
+        continue;
       }
     }
+    // the loads of up to KB sources are issued together, then added in
+    // summation order
+    for (; s < e; s += KB) {
+      f32x4 t[KB][PER];
 #pragma unroll
-    for (int k = 0; k < KB; ++k)
-      if (s0 + k < a.ninc) {
+      for (int k = 0; k < KB; ++k) {
 #pragma unroll
-        for (int q = 0; q < PER; ++q)
-          if (ok[q]) v[q] += t[k][q];
+        for (int q = 0; q < PER; ++q) t[k][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (s + k < e) {
+          const __amdgpu_buffer_rsrc_t ri = uniform_rsrc(a.inc[s + k], bytes);
+#pragma unroll
+          for (int q = 0; q < PER; ++q)
+            if (ok[q]) t[k][q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ri, off[q], 0, 1 | 2 | 16));
+        }
       }
+#pragma unroll
+      for (int k = 0; k < KB; ++k)
+        if (s + k < e) {
+#pragma unroll
+          for (int q = 0; q < PER; ++q)
+            if (ok[q]) v[q] += t[k][q];
+        }
+    }
+    s = e;
   }
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
@@ -990,7 +1011,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
           put4(dbase, ld, row, col, clim, bf, vec_ok, wt, val);
         }
       }
-      if (to_out && a.fused && c == a.local) {
+      if (a.fused && to_out && c == a.local) {
         // fused: publish the local tile for the shard units once its
         // written-through stores are acknowledged
         wait_stores();
