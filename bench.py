@@ -542,6 +542,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--link-sweep", action="store_true",
                     help="also sweep the per-link bandwidth (end-to-end time and tail per schedule)")
+    ap.add_argument("--steps-only", action="store_true",
+                    help="time the steps and launch nothing else (counter runs name the GEMM launches "
+                         "by their order: fo_ag_gemm, fo_gemm_rs, ...)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB copy (for scaling profiled byte counters)")
     args = ap.parse_args()
@@ -619,10 +622,11 @@ def main():
             "flops_per_launch": d_flops,
         },
     }
-    f_us, u_us = fused_rs_us(fo, path)
-    out["gemm_rs_reduce_fused_cfg3"] = {"us": round(f_us, 2), "unfused_rs_plus_reduce_us": round(u_us, 2)}
-    log(f"fused GEMM-RS + reduce {f_us:.1f} us against {u_us:.1f} us unfused")
-    if not args.quick:
+    if not args.steps_only:
+        f_us, u_us = fused_rs_us(fo, path)
+        out["gemm_rs_reduce_fused_cfg3"] = {"us": round(f_us, 2), "unfused_rs_plus_reduce_us": round(u_us, 2)}
+        log(f"fused GEMM-RS + reduce {f_us:.1f} us against {u_us:.1f} us unfused")
+    if not args.quick and not args.steps_only:
         for cfg in (wl.CFG5,):
             tf, ms = gemm_rate(fo, cfg)
             out["qkv_ag_gemm_cfg5"] = {"us": round(ms * 1e3, 1), "tflops": round(tf, 1)}
