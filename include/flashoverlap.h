@@ -168,16 +168,41 @@ fo_status fo_gemm_rs(const void *x, const void *w, float *partial, uint32_t *don
  *             is ignored.  With s->arrived, incoming[q] is read only after
  *             arrived[q] shows the epoch (system-coherent loads: a copy
  *             engine may write it during the call); the GEMM itself is not
- *             gated.  The launch holds its workgroups until every partial has
- *             landed, so use it when they land before the local chunk's
- *             tiles finish; otherwise fo_gemm_rs + fo_chunk_reduce.
+ *             gated.  Shard units are taken after every GEMM unit; a
+ *             workgroup holding one adds each run of landed partials as it
+ *             lands, so only the partials that land last are read after the
+ *             last landing.
  * n % 4 == 0 and (m/R) * n * 4 < 2^31 are required; split factors other
  * than 1 are rejected.  Errors as fo_gemm_rs, plus DTYPE, ALIAS (shard
- * overlapping partial, x or w). */
+ * overlapping partial, x or w; an incoming partial overlapping the shard or
+ * partial). */
 fo_status fo_gemm_rs_reduce(const void *x, const void *w, float *partial, uint32_t *done,
                             void *shard, fo_dtype shard_dtype, const float *const *incoming,
                             int64_t m, int64_t n, int64_t k, const fo_schedule *s,
                             void *ws, size_t ws_bytes, void *stream);
+
+/* Ring form of the fused GEMM-RS (technical summary §2, Flash-RS: at each
+ * step a rank adds its partial of the chunk passing through it to the
+ * accumulated partial received from its predecessor and forwards the sum; the
+ * chunk that stays local is the last step).  Computes fo_gemm_rs's partials
+ * and, in the same launch, for every chunk c with incoming[c] != NULL:
+ *   c != local: partial[rows of c] = partial[rows of c] + incoming[c]
+ *               (fp32, in place, written through: the message to forward);
+ *   c == local: shard = partial[rows of local] + incoming[local]
+ *               (incoming[local] NULL: shard = partial rows of local).
+ * done[c] = epoch is released once chunk c's rows (or the shard) are final.
+ * With s->arrived, chunk c's sum starts only after arrived[c] shows the epoch
+ * (system-coherent loads of incoming[c]); its workgroups take other work
+ * meanwhile.  In a ring of R ranks the predecessor's message for chunk c
+ * holds the partials of ranks c+1 .. local-1; the chunk with no incoming
+ * partial (local-1, whose accumulation this rank starts) is sent as computed.
+ *   shard, shard_dtype: as fo_gemm_rs_reduce.
+ *   incoming  host [R] array of device fp32 [m/R][n] pointers, any NULL.
+ * Requirements and errors as fo_gemm_rs_reduce. */
+fo_status fo_gemm_rs_ring(const void *x, const void *w, float *partial, uint32_t *done,
+                          void *shard, fo_dtype shard_dtype, const float *const *incoming,
+                          int64_t m, int64_t n, int64_t k, const fo_schedule *s,
+                          void *ws, size_t ws_bytes, void *stream);
 
 /* Chunk reduce-add (technical summary §1 DP reduce-scatter, §2 Flash-RS).
  *   srcs  host [R] array of device fp32 pointers, n elements each.

@@ -150,6 +150,33 @@ def reduce(srcs) -> np.ndarray:
     return out.reshape(np.shape(srcs[0]))
 
 
+def ring_rs_rank(x_bits, w_bits, R: int, local: int, incoming):
+    """One rank's step of the ring reduce-scatter fused with its GEMM: its
+    partials X*W by row chunk, each chunk with an incoming accumulated partial
+    (from the predecessor) plus that partial; the local chunk's sum is the
+    shard.  Returns (forward, shard): forward [m, n] fp64 holds, per chunk c,
+    P_c + incoming[c] (or P_c when incoming[c] is None); shard = the local
+    chunk's rows of forward.
+
+    Pages: gist.science technical summary §2, Flash-RS (each step adds the
+    rank's own partial of the passing chunk to the accumulated one received
+    and forwards the sum; the local chunk is the last step).
+    """
+    p = gemm(x_bits, w_bits)
+    m, n = p.shape
+    mc = m // R
+    fwd = p.copy()
+    for c in range(R):
+        a = incoming[c]
+        if a is None:
+            continue
+        a = np.asarray(a, dtype=np.float64)
+        if a.shape != (mc, n):
+            raise ValueError("incoming partial shape")
+        fwd[c * mc:(c + 1) * mc] += a
+    return fwd, fwd[local * mc:(local + 1) * mc].copy()
+
+
 def gemm_rs_shard(x_bits, w_bits, R: int, local: int, incoming) -> np.ndarray:
     """GEMM-RS local shard: rows of chunk `local` of X*W plus every incoming
     fp32 partial (incoming[local] ignored), summed exactly.

@@ -26,7 +26,7 @@ FO_F32, FO_BF16 = 0, 1
 FO_SCHED_READY_FIRST, FO_SCHED_STRICT = 0, 1
 FO_MAX_CHUNKS = 64
 
-EXPORTS = ("fo_workspace_bytes", "fo_ag_gemm", "fo_gemm_rs", "fo_gemm_rs_reduce", "fo_chunk_reduce",
+EXPORTS = ("fo_workspace_bytes", "fo_ag_gemm", "fo_gemm_rs", "fo_gemm_rs_reduce", "fo_gemm_rs_ring", "fo_chunk_reduce",
            "fo_emulate_arrivals", "fo_emulate_arrivals_gated", "fo_plan_ag_schedule", "fo_device_info", "fo_status_string",
            "fo_last_hip_error")
 
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.fo_gemm_rs.argtypes = [P, P, P, P, i64, i64, i64, S, P, sz, P]
     L.fo_gemm_rs_reduce.restype = i32
     L.fo_gemm_rs_reduce.argtypes = [P, P, P, P, P, i32, P, i64, i64, i64, S, P, sz, P]
+    L.fo_gemm_rs_ring.restype = i32
+    L.fo_gemm_rs_ring.argtypes = [P, P, P, P, P, i32, P, i64, i64, i64, S, P, sz, P]
     L.fo_chunk_reduce.restype = i32
     L.fo_chunk_reduce.argtypes = [P, i32, P, i64, S, P]
     L.fo_emulate_arrivals.restype = i32
@@ -244,6 +246,26 @@ def fo_gemm_rs_reduce(x, w, partial, done, shard, incoming, sched: Schedule, ws,
     del keep
     if raise_on_error:
         _check(st, "fo_gemm_rs_reduce")
+    return st
+
+
+def fo_gemm_rs_ring(x, w, partial, done, shard, incoming, sched: Schedule, ws, stream=None, *,
+                    raise_on_error=True) -> int:
+    """Ring form: fo_gemm_rs plus, in the same launch, partial[rows of c] +=
+    incoming[c] for every peer chunk with an incoming partial (in place) and
+    shard = partial[rows of local] + incoming[local].  incoming: R tensors or
+    None, indexed by chunk."""
+    m, k = x.shape
+    n = w.shape[0]
+    R = len(incoming)
+    arr = (ctypes.c_void_p * R)(*[_ptr(t) for t in incoming])
+    s, keep = sched._c()
+    st = lib().fo_gemm_rs_ring(_ptr(x), _ptr(w), _ptr(partial), _ptr(done), _ptr(shard),
+                               _dtype_code(shard), arr, m, n, k, ctypes.byref(s), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(stream))
+    del keep
+    if raise_on_error:
+        _check(st, "fo_gemm_rs_ring")
     return st
 
 

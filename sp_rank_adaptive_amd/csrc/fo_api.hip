@@ -137,6 +137,7 @@ struct FusedRs {
   void *shard;
   bool shard_bf16;
   const float *const *incoming;   // host [R] of device pointers
+  bool ring;                      // ring form: incoming[c] is chunk c's accumulated partial (may be null)
 };
 
 fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t *done,
@@ -153,11 +154,14 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
   if (rs_mode && s->arrived && !fz) return FO_ERR_SCHEDULE;
   if (fz) {
     if (!fz->shard || !fz->incoming) return FO_ERR_NULL;
+    // direct form: every peer's partial is required (incoming[local] is
+    // ignored); ring form: any entry may be null (no incoming partial)
+    auto used = [&](int c) { return fz->ring ? fz->incoming[c] != nullptr : c != s->local; };
     for (int c = 0; c < R; ++c)
-      if (c != s->local && !fz->incoming[c]) return FO_ERR_NULL;
+      if (!fz->ring && c != s->local && !fz->incoming[c]) return FO_ERR_NULL;
     if (n % 4 != 0 || !aligned16(fz->shard)) return FO_ERR_ALIGN;
     for (int c = 0; c < R; ++c)
-      if (c != s->local && !aligned16(fz->incoming[c])) return FO_ERR_ALIGN;
+      if (used(c) && !aligned16(fz->incoming[c])) return FO_ERR_ALIGN;
     if ((m / R) * n * 4 >= ((int64_t)1 << 31)) return FO_ERR_SHAPE;
     if (s->split)
       for (int c = 0; c < R; ++c)
@@ -171,8 +175,8 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
     // the shard
     const size_t inc_bytes = (size_t)(m / R) * n * 4;
     for (int c = 0; c < R; ++c)
-      if (c != s->local && (overlaps(fz->incoming[c], inc_bytes, fz->shard, shard_bytes) ||
-                            overlaps(fz->incoming[c], inc_bytes, y, (size_t)m * n * 4)))
+      if (used(c) && (overlaps(fz->incoming[c], inc_bytes, fz->shard, shard_bytes) ||
+                      overlaps(fz->incoming[c], inc_bytes, y, (size_t)m * n * 4)))
         return FO_ERR_ALIAS;
   }
   const size_t ybytes = (size_t)m * n * (y_bf16 ? 2 : 4);
@@ -277,24 +281,34 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
     total_units += a.units[c] + a.red_units[c];
   }
   if (fz) {
-    // the local chunk's tiles get shard units (RED_SLICES row slices each)
-    // and a ready list; the incoming partials are summed in priority order
-    const int c = s->local;
+    // Direct form: the local chunk's tiles get shard units (RED_SLICES row
+    // slices each) and a ready list; the incoming partials are summed in
+    // priority order.  Ring form: so do the tiles of every chunk with an
+    // incoming partial (inc[] indexed by chunk), and of the local chunk.
     a.fused = 1;
+    a.ring = fz->ring ? 1 : 0;
     a.shard = fz->shard;
     a.shard_bf16 = fz->shard_bf16 ? 1 : 0;
     a.inc_arrived = s->arrived;
-    a.red_units[c] = p.tiles * RED_SLICES;
-    a.ctr_base[c] = (int32_t)ctr_used;
-    ctr_used += (size_t)p.tiles;
-    total_units += a.red_units[c];
     a.ninc = 0;
-    for (int i = 0; i < R; ++i) {
-      const int q = a.order[i];
-      if (q == c) continue;
-      a.inc[a.ninc] = fz->incoming[q];
-      a.inc_chunk[a.ninc] = q;
-      ++a.ninc;
+    for (int c = 0; c < R; ++c) {
+      const bool units = fz->ring ? (fz->incoming[c] != nullptr || c == s->local) : c == s->local;
+      if (!units) continue;
+      a.red_units[c] = p.tiles * RED_SLICES;
+      a.ctr_base[c] = (int32_t)ctr_used;
+      ctr_used += (size_t)p.tiles;
+      total_units += a.red_units[c];
+    }
+    if (fz->ring) {
+      for (int c = 0; c < R; ++c) a.inc[c] = fz->incoming[c];
+    } else {
+      for (int i = 0; i < R; ++i) {
+        const int q = a.order[i];
+        if (q == s->local) continue;
+        a.inc[a.ninc] = fz->incoming[q];
+        a.inc_chunk[a.ninc] = q;
+        ++a.ninc;
+      }
     }
   }
   a.ready_off = p.ready_off;
@@ -346,7 +360,7 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
       const int64_t wgs_g = (a.grid - g + XCDS - 1) / XCDS;
       exact = exact && (int64_t)a.gunits[g] == wgs_g;
     }
-    a.fused_static = exact ? 1 : 0;
+    a.fused_static = (exact && !fz->ring) ? 1 : 0;
   }
 
   hipError_t e = launch_gemm(a, p.tile, static_cast<hipStream_t>(stream));
@@ -394,7 +408,15 @@ fo_status fo_gemm_rs_reduce(const void *x, const void *w, float *partial, uint32
                             int64_t m, int64_t n, int64_t k, const fo_schedule *s, void *ws,
                             size_t ws_bytes, void *stream) {
   if (shard_dtype != FO_F32 && shard_dtype != FO_BF16) return FO_ERR_DTYPE;
-  const FusedRs fz{shard, shard_dtype == FO_BF16, incoming};
+  const FusedRs fz{shard, shard_dtype == FO_BF16, incoming, false};
+  return run_gemm(x, w, partial, false, done, true, m, n, k, s, ws, ws_bytes, stream, &fz);
+}
+
+fo_status fo_gemm_rs_ring(const void *x, const void *w, float *partial, uint32_t *done, void *shard,
+                          fo_dtype shard_dtype, const float *const *incoming, int64_t m, int64_t n,
+                          int64_t k, const fo_schedule *s, void *ws, size_t ws_bytes, void *stream) {
+  if (shard_dtype != FO_F32 && shard_dtype != FO_BF16) return FO_ERR_DTYPE;
+  const FusedRs fz{shard, shard_dtype == FO_BF16, incoming, true};
   return run_gemm(x, w, partial, false, done, true, m, n, k, s, ws, ws_bytes, stream, &fz);
 }
 

@@ -363,15 +363,23 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
   }
   for (;;) {
     // landed[s]: chunk order[s] usable; red[s]: split chunk with reduce units left
-    bool ok = false, redp = false;
+    // ring form: a chunk's shard units wait for its incoming partial, so they
+    // are claimable only once it has landed (blocked: units left, not landed)
+    bool ok = false, redp = false, blk = false;
     if (lane < R) {
       const int c = a.order[lane];
       ok = a.arrived == nullptr || c == a.local ||
            epoch_reached(load_relaxed(a.arrived + c), a.epoch);
       if (a.red_units[c] > 0) redp = load_relaxed(a.ws32 + WS_RED_CLAIM + c) < (uint32_t)a.red_units[c];
+      if (redp && a.ring && a.inc_arrived != nullptr && a.inc[c] != nullptr &&
+          !epoch_reached(load_relaxed(a.inc_arrived + c), a.epoch)) {
+        redp = false;
+        blk = true;
+      }
     }
     const uint64_t landed = __ballot(ok);
     const uint64_t red_left = __ballot(redp);
+    const uint64_t red_blocked = __ballot(blk);
     // GEMM units left per (order position, group), 8 positions per batch of
     // 64 lanes; each batch is looked at as it is read (no arrays indexed at
     // run time: the compiler would keep them in registers across the whole
@@ -467,7 +475,7 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
       }
       continue;   // lost the race for the last unit: look again
     }
-    if (has_work == 0 && red_left == 0) { r.c = -1; return r; }   // every unit claimed
+    if (has_work == 0 && red_left == 0 && red_blocked == 0) { r.c = -1; return r; }   // every unit claimed
     // Work is left only in chunks that have not landed (or, in STRICT mode,
     // behind one), and only a landing can change that: other workgroups'
     // claims only remove work.  So until the landed set changes, only the
@@ -487,12 +495,14 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
         return r;
       }
       __builtin_amdgcn_s_sleep(4);
-      bool now_ok = false;
+      bool now_ok = false, now_blk = false;
       if (lane < R) {
         const int c = a.order[lane];
         now_ok = a.arrived == nullptr || c == a.local || epoch_reached(load_relaxed(a.arrived + c), a.epoch);
+        if (((red_blocked >> lane) & 1) && a.inc_arrived != nullptr)
+          now_blk = !epoch_reached(load_relaxed(a.inc_arrived + c), a.epoch);
       }
-      if (__ballot(now_ok) != landed) break;
+      if (__ballot(now_ok) != landed || __ballot(now_blk) != red_blocked) break;
     }
   }
 }
@@ -566,30 +576,39 @@ __device__ __forceinline__ void reduce_unit(const GemmArgs &a, int c, int tile, 
   }
 }
 
-// Shard unit (fo_gemm_rs_reduce): row slice `slice` of tile `tile` of the
-// local chunk, whose partial is in memory (written through by its unit).
-// Sums the local partial and the incoming partials in summation order (fp32,
-// left to right: the order fo_chunk_reduce uses, so the bits match the
-// unfused pair) and stores the shard rows (fp32, or bf16 rounded to nearest
-// even).  Each wave keeps its running sums in registers and adds, whenever it
-// finds some, the longest run of pending sources whose flags show the epoch:
-// only the sources that land last are left to read after the last landing,
-// and all of them are read together when they are already there.  The
-// partial and the incoming partials are read with system-coherent loads: a
-// copy engine or another XCD wrote them during the launch.  Returns false
-// after a timeout (status set, the launch aborted).  No barrier: the waves of
-// the workgroup run through it independently.
+// Shard unit (fo_gemm_rs_reduce, fo_gemm_rs_ring): row slice `slice` of a
+// tile of chunk c, whose partial is in memory (written through by its unit).
+// Sums the partial and the incoming partials in summation order (fp32, left
+// to right) and stores the result:
+//  - direct form (c = local): the incoming partials are inc[0 .. ninc-1]
+//    (priority order without local: the order fo_chunk_reduce uses, so the
+//    bits match the unfused pair); the sum goes to the shard (fp32, or bf16
+//    rounded to nearest even);
+//  - ring form: the one incoming partial is inc[c] (none if null), the
+//    accumulated partial from the predecessor; the sum goes to the shard for
+//    the local chunk and back over the partial rows (written through, to be
+//    forwarded) for the others.
+// Each wave keeps its running sums in registers and adds, whenever it finds
+// some, the longest run of pending sources whose flags show the epoch: only
+// the sources that land last are left to read after the last landing, and
+// all of them are read together when they are already there.  The partial and
+// the incoming partials are read with system-coherent loads: a copy engine or
+// another XCD wrote them during the launch.  Returns false after a timeout
+// (status set, the launch aborted).  No barrier: the waves of the workgroup
+// run through it independently.
 template <int BM, int BN, int NTT>
-__device__ __forceinline__ bool shard_unit(const GemmArgs &a, int slice, int64_t row0, int64_t rowlim,
+__device__ __forceinline__ bool shard_unit(const GemmArgs &a, int c, int slice, int64_t row0, int64_t rowlim,
                                            int64_t col0) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));   // computed per unit, not kept live across the loop
   const int lane = tid & 63;
   const int64_t N = a.n;
   const int bytes = (int)((int64_t)a.mc * N * 4);              // one chunk of fp32 rows (< 2 GiB)
-  const int64_t lrow0 = row0 - (int64_t)a.local * a.mc;        // first row inside the local chunk
-  const __amdgpu_buffer_rsrc_t rp =
-      uniform_rsrc(reinterpret_cast<const float *>(a.y) + (int64_t)a.local * a.mc * N, bytes);
+  const int64_t lrow0 = row0 - (int64_t)c * a.mc;              // first row inside the chunk
+  float *const prow = reinterpret_cast<float *>(a.y) + (int64_t)c * a.mc * N;
+  const __amdgpu_buffer_rsrc_t rp = uniform_rsrc(prow, bytes);
+  const bool ring = a.ring != 0;
+  const int ninc = ring ? (a.inc[c] != nullptr ? 1 : 0) : a.ninc;
   constexpr int ROWS = BM / RED_SLICES;
   constexpr int PPR = BN / 4;                       // 16-byte pieces per row
   constexpr int PER = (ROWS * PPR + NTT - 1) / NTT; // pieces per thread
@@ -610,12 +629,13 @@ __device__ __forceinline__ bool shard_unit(const GemmArgs &a, int slice, int64_t
   }
   const uint64_t t0 = now_ticks();
   int s = 0;
-  while (s < a.ninc) {
+  while (s < ninc) {
     // sources s .. e-1 have landed (lane i looks at source i's flag)
-    int e = a.ninc;
+    int e = ninc;
     if (a.inc_arrived) {
       bool landed = true;
-      if (lane < a.ninc) landed = epoch_reached(load_relaxed(a.inc_arrived + a.inc_chunk[lane]), a.epoch);
+      if (lane < ninc)
+        landed = epoch_reached(load_relaxed(a.inc_arrived + (ring ? c : a.inc_chunk[lane])), a.epoch);
       const uint64_t pending = ~__ballot(landed) >> s;
       if (pending) e = s + __builtin_ctzll(pending);
       if (e == s) {
@@ -642,7 +662,7 @@ __device__ __forceinline__ bool shard_unit(const GemmArgs &a, int slice, int64_t
 #pragma unroll
         for (int q = 0; q < PER; ++q) t[k][q] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (s + k < e) {
-          const __amdgpu_buffer_rsrc_t ri = uniform_rsrc(a.inc[s + k], bytes);
+          const __amdgpu_buffer_rsrc_t ri = uniform_rsrc(ring ? a.inc[c] : a.inc[s + k], bytes);
 #pragma unroll
           for (int q = 0; q < PER; ++q)
             if (ok[q]) t[k][q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ri, off[q], 0, 1 | 2 | 16));
@@ -658,11 +678,14 @@ __device__ __forceinline__ bool shard_unit(const GemmArgs &a, int slice, int64_t
     }
     s = e;
   }
+  const bool to_shard = !ring || c == a.local;
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
     if (!ok[q]) continue;
     const int64_t idx = off[q] / 4;
-    if (a.shard_bf16) {
+    if (!to_shard) {
+      store_wt16(prow + idx, v[q]);
+    } else if (a.shard_bf16) {
       const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[q][0]) | ((uint32_t)f32_to_bf16_rne(v[q][1]) << 16);
       const uint32_t hi = (uint32_t)f32_to_bf16_rne(v[q][2]) | ((uint32_t)f32_to_bf16_rne(v[q][3]) << 16);
       *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.shard) + idx) = u32x2{lo, hi};
@@ -762,8 +785,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
     const int KT = (int)((k1 - k0 + BK - 1) / BK);
 
     if (un.red) {
-      if (a.fused && c == a.local)
-        shard_unit<BM, BN, NTT>(a, un.sp, row0, rowlim, col0);
+      if (a.fused)   // no split chunks: every reduce unit is a shard unit
+        shard_unit<BM, BN, NTT>(a, c, un.sp, row0, rowlim, col0);
       else
         reduce_unit<BM, BN, NTT>(a, c, tile, un.sp, row0, rowlim, col0);
     } else {
@@ -1011,8 +1034,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
           put4(dbase, ld, row, col, clim, bf, vec_ok, wt, val);
         }
       }
-      if (a.fused && to_out && c == a.local) {
-        // fused: publish the local tile for the shard units once its
+      if (a.fused && to_out && a.red_units[c] > 0) {
+        // fused: publish the tile for its shard units once its
         // written-through stores are acknowledged
         wait_stores();
         __syncthreads();

@@ -49,7 +49,10 @@ struct GemmArgs {
   int32_t one_unit;           // flags: a workgroup whose first claim succeeds leaves after it
   // Fused reduce of the local chunk (fo_gemm_rs_reduce): the local chunk's
   // reduce units sum its partial and the incoming partials into the shard.
-  int32_t fused;                      // 1: red_units[local] are shard units
+  int32_t fused;                      // 1: red_units[c] > 0 are shard units
+  int32_t ring;                       // 1: ring form: chunk c's shard units add inc[c] (indexed by
+                                      //    chunk, flag inc_arrived[c]) and write in place, the local
+                                      //    chunk's to the shard; claimed only once inc[c] landed
   int32_t fused_static;               // 1: shard units assigned statically (b, b + grid, ...)
   int32_t shard_bf16;
   int32_t ninc;                       // incoming partials, in summation order

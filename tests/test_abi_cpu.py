@@ -167,6 +167,34 @@ def test_gemm_rs_reduce_validation(L):
     assert fz(inc=over) == fo.FO_ERR_ALIAS
 
 
+def test_gemm_rs_ring_validation(L):
+    R, m, n, k = 4, 256, 512, 512
+    mc = m // R
+    inc_ok = [A2 + 0x1000000 * (q + 1) for q in range(R)]
+    shard = A2 + 0x8000000
+
+    def rg(sh=shard, dt=fo.FO_F32, inc=inc_ok, nn=n, wsb=1 << 30):
+        s, keep = sched()
+        arr = None if inc is None else (ctypes.c_void_p * R)(*inc)
+        return L.fo_gemm_rs_ring(A, A + 0x100000, A2, None, sh, dt, arr, m, nn, k,
+                                 ctypes.byref(s), WS, wsb, None)
+    assert rg(sh=None) == fo.FO_ERR_NULL
+    assert rg(inc=None) == fo.FO_ERR_NULL
+    assert rg(dt=9) == fo.FO_ERR_DTYPE
+    # any entry may be null (no incoming partial): the call gets as far as the workspace
+    assert rg(inc=[None] * R, wsb=16) == fo.FO_ERR_WORKSPACE
+    assert rg(inc=[inc_ok[0], None, None, inc_ok[3]], wsb=16) == fo.FO_ERR_WORKSPACE
+    assert rg(nn=510) == fo.FO_ERR_ALIGN
+    mis = list(inc_ok)
+    mis[0] += 4                                        # the local chunk's entry is used too
+    assert rg(inc=mis) == fo.FO_ERR_ALIGN
+    over = list(inc_ok)
+    over[0] = A2 + 4096                                # incoming inside the partials
+    assert rg(inc=over) == fo.FO_ERR_ALIAS
+    over[0] = shard + mc * n * 4 - 16                  # incoming overlapping the shard
+    assert rg(inc=over) == fo.FO_ERR_ALIAS
+
+
 def test_chunk_reduce_validation(L):
     R = 4
     n = 1024

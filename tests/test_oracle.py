@@ -234,6 +234,46 @@ def test_ring_rs_equals_collective(orc, mode):
         assert done[r][-1] == r       # the local chunk is computed last
 
 
+@pytest.mark.parametrize("mode", ["int", "gauss"])
+def test_ring_rs_rank_composes_to_collective(orc, mode):
+    """ring_rs_rank run on every rank, each rank's incoming partial of chunk
+    c being its predecessor's forwarded sum (none where the chunk starts, at
+    rank c+1), gives every rank the collective's shard: exactly on integers,
+    and equal to the message-passing simulation in ring.py bit for bit."""
+    R, m, n = 4, 16, 10
+    ks = [6, 9, 5, 12]
+    xs = [wl.bf16_operand((m, ks[r]), mode, 1.0, 820 + r) for r in range(R)]
+    ws = [wl.bf16_operand((n, ks[r]), mode, 0.5, 830 + r) for r in range(R)]
+    mc = m // R
+    fwd = [None] * R
+    shards = [None] * R
+    for _ in range(R):          # R rounds settle every chain of R - 1 hops
+        new = []
+        for r in range(R):
+            prev = (r - 1) % R
+            inc = [None if (c == prev or fwd[prev] is None) else fwd[prev][c * mc:(c + 1) * mc]
+                   for c in range(R)]
+            f, sh = orc.ring_rs_rank(xs[r], ws[r], R, r, inc)
+            new.append(f)
+            shards[r] = sh
+        fwd = new
+    ref, _ = ring.ring_rs(xs, ws)
+    for r in range(R):
+        assert np.array_equal(shards[r], ref[r])
+        if mode == "int":
+            exact = [[sum((brute.gemm(xs[q][r * mc:(r + 1) * mc], ws[q])[i][j] for q in range(R)), 0)
+                      for j in range(n)] for i in range(mc)]
+            assert np.array_equal(shards[r], brute.to_float(exact))
+
+
+def test_ring_rs_rank_single_rank(orc):
+    """One chunk, no incoming partial: the shard is the product itself."""
+    x = wl.bf16_operand((8, 16), "int", 1.0, 840)
+    w = wl.bf16_operand((6, 16), "int", 1.0, 841)
+    f, sh = orc.ring_rs_rank(x, w, 1, 0, [None])
+    assert np.array_equal(sh, orc.gemm(x, w)) and np.array_equal(f, sh)
+
+
 def test_golden_worked_example(orc):
     """Hand-worked 4x2 example (tests/golden/worked_example.txt)."""
     vals = {}
