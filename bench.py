@@ -290,6 +290,10 @@ def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LI
     the time from the last landing to the bf16 shard written.
       flashoverlap: GEMM-RS, then a reduce that adds partials as they land;
       fused: one fo_gemm_rs_reduce launch whose shard units wait for them;
+      ring: the ring form (fo_gemm_rs_ring): the accumulated partials of
+        chunks local-2, local-3, ..., local land one per step and each is
+        added to this rank's partial of its chunk (in place, to forward; the
+        local chunk's sum is the shard);
       naive: wait for every partial, then GEMM-RS and the reduce."""
     import torch
     xb, wb = wl.gemm_inputs(cfg, "gauss")
@@ -302,6 +306,13 @@ def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LI
     inbox = [None if a is None else (torch.empty_like(a) if copy else a.clone()) for a in staging]
     shard = torch.empty((mc, cfg.n), dtype=torch.bfloat16, device="cuda")
     order = wl.ring_arrival_order(cfg.R, cfg.local)
+    if schedule == "ring":
+        # chunk local-1 starts here (nothing incoming); the local chunk's
+        # accumulated partial lands last
+        start = (cfg.local - 1) % cfg.R
+        order = [(cfg.local - 2 - s_) % cfg.R for s_ in range(cfg.R - 1)]
+        staging[cfg.local], staging[start] = staging[start], None
+        inbox[cfg.local], inbox[start] = inbox[start], None
     nbytes = mc * cfg.n * 4
     flags = torch.zeros(cfg.R, dtype=torch.int32, device="cuda")
     es = torch.zeros(cfg.R + 2, dtype=torch.int64, device="cuda")
@@ -331,6 +342,10 @@ def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LI
             fo.fo_gemm_rs_reduce(x, w, part, done, shard, inbox,
                                  fo.Schedule(nchunks=cfg.R, epoch=e, arrived=flags, stamps=gs,
                                              timeout_ns=5_000_000_000), ws)
+        elif schedule == "ring":
+            fo.fo_gemm_rs_ring(x, w, part, done, shard, inbox,
+                               fo.Schedule(nchunks=cfg.R, epoch=e, arrived=flags, stamps=gs,
+                                           timeout_ns=5_000_000_000), ws)
         else:
             fo.fo_gemm_rs(x, w, part, done, fo.Schedule(nchunks=cfg.R, epoch=e, stamps=gs), ws)
             srcs = [part[cfg.local * mc:(cfg.local + 1) * mc] if q == cfg.local else inbox[q]
@@ -343,7 +358,7 @@ def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LI
         last_arrival = max(e_st[1 + q] for q in order)
         g0 = int(gs[2 * cfg.R].item())
         t_start = e_st[0] if schedule == "naive" else min(e_st[0], g0)
-        t_done = int(gs[2 * cfg.R + 1].item()) if schedule == "fused" else int(rs_st[1].item())
+        t_done = int(gs[2 * cfg.R + 1].item()) if schedule in ("fused", "ring") else int(rs_st[1].item())
         if rep > 0:
             tails.append(ticks_to_us(t_done - last_arrival, hz))
             spans.append(ticks_to_us(last_arrival - t_start, hz))
@@ -383,7 +398,7 @@ def link_sweep(fo, hz, bws=(50e9, 153e9, 400e9, 1000e9)):
             row[f"cfg2_{sched}_total_us"] = round(t + sp, 2)
             row[f"cfg2_{sched}_tail_us"] = round(t, 2)
         row["cfg2_last_arrival_us"] = round(sp, 2)
-        for sched in ("flashoverlap", "fused", "naive"):
+        for sched in ("flashoverlap", "fused", "ring", "naive"):
             t, sp = measure_tail_rs(fo, c3, hz, sched, link_bw=bw, copy=False, span=True)
             row[f"cfg3_{sched}_total_us"] = round(t + sp, 2)
             row[f"cfg3_{sched}_tail_us"] = round(t, 2)
@@ -664,7 +679,7 @@ def main():
             tails[key] = row
             log(f"tail {key}: {row}")
         row = {}
-        for s_ in ("flashoverlap", "fused", "naive"):
+        for s_ in ("flashoverlap", "fused", "ring", "naive"):
             sp = {}
             row[s_ + "_us"] = round(measure_tail_rs(fo, c3, hz, s_, spread=sp), 2)
             row[s_ + "_p10_p90_us"] = [sp["p10"], sp["p90"]]

@@ -299,6 +299,9 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
       ctr_used += (size_t)p.tiles;
       total_units += a.red_units[c];
     }
+    a.nshard = 0;
+    for (int i = 0; i < R; ++i)
+      if (a.red_units[a.order[i]] > 0) a.shard_seq[a.nshard++] = a.order[i];
     if (fz->ring) {
       for (int c = 0; c < R; ++c) a.inc[c] = fz->incoming[c];
     } else {
@@ -353,14 +356,17 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
   }
   if (fz) {
     // shard units are assigned statically (workgroup b takes b, b + grid,
-    // ...) only when every workgroup's static first claim is a GEMM unit, so
-    // no dynamic claim of a shard unit can happen
+    // ... of each chunk with shard units, in priority order) only when every
+    // workgroup's static first claim is a GEMM unit, so no dynamic claim of a
+    // shard unit can happen.  Dynamic claims of a ring chunk's units wait for
+    // its landing; hundreds of workgroups claiming at each landing would queue
+    // on the counters.
     bool exact = true;
     for (int g = 0; g < XCDS; ++g) {
       const int64_t wgs_g = (a.grid - g + XCDS - 1) / XCDS;
       exact = exact && (int64_t)a.gunits[g] == wgs_g;
     }
-    a.fused_static = (exact && !fz->ring) ? 1 : 0;
+    a.fused_static = exact ? 1 : 0;
   }
 
   hipError_t e = launch_gemm(a, p.tile, static_cast<hipStream_t>(stream));

@@ -262,13 +262,20 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
   // (static_rr == 2) the first unit comes from the static first claim below
   // and the next claim ends the workgroup.
   // Fused shard units with one GEMM unit per workgroup: after its static
-  // first unit, workgroup b takes shard units b, b + grid, ... of the local
-  // chunk (no claim counter).
+  // first unit, workgroup b takes shard units b, b + grid, ... of each chunk
+  // that has them, in priority order (no claim counter; a unit waits for its
+  // chunk's incoming partials itself).
   if (a.fused_static && rank_hint < 0) {
-    const uint32_t v = blockIdx.x + (uint32_t)st.taken * (uint32_t)a.grid;
-    ++st.taken;
-    if (v >= (uint32_t)a.red_units[a.local]) return r;
-    take_reduce_unit(a, a.local, v, r);
+    // the t-th shard unit of this workgroup: units b, b + grid, ... of each
+    // chunk with shard units (every such chunk has the same number), chunks
+    // in priority order (the landing order)
+    const int t = st.taken++;
+    const int b = (int)blockIdx.x;
+    const int U = a.red_units[a.shard_seq[0]];
+    const int nu = U > b ? (U - b + a.grid - 1) / a.grid : 0;
+    if (nu == 0 || t >= nu * a.nshard) return r;
+    const int i = t / nu;
+    take_reduce_unit(a, a.shard_seq[i], (uint32_t)(b + (t - i * nu) * a.grid), r);
     return r;
   }
   if (a.static_rr == 2 && rank_hint < 0) return r;   // one unit per workgroup: done

@@ -54,6 +54,8 @@ struct GemmArgs {
                                       //    chunk, flag inc_arrived[c]) and write in place, the local
                                       //    chunk's to the shard; claimed only once inc[c] landed
   int32_t fused_static;               // 1: shard units assigned statically (b, b + grid, ...)
+  int32_t nshard;                     // chunks with shard units
+  int32_t shard_seq[FO_MAX_CHUNKS];   // those chunks in priority order
   int32_t shard_bf16;
   int32_t ninc;                       // incoming partials, in summation order
   void *shard;                        // [mc][n]
