@@ -260,12 +260,16 @@ def test_ring_cfg3_bitwise_against_unfused_add(fo, orc):
     check_tolerance(shard[rows], ref[rows], what="cfg3 ring shard")
 
 
-def test_ring_with_emulated_arrivals(fo, orc):
+@pytest.mark.parametrize("grid", [0, 100])
+def test_ring_with_emulated_arrivals(fo, orc, grid):
     """The accumulated partials land by SDMA into NaN-poisoned inboxes at ring
     times (chunk local-2 first, the local chunk last) while the launch runs:
     each chunk's sum starts only after its landing (chunk completion stamps
-    after landing stamps), and the results are exact on integers."""
+    after landing stamps), and the results are exact on integers.  grid 0:
+    one GEMM unit per workgroup, shard units assigned statically; grid 100:
+    dynamic claims, a chunk's shard units claimable once it has landed."""
     m, n, k, R, local = 1024, 448, 512, 8, 3
+    log(f"case: ring with emulated arrivals, grid {grid}")
     xb = wl.bf16_operand((m, k), "int", 1.0, 4700)
     wb = wl.bf16_operand((n, k), "int", 1.0, 4701)
     inc = ring_incoming(m, n, R, local, "int", 4710)
@@ -300,7 +304,7 @@ def test_ring_with_emulated_arrivals(fo, orc):
                                    flags, e, es, stream=side, gate=gs[2 * R:2 * R + 1])
         fo.fo_gemm_rs_ring(x, w, part, done, shard, inbox,
                            fo.Schedule(nchunks=R, local=local, epoch=e, arrived=flags, stamps=gs,
-                                       status=status, timeout_ns=5_000_000_000), ws)
+                                       status=status, timeout_ns=5_000_000_000, max_workgroups=grid), ws)
         torch.cuda.synchronize()
         assert int(status.item()) == 0, "flag wait timed out"
         assert (host(done) == e).all()
