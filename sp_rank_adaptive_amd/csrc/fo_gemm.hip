@@ -752,7 +752,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
   const int wm = cwave / WGN, wn = cwave % WGN;
   const int cg = __builtin_amdgcn_readfirstlane(wave >> 2);             // copy group
   const int cw = wave & 3;                                               // wave in its copy group
-  const int gtid = tid & (NT - 1);                                       // thread in its copy group
   const int64_t K = a.k, N = a.n;
   const int xg = (int)(blockIdx.x % XCDS);
 
