@@ -192,8 +192,8 @@ fo_status fo_gemm_rs_reduce(const void *x, const void *w, float *partial, uint32
  *               (incoming[local] NULL: shard = partial rows of local).
  * done[c] = epoch is released once chunk c's rows (or the shard) are final.
  * With s->arrived, chunk c's sum starts only after arrived[c] shows the epoch
- * (system-coherent loads of incoming[c]); its workgroups take other work
- * meanwhile.  In a ring of R ranks the predecessor's message for chunk c
+ * (system-coherent loads of incoming[c]); no workgroup waits on a landing
+ * while GEMM work is left.  In a ring of R ranks the predecessor's message for chunk c
  * holds the partials of ranks c+1 .. local-1; the chunk with no incoming
  * partial (local-1, whose accumulation this rank starts) is sent as computed.
  *   shard, shard_dtype: as fo_gemm_rs_reduce.
