@@ -564,8 +564,8 @@ def main():
                     help="also run a plain 512 MiB copy (for scaling profiled byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU's share of the path; runs on more than one GPU are "
-              "not part of this build (the multi-GPU design is documented, not launched).",
+        print("bench.py measures one GPU's share of the path and runs on one GPU only; the "
+              "library has no multi-GPU transport (its sharding is a design, not code).",
               file=sys.stderr)
         sys.exit(2)
 
