@@ -106,7 +106,8 @@ typedef struct fo_schedule {
                                   (1..8).  NULL = auto: 1 everywhere when
                                   arrived == NULL, otherwise the last peer in
                                   `order` (the chunk expected to land last) is
-                                  split so its tiles fill the GPU.             */
+                                  split so its tiles fill the GPU, keeping at
+                                  least 1024 of k per split.                   */
   int32_t         max_workgroups; /* 0 = auto.  fo_chunk_reduce may exceed it
                                      so no workgroup owns more than 1 GiB.     */
   int32_t         reserved;

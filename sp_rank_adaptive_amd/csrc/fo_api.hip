@@ -17,6 +17,7 @@ namespace {
 constexpr int kMaxDevices = 64;
 constexpr uint64_t kDefaultTimeoutNs = 10ull * 1000 * 1000 * 1000;
 constexpr int kMaxSplit = 8;
+constexpr int kMinSplitStages = 16;   // automatic split: k stages per split, at least
 
 struct DevInfo {
   int cus = 0;
@@ -248,9 +249,15 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
     int tail = -1;
     for (int i = R - 1; i >= 0; --i)
       if (a.order[i] != s->local) { tail = a.order[i]; break; }
+    // Split so its tiles fill the GPU, but keep at least kMinSplitStages
+    // 64-wide k stages per split: a shorter split spends as much on writing
+    // and reducing its partial tile as on its k-loop.  (On the TP=8 MLP share,
+    // k = 4096, split 4 was the best measured at every link bandwidth from 50
+    // to 400 GB/s and split 8 up to 9% slower; on the QKV share, k = 8192,
+    // split 8 was the best at 50 GB/s.)
     int sk = (grid_cap + p.tiles - 1) / p.tiles;
     if (sk > kMaxSplit) sk = kMaxSplit;
-    if (sk > p.kt_total) sk = p.kt_total;
+    if (sk > p.kt_total / kMinSplitStages) sk = p.kt_total / kMinSplitStages;
     if (sk < 1) sk = 1;
     if (tail >= 0) split[tail] = sk;
   }
