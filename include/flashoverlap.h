@@ -54,7 +54,8 @@ typedef int32_t fo_status;
 enum {
   FO_OK = 0,
   FO_ERR_NULL = 1,       /* a required pointer is NULL                        */
-  FO_ERR_SHAPE = 2,      /* non-positive size, m % R != 0, R out of range     */
+  FO_ERR_SHAPE = 2,      /* non-positive size, m % R != 0, R out of range,
+                            k > 2^21 (GEMM calls)                             */
   FO_ERR_ALIGN = 3,      /* pointer not 16-byte aligned, or k % 8 != 0        */
   FO_ERR_DTYPE = 4,      /* unknown dtype, or a dtype the call cannot store   */
   FO_ERR_ORDER = 5,      /* order is not a permutation of 0..R-1              */
@@ -108,8 +109,12 @@ typedef struct fo_schedule {
                                   `order` (the chunk expected to land last) is
                                   split so its tiles fill the GPU, keeping at
                                   least 1024 of k per split.                   */
-  int32_t         max_workgroups; /* 0 = auto.  fo_chunk_reduce may exceed it
-                                     so no workgroup owns more than 1 GiB.     */
+  int32_t         max_workgroups; /* 0 = auto.  GEMM calls cap it at one
+                                     workgroup per CU (the persistent grid
+                                     must be resident at once; larger values
+                                     act as the cap).  fo_chunk_reduce may
+                                     exceed it so no workgroup owns more than
+                                     1 GiB.                                    */
   int32_t         reserved;
 } fo_schedule;
 
@@ -131,8 +136,9 @@ size_t fo_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t nchunks);
  *   ws device workspace of ws_bytes >= fo_workspace_bytes(m, n, k, R).
  * Each output tile is computed from bf16 MFMA products with fp32 accumulation
  * in a fixed k order, so a given shape, split vector and input give the same
- * bits on every run.  Errors: NULL, SHAPE, ALIGN, DTYPE, ORDER, SCHEDULE,
- * WORKSPACE, ALIAS (y overlapping x or w), HIP. */
+ * bits on every run.  Sizes: 1 <= k <= 2^21 with k % 8 == 0; m/R and n at
+ * most 2^30.  Errors: NULL, SHAPE, ALIGN, DTYPE, ORDER, SCHEDULE, WORKSPACE,
+ * ALIAS (y overlapping x or w), HIP. */
 fo_status fo_ag_gemm(const void *x, const void *w, void *y, fo_dtype y_dtype,
                      int64_t m, int64_t n, int64_t k,
                      const fo_schedule *s, void *ws, size_t ws_bytes,
@@ -143,7 +149,10 @@ fo_status fo_ag_gemm(const void *x, const void *w, void *y, fo_dtype y_dtype,
  *   partial  device fp32 [m][n]: partial[rows of c] = x[rows of c] * W.
  *   done     device [R] epoch flags, optional: done[c] = epoch is stored with
  *            release semantics once chunk c is complete, so a copy engine or
- *            a peer may send it on.
+ *            a peer may send it on.  Every row of chunk c (and, in the fused
+ *            calls below, of the shard) is written through to memory before
+ *            its flag, so a consumer polling done[c] on another stream or
+ *            engine reads final data.
  * Default order: peers in send order local-1, ..., local+1, then the local
  * chunk last.  s->arrived must be NULL (the input rows are local).
  * Errors as fo_ag_gemm. */
@@ -231,8 +240,13 @@ fo_status fo_chunk_reduce(void *dst, fo_dtype dst_dtype, const float *const *src
  * order; a consumer acquires before reading the chunk).  stamps[0] receives
  * t0.
  *   dst, src, bytes, issue_ns, release_ns, chunk_id: host arrays [count];
- *   issue_ns may be NULL (each copy is issued at its release time).
- *   arrived: device [R]; stamps: device [1 + max chunk id + 1], optional. */
+ *   issue_ns may be NULL (each copy is issued at its release time); a zero
+ *   bytes[i] releases only the flag (the data are already in place).
+ *   arrived: device [R].
+ *   stamps: device [2 + max chunk id], required: stamps[0] is the timeline's
+ *   start, which every flag kernel of the call reads (NULL: FO_ERR_NULL).
+ * Errors: NULL, SHAPE (count < 0), SCHEDULE (epoch 0, chunk id out of range,
+ * negative or inverted times), HIP. */
 fo_status fo_emulate_arrivals(void *const *dst, const void *const *src,
                               const size_t *bytes, const int64_t *issue_ns,
                               const int64_t *release_ns, const int32_t *chunk_id,

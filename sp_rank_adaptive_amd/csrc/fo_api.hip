@@ -18,6 +18,10 @@ constexpr int kMaxDevices = 64;
 constexpr uint64_t kDefaultTimeoutNs = 10ull * 1000 * 1000 * 1000;
 constexpr int kMaxSplit = 8;
 constexpr int kMinSplitStages = 16;   // automatic split: k stages per split, at least
+// Largest k: a tile's operand rows (at most 256 of them) are addressed with
+// 32-bit byte offsets, and an offset of 2^30 past a row block must lie beyond
+// it (it stands for "k past the end", which reads as zero).
+constexpr int64_t kMaxK = (int64_t)1 << 21;
 
 struct DevInfo {
   int cus = 0;
@@ -111,10 +115,10 @@ struct GemmPlan {
 GemmPlan plan_workspace(int64_t m, int64_t n, int64_t k, int R) {
   GemmPlan p{};
   p.mc = m / R;
-  int bm = 0, bn = 0;
-  max_tile_dims(&bm, &bn);
-  const int64_t most_tiles = ((p.mc + 127) / 128) * ((n + 127) / 128);      // smallest tiles
-  const int64_t padded = ((p.mc + bm - 1) / bm * bm) * ((n + bn - 1) / bn * bn);
+  // every tile shape the launch may pick: the most tiles per chunk (counters
+  // and ready lists) and the largest padded chunk area (split partials)
+  const int64_t most_tiles = max_tiles_per_chunk(p.mc, n);
+  const int64_t padded = max_padded_tile_area(p.mc, n);
   (void)k;
   p.ready_off = (int)(WS_TILE_CTR + R * most_tiles);
   p.counter_bytes = WS_HEADER_BYTES + 2 * (size_t)R * most_tiles * sizeof(uint32_t);
@@ -149,7 +153,7 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
   if (st != FO_OK) return st;
   const int R = s->nchunks;
   if (m <= 0 || n <= 0 || k <= 0 || m % R != 0) return FO_ERR_SHAPE;
-  if (m / R > (int64_t)1 << 30 || n > (int64_t)1 << 30) return FO_ERR_SHAPE;
+  if (m / R > (int64_t)1 << 30 || n > (int64_t)1 << 30 || k > kMaxK) return FO_ERR_SHAPE;
   if (k % 8 != 0 || !aligned16(x) || !aligned16(w)) return FO_ERR_ALIGN;
   if (!aligned16(y) && !y_bf16) return FO_ERR_ALIGN;
   if (rs_mode && s->arrived && !fz) return FO_ERR_SCHEDULE;
@@ -192,8 +196,12 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
   // Workgroups: one per CU.  With arrival flags the tile configuration must
   // leave registers free on every SIMD, so the one-wave timer and flag
   // kernels of a copy engine emulator can run beside the persistent grid.
+  // Every workgroup of the persistent grid must be resident at once (a
+  // workgroup may wait for units that others hold, and the first units are
+  // assigned by workgroup index), and each takes one CU's LDS: the grid is
+  // capped at one workgroup per CU.
   const int full = I->cus;
-  const int grid_cap = s->max_workgroups > 0 ? s->max_workgroups : full;
+  const int grid_cap = (s->max_workgroups > 0 && s->max_workgroups < full) ? s->max_workgroups : full;
   const GemmPlan p = plan_gemm(m, n, k, R, grid_cap, s->arrived != nullptr);
 
   GemmArgs a{};
@@ -401,6 +409,7 @@ extern "C" {
 
 size_t fo_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t nchunks) {
   if (m <= 0 || n <= 0 || k <= 0 || nchunks < 1 || nchunks > FO_MAX_CHUNKS || m % nchunks) return 0;
+  if (m / nchunks > (int64_t)1 << 30 || n > (int64_t)1 << 30 || k > kMaxK) return 0;
   return plan_workspace(m, n, k, nchunks).total_bytes;
 }
 

@@ -97,6 +97,10 @@ __device__ __forceinline__ void store_wt16(void *p, const f32x4 &v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" :: "v"(p), "v"(v) : "memory");
 }
 
+__device__ __forceinline__ void store_wt8(void *p, const u32x2 &v) {
+  asm volatile("global_store_dwordx2 %0, %1, off sc0 sc1" :: "v"(p), "v"(v) : "memory");
+}
+
 __device__ __forceinline__ void wait_stores() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -685,6 +689,10 @@ __device__ __forceinline__ bool shard_unit(const GemmArgs &a, int c, int slice, 
     }
     s = e;
   }
+  // Every store is written through to memory: the unit is counted towards
+  // done[c] once its stores are acknowledged, and a consumer of done[c] (a
+  // copy engine, another stream) reads the rows without any cache
+  // maintenance by this launch.
   const bool to_shard = !ring || c == a.local;
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
@@ -695,9 +703,9 @@ __device__ __forceinline__ bool shard_unit(const GemmArgs &a, int c, int slice, 
     } else if (a.shard_bf16) {
       const uint32_t lo = (uint32_t)f32_to_bf16_rne(v[q][0]) | ((uint32_t)f32_to_bf16_rne(v[q][1]) << 16);
       const uint32_t hi = (uint32_t)f32_to_bf16_rne(v[q][2]) | ((uint32_t)f32_to_bf16_rne(v[q][3]) << 16);
-      *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.shard) + idx) = u32x2{lo, hi};
+      store_wt8(reinterpret_cast<uint16_t *>(a.shard) + idx, u32x2{lo, hi});
     } else {
-      __builtin_nontemporal_store(v[q], reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.shard) + idx));
+      store_wt16(reinterpret_cast<float *>(a.shard) + idx, v[q]);
     }
   }
   return true;
@@ -1190,14 +1198,22 @@ TileCfg choose_tile(int64_t mc, int64_t n, int64_t k, int R, int grid, bool leav
   return TileCfg{pick.bm, pick.bn, pick.stages};
 }
 
-void max_tile_dims(int *bm, int *bn) {
-  int m = 0, n = 0;
+int64_t max_padded_tile_area(int64_t mc, int64_t n) {
+  int64_t best = 0;
   for (const Cand &c : kCands) {
-    if (c.bm > m) m = c.bm;
-    if (c.bn > n) n = c.bn;
+    const int64_t a = (mc + c.bm - 1) / c.bm * c.bm * ((n + c.bn - 1) / c.bn * c.bn);
+    if (a > best) best = a;
   }
-  *bm = m;
-  *bn = n;
+  return best;
+}
+
+int64_t max_tiles_per_chunk(int64_t mc, int64_t n) {
+  int64_t best = 0;
+  for (const Cand &c : kCands) {
+    const int64_t t = ((mc + c.bm - 1) / c.bm) * ((n + c.bn - 1) / c.bn);
+    if (t > best) best = t;
+  }
+  return best;
 }
 
 size_t partial_slot_bytes(const TileCfg &t) { return (size_t)t.bm * t.bn * sizeof(float); }

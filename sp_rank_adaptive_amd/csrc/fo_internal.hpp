@@ -100,8 +100,11 @@ struct ReduceArgs {
 // Tile configuration chosen for a problem (host).
 TileCfg choose_tile(int64_t mc, int64_t n, int64_t k, int R, int grid, bool leave_room);
 size_t partial_slot_bytes(const TileCfg &t);
-// Largest tile area any configuration can use (bounds the partial-tile area).
-void max_tile_dims(int *bm, int *bn);
+// Bounds over every compiled tile configuration, for workspace sizing: the
+// largest padded chunk area (rows and columns rounded up to whole tiles) and
+// the most tiles per chunk.
+int64_t max_padded_tile_area(int64_t mc, int64_t n);
+int64_t max_tiles_per_chunk(int64_t mc, int64_t n);
 
 hipError_t launch_gemm(const GemmArgs &a, const TileCfg &t, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs &a, int grid, hipStream_t stream);

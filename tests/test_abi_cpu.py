@@ -77,6 +77,28 @@ def test_workspace_bytes(L):
     assert fo.fo_workspace_bytes(4096, 1792, 4096, 7) == 0      # m % R != 0
     assert fo.fo_workspace_bytes(0, 1, 8, 1) == 0
     assert fo.fo_workspace_bytes(64, 64, 64, 65) == 0            # R > max
+    assert fo.fo_workspace_bytes(64, 64, 1 << 21, 1) > 0         # largest k
+    assert fo.fo_workspace_bytes(64, 64, (1 << 21) + 8, 1) == 0  # k too large
+
+
+# The tile shapes the GEMM launches may pick (BM x BN).
+TILE_SHAPES = [(256, 256), (256, 160), (128, 224), (128, 128)]
+
+
+@pytest.mark.parametrize("R", [8, 16])
+def test_workspace_covers_every_tile_shape(L, R):
+    """fo_workspace_bytes must hold 8 split partials of the padded chunk area
+    for whichever tile shape the launch picks, plus its counters and ready
+    lists, on ragged n (a 224-wide tile pads n further than a 256-wide one)."""
+    for mc in (256, 512, 1000, 1024):
+        for n in range(2272, 2945, 32):
+            ws = fo.fo_workspace_bytes(mc * R, n, 8192, R)
+            for bm, bn in TILE_SHAPES:
+                tiles = -(-mc // bm) * -(-n // bn)
+                counters = 4096 + 2 * R * tiles * 4
+                start = (counters + 255) // 256 * 256
+                need = start + 8 * tiles * bm * bn * 4
+                assert ws >= need, (mc, n, R, bm, bn, ws, need)
 
 
 def sched(R=4, **kw):
@@ -99,6 +121,7 @@ def test_ag_gemm_validation(L):
     assert ag(L, m=255) == fo.FO_ERR_SHAPE                  # m % R
     assert ag(L, n=0) == fo.FO_ERR_SHAPE
     assert ag(L, k=12) == fo.FO_ERR_ALIGN                   # k % 8
+    assert ag(L, k=(1 << 21) + 8) == fo.FO_ERR_SHAPE        # 32-bit row-block offsets
     assert ag(L, x=A + 8) == fo.FO_ERR_ALIGN
     assert ag(L, y=A) == fo.FO_ERR_ALIAS                    # y overlaps x
     assert ag(L, ws=None) == fo.FO_ERR_WORKSPACE

@@ -291,3 +291,61 @@ def test_gemm_rs_parity_done_flags_and_order(fo, orc):
     check_tolerance(host(part)[rows], ref, what="rs gauss, 64 workgroups")
     first = host(stamps).astype(np.int64)[:cfg.R]
     assert first[0] >= first[2:].max()
+
+
+def test_workspace_size_covers_padded_tiles(fo, orc):
+    """m = 2048, R = 8, n = 2560, k = 8192 with arrival flags: the automatic
+    split (8 ways, 128 x 224 tiles, n padded to 2688) needs more partial area
+    than a 256-wide tile's padding; fo_workspace_bytes must cover it."""
+    m, n, k, R = 2048, 2560, 8192, 8
+    xb = wl.bf16_operand((m, k), "int", 1.0, 14001)
+    wb = wl.bf16_operand((n, k), "int", 1.0, 14002)
+    x, w = dev_bf16(xb), dev_bf16(wb)
+    flags = torch.full((R,), EP.e + 1, dtype=torch.int32, device="cuda")
+    log(f"case: workspace sizing {m}x{n}x{k} R={R}, automatic split")
+    y, ws = run_ag(fo, x, w, R, arrived=flags)
+    assert ws.numel() == fo.fo_workspace_bytes(m, n, k, R)
+    check_exact(host(y), orc.gemm(xb, wb), "padded split tiles")
+
+
+def test_grid_request_above_cus_is_capped(fo, orc):
+    """A max_workgroups request above one per CU acts as the cap: a split
+    chunk without flags (reduce units waiting for split tiles held by other
+    workgroups) still completes, exactly."""
+    cus, _, _ = fo.fo_device_info()
+    m, n, k, R = 1024, 448, 2048, 4
+    xb = wl.bf16_operand((m, k), "int", 1.0, 14101)
+    wb = wl.bf16_operand((n, k), "int", 1.0, 14102)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    log(f"case: max_workgroups {4 * cus} on {cus} CUs, split [8, 8, 1, 2]")
+    ws = torch.zeros(4 * fo.fo_workspace_bytes(m, n, k, R), dtype=torch.uint8, device="cuda")
+    y, _ = run_ag(fo, dev_bf16(xb), dev_bf16(wb), R, ws=ws, split=[8, 8, 1, 2], max_workgroups=4 * cus,
+                  status=status, timeout_ns=2_000_000_000)
+    assert int(status.item()) == 0
+    check_exact(host(y), orc.gemm(xb, wb), "capped grid")
+
+
+@pytest.mark.parametrize("R", [24, 64])
+@pytest.mark.parametrize("grid", [8, 100, 256])
+def test_claim_walk_many_chunks_preset_flags(fo, orc, R, grid):
+    """R = 24 and 64 chunks with arrival flags: the claim walk reads three and
+    eight 64-lane batches of (position, XCD group) counters; a priority order
+    that is a seeded permutation, the automatic split of its last peer, and
+    every element written once and exact."""
+    mc, n, k = 64, 264, 2048
+    m = R * mc
+    xb = wl.bf16_operand((m, k), "int", 1.0, 15000 + R)
+    wb = wl.bf16_operand((n, k), "int", 1.0, 15001)
+    x, w = dev_bf16(xb), dev_bf16(wb)
+    ref = orc.gemm(xb, wb)
+    order = wl.seeded_permutation(list(range(R)), R + grid)
+    local = order[-1]
+    flags = torch.full((R,), EP.e + 1, dtype=torch.int32, device="cuda")
+    log(f"case: R={R} grid={grid} preset flags, order {order[:4]}..., local {local}")
+    y, ws = run_ag(fo, x, w, R, arrived=flags, order=order, local=local, max_workgroups=grid)
+    assert not torch.isnan(y).any()
+    check_exact(host(y), ref, f"R={R} grid={grid}")
+    assert int(ws[:4096].sum()) == 0
+    y, _ = run_ag(fo, x, w, R, ws=ws, arrived=torch.full((R,), EP.e + 1, dtype=torch.int32, device="cuda"),
+                  order=order, local=local, max_workgroups=grid, mode=fo.FO_SCHED_STRICT)
+    check_exact(host(y), ref, f"R={R} grid={grid} strict")
