@@ -294,6 +294,8 @@ def test_tp8_mlp_rs_full_int_partials_and_shards(fo, orc):
     ring_inc = [None if q == start else d_inc[q if q != c.local else start] for q in range(c.R)]
     host_inc = [None if q == start else inc[q if q != c.local else start] for q in range(c.R)]
     fwd, shard = orc.ring_rs_rank(xb, wb, c.R, c.local, host_inc)
+    # the local chunk's partial rows keep its own product; its sum is the shard
+    fwd[c.local * mc:(c.local + 1) * mc] = ref[c.local * mc:(c.local + 1) * mc]
     part.fill_(float("nan"))
     sh.fill_(float("nan"))
     e = epoch()
