@@ -203,3 +203,31 @@ def gemm_rs_shard(x_bits, w_bits, R: int, local: int, incoming) -> np.ndarray:
     if rc:
         raise ValueError("bad shape or local rank")
     return out
+
+
+def a2a_gemm(pieces, w_bits) -> np.ndarray:
+    """Flash All-to-All output projection: Y = [A_0 | A_1 | ... | A_{P-1}] * W.
+
+    The all-to-all of Ulysses parallelism hands each rank, from every rank q,
+    the rows of its own sequence slice for q's group of heads: a column block
+    A_q of the attention output [m, k/P] (bf16).  Decomposed into P2P pieces,
+    the output projection over the gathered heads is still exactly the plain
+    GEMM over the blocks placed side by side along k, which is what this
+    returns (fp64, k ascending).  W is stored [n, k]; block q meets columns
+    [q*k/P, (q+1)*k/P) of it.
+
+    Pages: gist.science technical summary §1 (Ulysses parallelism needs
+    all-to-all) and §2 (Flash All-to-All, the extension of the decomposed
+    primitives to Ulysses parallelism); the abstract (the decomposition is
+    exact).
+    """
+    blocks = [_u16(p) for p in pieces]
+    if not blocks:
+        raise ValueError("no pieces")
+    m = blocks[0].shape[0]
+    if any(b.ndim != 2 or b.shape[0] != m for b in blocks):
+        raise ValueError("pieces must be [m, k/P] with one m")
+    x = np.ascontiguousarray(np.concatenate(blocks, axis=1))
+    if x.shape[1] != _u16(w_bits).shape[1]:
+        raise ValueError("k mismatch")
+    return gemm(x, w_bits)

@@ -292,3 +292,94 @@ def test_golden_worked_example(orc):
     srcs = [vals["SRC0"].astype(np.float32), vals["SRC1"].astype(np.float32),
             vals["SRC2"].astype(np.float32)]
     assert np.array_equal(orc.reduce(srcs), vals["SUM"])
+
+
+# ---- Flash All-to-All (Ulysses output projection) ----------------------------
+
+def a2a_case(m, k, n, P, mode, seed):
+    x = wl.bf16_operand((m, k), mode, 1.0, seed)
+    w = wl.bf16_operand((n, k), mode, 0.02 if mode == "gauss" else 1.0, seed + 1)
+    kp = k // P
+    pieces = [np.ascontiguousarray(x[:, q * kp:(q + 1) * kp]) for q in range(P)]
+    return x, w, pieces
+
+
+@pytest.mark.parametrize("m,k,n,P", [(37, 48, 23, 4), (64, 128, 40, 8), (5, 30, 7, 3)])
+def test_a2a_gemm_vs_numpy_block_sum(orc, m, k, n, P):
+    """Y against numpy fp64 as a sum of per-piece block products (a different
+    formula from the oracle's assembled product): block q of the gathered
+    rows must meet columns block q of W."""
+    x, w, pieces = a2a_case(m, k, n, P, "gauss", 700 + m)
+    kp = k // P
+    wf = orc.bf16_to_f64(w)
+    ref = sum(orc.bf16_to_f64(pieces[q]) @ wf[:, q * kp:(q + 1) * kp].T for q in range(P))
+    scale = np.abs(orc.bf16_to_f64(x)) @ np.abs(wf).T
+    y = orc.a2a_gemm(pieces, w)
+    assert np.all(np.abs(y - ref) <= 1e-12 * scale + 1e-300)
+    xi, wi, pi = a2a_case(m, k, n, P, "int", 800 + m)
+    ri = sum(orc.bf16_to_f64(pi[q]).astype(np.int64) @ orc.bf16_to_f64(wi[:, q * kp:(q + 1) * kp]).astype(np.int64).T
+             for q in range(P))
+    assert np.array_equal(orc.a2a_gemm(pi, wi), ri.astype(np.float64))
+
+
+@pytest.mark.parametrize("mode", ["int", "gauss"])
+def test_a2a_gemm_vs_fraction_bruteforce(orc, mode):
+    for (m, k, n, P), seed in zip([(3, 8, 4, 2), (4, 12, 5, 3), (2, 16, 3, 4)], (1, 2, 3)):
+        x, w, pieces = a2a_case(m, k, n, P, mode, 900 + seed)
+        kp = k // P
+        exact = None
+        for q in range(P):
+            part = brute.gemm(pieces[q], np.ascontiguousarray(w[:, q * kp:(q + 1) * kp]))
+            exact = part if exact is None else [[a + b for a, b in zip(ra, rb)] for ra, rb in zip(exact, part)]
+        ex = brute.to_float(exact)
+        y = orc.a2a_gemm(pieces, w)
+        if mode == "int":
+            assert np.array_equal(y, ex)
+        else:
+            absx = np.abs(orc.bf16_to_f64(x)) @ np.abs(orc.bf16_to_f64(w)).T
+            assert np.all(np.abs(y - ex) <= k * 2.0 ** -53 * absx)
+
+
+def test_a2a_gemm_special_cases(orc):
+    x, w, pieces = a2a_case(9, 16, 6, 1, "gauss", 1001)
+    assert np.array_equal(orc.a2a_gemm(pieces, w), orc.gemm(x, w))        # one rank
+    k, P = 24, 4
+    x, _, pieces = a2a_case(10, k, 1, P, "gauss", 1002)
+    eye = wl.f32_to_bf16_bits(np.eye(k, dtype=np.float32))
+    assert np.array_equal(orc.a2a_gemm(pieces, eye), orc.bf16_to_f64(x))  # W = I
+    # a zero piece contributes nothing: the others' block products alone
+    x, w, pieces = a2a_case(8, k, 5, P, "int", 1003)
+    pieces[2] = np.zeros_like(pieces[2])
+    kp = k // P
+    keep = [q for q in range(P) if q != 2]
+    ref = sum(orc.gemm(pieces[q], np.ascontiguousarray(w[:, q * kp:(q + 1) * kp])) for q in keep)
+    assert np.array_equal(orc.a2a_gemm(pieces, w), ref)
+
+
+@pytest.mark.parametrize("P", [2, 4, 8])
+@pytest.mark.parametrize("mode", ["int", "gauss"])
+def test_ulysses_all_to_all_equals_collective(orc, P, mode):
+    """Every rank's pairwise-exchange all-to-all and piece-by-piece output
+    projection (oracle/ulysses.py) against the undistributed product of the
+    whole attention output with W (numpy); each rank's result also equals the
+    oracle's a2a_gemm over the pieces it received."""
+    from oracle import ulysses
+    S, k, n = 8 * P, 16 * P, 24
+    o = wl.bf16_operand((S, k), mode, 1.0, 1100 + P)
+    w = wl.bf16_operand((n, k), mode, 0.02 if mode == "gauss" else 1.0, 1101 + P)
+    ys, received = ulysses.ulysses_out_proj(o, w, P)
+    of, wf = orc.bf16_to_f64(o), orc.bf16_to_f64(w)
+    full = of @ wf.T
+    sp, kp = S // P, k // P
+    for r in range(P):
+        assert received[r] == [(r - s) % P for s in range(P)]
+        rows = full[r * sp:(r + 1) * sp]
+        pieces = [np.ascontiguousarray(o[r * sp:(r + 1) * sp, q * kp:(q + 1) * kp]) for q in range(P)]
+        if mode == "int":
+            ri = (of.astype(np.int64) @ wf.astype(np.int64).T)[r * sp:(r + 1) * sp]
+            assert np.array_equal(ys[r], ri.astype(np.float64))
+            assert np.array_equal(orc.a2a_gemm(pieces, w), ys[r])
+        else:
+            scale = (np.abs(of) @ np.abs(wf).T)[r * sp:(r + 1) * sp]
+            assert np.all(np.abs(ys[r] - rows) <= 1e-12 * scale + 1e-300)
+            assert np.all(np.abs(orc.a2a_gemm(pieces, w) - rows) <= 1e-12 * scale + 1e-300)

@@ -33,7 +33,7 @@ class GemmCfg:
     """Shape of one chunked GEMM workload (AG mode or RS mode)."""
     cfg: int
     name: str
-    mode: str          # "ag" or "rs"
+    mode: str          # "ag", "rs" or "a2a"
     m: int
     n: int
     k: int
@@ -63,7 +63,14 @@ CFG3 = GemmCfg(3, "tpsp_mlp_down_gemm_rs_tp8", "rs", 4096, 4096, 1792, 8,
 CFG4 = ReduceCfg(4, "dp_grad_reduce_r8", 1 << 27, 8)
 CFG5 = GemmCfg(5, "long_seq_qkv_ag_gemm_tp16", "ag", 16384, 1280, 8192, 16)
 
-CONFIGS = {1: CFG1, 2: CFG2, 3: CFG3, 4: CFG4, 5: CFG5}
+# Ulysses attention output projection, one rank's share at Ulysses degree 8:
+# a 16K-token sequence (the long end of the summary's 1K-16K sweep) with the
+# summary's hidden size 4096 as 32 heads of 128; the all-to-all hands this
+# rank its 2048 rows of every rank's 4 heads (8 pieces of 2048 x 512), and W
+# is the 4096 x 4096 output projection.
+CFG6 = GemmCfg(6, "ulysses_out_proj_a2a_up8", "a2a", 2048, 4096, 4096, 8)
+
+CONFIGS = {1: CFG1, 2: CFG2, 3: CFG3, 4: CFG4, 5: CFG5, 6: CFG6}
 
 # tensor ids used in seeds
 T_X, T_W, T_INC, T_SRC, T_ORDER = 1, 2, 3, 10, 50
@@ -120,6 +127,15 @@ def gemm_inputs(c: GemmCfg, mode: str, m: int | None = None):
     x = bf16_operand((m, c.k), mode, c.x_std, seed_for(c.cfg, T_X))
     w = bf16_operand((c.n, c.k), mode, c.w_std, seed_for(c.cfg, T_W))
     return x, w
+
+
+def a2a_pieces(c: GemmCfg, mode: str, m: int | None = None):
+    """(pieces, w_bits) of an all-to-all workload: the gathered operand
+    [m, k] drawn as one matrix and cut into R column blocks [m, k/R] (piece
+    q = the block that rank q's heads contribute), each contiguous."""
+    x, w = gemm_inputs(c, mode, m=m)
+    kp = c.k // c.R
+    return [np.ascontiguousarray(x[:, q * kp:(q + 1) * kp]) for q in range(c.R)], w
 
 
 def incoming_partials(c: GemmCfg, mode: str, rows: int | None = None):
