@@ -144,6 +144,23 @@ fo_status fo_ag_gemm(const void *x, const void *w, void *y, fo_dtype y_dtype,
                      const fo_schedule *s, void *ws, size_t ws_bytes,
                      void *stream);
 
+/* fo_ag_gemm for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same computation, kernels and bits as fo_ag_gemm with its workspace taken
+ * from a library-held device array instead of a caller buffer:
+ *   - the array is FO_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held from the
+ *     library's load until the process ends; a problem whose
+ *     fo_workspace_bytes exceeds it is refused with FO_ERR_WORKSPACE;
+ *   - every call on a GPU shares that GPU's array: its counters are cleared
+ *     by a kernel at the start of each call (on `stream`), so calls that
+ *     overlap on one GPU race and must be ordered by the caller;
+ *   - nothing is allocated or freed, by this call or anything it calls.
+ * Arguments, errors and results as fo_ag_gemm (without ws, ws_bytes). */
+#define FO_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+fo_status fo_ag_gemm_noalloc(const void *x, const void *w, void *y, fo_dtype y_dtype,
+                             int64_t m, int64_t n, int64_t k,
+                             const fo_schedule *s, void *stream);
+
 /* Chunked GEMM-RS (technical summary §2, Flash-RS).
  *   x        device bf16 [m][k]; w device bf16 [n][k].
  *   partial  device fp32 [m][n]: partial[rows of c] = x[rows of c] * W.

@@ -26,7 +26,9 @@ FO_F32, FO_BF16 = 0, 1
 FO_SCHED_READY_FIRST, FO_SCHED_STRICT = 0, 1
 FO_MAX_CHUNKS = 64
 
-EXPORTS = ("fo_workspace_bytes", "fo_ag_gemm", "fo_gemm_rs", "fo_gemm_rs_reduce", "fo_gemm_rs_ring", "fo_chunk_reduce",
+FO_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+EXPORTS = ("fo_workspace_bytes", "fo_ag_gemm", "fo_ag_gemm_noalloc", "fo_gemm_rs", "fo_gemm_rs_reduce", "fo_gemm_rs_ring", "fo_chunk_reduce",
            "fo_emulate_arrivals", "fo_emulate_arrivals_gated", "fo_plan_ag_schedule", "fo_device_info", "fo_status_string",
            "fo_last_hip_error")
 
@@ -74,6 +76,8 @@ def lib() -> ctypes.CDLL:
     L.fo_workspace_bytes.argtypes = [i64, i64, i64, i32]
     L.fo_ag_gemm.restype = i32
     L.fo_ag_gemm.argtypes = [P, P, P, i32, i64, i64, i64, S, P, sz, P]
+    L.fo_ag_gemm_noalloc.restype = i32
+    L.fo_ag_gemm_noalloc.argtypes = [P, P, P, i32, i64, i64, i64, S, P]
     L.fo_gemm_rs.restype = i32
     L.fo_gemm_rs.argtypes = [P, P, P, P, i64, i64, i64, S, P, sz, P]
     L.fo_gemm_rs_reduce.restype = i32
@@ -213,6 +217,20 @@ def fo_ag_gemm(x, w, y, sched: Schedule, ws, stream=None, *, raise_on_error=True
     del keep
     if raise_on_error:
         _check(st, "fo_ag_gemm")
+    return st
+
+
+def fo_ag_gemm_noalloc(x, w, y, sched: Schedule, stream=None, *, raise_on_error=True) -> int:
+    """fo_ag_gemm with the library's per-GPU scratch array as its workspace
+    (no workspace argument; nothing is allocated)."""
+    m, k = x.shape
+    n = w.shape[0]
+    s, keep = sched._c()
+    st = lib().fo_ag_gemm_noalloc(_ptr(x), _ptr(w), _ptr(y), _dtype_code(y), m, n, k,
+                                  ctypes.byref(s), _stream(stream))
+    del keep
+    if raise_on_error:
+        _check(st, "fo_ag_gemm_noalloc")
     return st
 
 

@@ -145,9 +145,17 @@ struct FusedRs {
   bool ring;                      // ring form: incoming[c] is chunk c's accumulated partial (may be null)
 };
 
+// Zeroes n 32-bit words with vector stores (a kernel rather than a memset, so
+// the clearing can sit inside a captured stream).
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t *p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
 fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t *done,
                    bool rs_mode, int64_t m, int64_t n, int64_t k, const fo_schedule *s,
-                   void *ws, size_t ws_bytes, void *stream, const FusedRs *fz = nullptr) {
+                   void *ws, size_t ws_bytes, void *stream, const FusedRs *fz = nullptr,
+                   bool clear_counters = false) {
   if (!x || !w || !y || !s) return FO_ERR_NULL;
   fo_status st = check_schedule(s);
   if (st != FO_OK) return st;
@@ -384,9 +392,51 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
     a.fused_static = exact ? 1 : 0;
   }
 
+  if (clear_counters) {
+    // the counters (claims, completions, split tiles, ready lists) start at zero
+    const int64_t words = (int64_t)(p.counter_bytes / sizeof(uint32_t));
+    hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<uint32_t *>(ws), words);
+    const hipError_t ez = hipGetLastError();
+    if (ez != hipSuccess) { record(ez); return FO_ERR_HIP; }
+  }
   hipError_t e = launch_gemm(a, p.tile, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) { record(e); return FO_ERR_HIP; }
   return FO_OK;
+}
+
+// Workspace of fo_ag_gemm_noalloc: one array per GPU, held from the library's
+// load until the process ends, shared by every such call on that GPU.  Host
+// code never uses the array's name as an address: the device address comes
+// from hipGetSymbolAddress, once per device (scratch_address).
+constexpr size_t kNoAllocBytes = FO_NOALLOC_SCRATCH_BYTES;
+
+}  // namespace
+}  // namespace fo
+
+static __device__ __align__(256) unsigned char scratch[fo::kNoAllocBytes];
+
+namespace fo {
+namespace {
+
+void *g_scratch[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// Device address of this GPU's scratch array (the current device), looked up
+// on the first call on that device with the device current.
+void *scratch_address() {
+  int d = 0;
+  const hipError_t e = hipGetDevice(&d);
+  if (e != hipSuccess) { record(e); return nullptr; }
+  if (d < 0 || d >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[d], [d]() {
+    void *ptr = nullptr;
+    g_scratch_err[d] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch[d] = g_scratch_err[d] == hipSuccess ? ptr : nullptr;
+  });
+  if (g_scratch_err[d] != hipSuccess) { record(g_scratch_err[d]); return nullptr; }
+  return g_scratch[d];
 }
 
 }  // namespace
@@ -417,6 +467,21 @@ fo_status fo_ag_gemm(const void *x, const void *w, void *y, fo_dtype y_dtype, in
                      int64_t k, const fo_schedule *s, void *ws, size_t ws_bytes, void *stream) {
   if (y_dtype != FO_F32 && y_dtype != FO_BF16) return FO_ERR_DTYPE;
   return run_gemm(x, w, y, y_dtype == FO_BF16, nullptr, false, m, n, k, s, ws, ws_bytes, stream);
+}
+
+fo_status fo_ag_gemm_noalloc(const void *x, const void *w, void *y, fo_dtype y_dtype, int64_t m, int64_t n,
+                             int64_t k, const fo_schedule *s, void *stream) {
+  if (y_dtype != FO_F32 && y_dtype != FO_BF16) return FO_ERR_DTYPE;
+  if (!x || !w || !y || !s) return FO_ERR_NULL;
+  // the problem's workspace bound must fit the scratch array
+  const size_t need = fo_workspace_bytes(m, n, k, s->nchunks);
+  if (need > kNoAllocBytes) return FO_ERR_WORKSPACE;
+  // need == 0 means an invalid shape, which the validation in run_gemm
+  // reports before it looks at the workspace
+  void *ws = need ? scratch_address() : nullptr;
+  if (need && !ws) return FO_ERR_HIP;
+  return run_gemm(x, w, y, y_dtype == FO_BF16, nullptr, false, m, n, k, s, ws, kNoAllocBytes, stream,
+                  nullptr, true);
 }
 
 fo_status fo_gemm_rs(const void *x, const void *w, float *partial, uint32_t *done, int64_t m,

@@ -273,3 +273,19 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fo, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         fo.lib()
+
+
+def test_ag_gemm_noalloc_validation(L):
+    """The allocation-free AG-GEMM validates like fo_ag_gemm and refuses a
+    problem whose workspace bound exceeds its scratch array, before any HIP
+    call."""
+    s, keep = sched()
+    na = L.fo_ag_gemm_noalloc
+    assert na(None, A, A2, fo.FO_F32, 256, 512, 512, ctypes.byref(s), None) == fo.FO_ERR_NULL
+    assert na(A, A, A2, fo.FO_F32, 256, 512, 512, None, None) == fo.FO_ERR_NULL
+    assert na(A, A, A2, 7, 256, 512, 512, ctypes.byref(s), None) == fo.FO_ERR_DTYPE
+    assert na(A, A, A2, fo.FO_F32, 255, 512, 512, ctypes.byref(s), None) == fo.FO_ERR_SHAPE
+    assert na(A, A, A2, fo.FO_F32, 256, 512, (1 << 21) + 8, ctypes.byref(s), None) == fo.FO_ERR_SHAPE
+    s8, keep8 = sched(R=8)
+    assert fo.fo_workspace_bytes(65536, 8192, 4096, 8) > fo.FO_NOALLOC_SCRATCH_BYTES
+    assert na(A, A, A2, fo.FO_F32, 65536, 8192, 4096, ctypes.byref(s8), None) == fo.FO_ERR_WORKSPACE
