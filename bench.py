@@ -368,6 +368,79 @@ def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LI
     return float(np.median(tails))
 
 
+def a2a_rate(fo, cfg, launches=30):
+    """All-landed Flash All-to-All GEMM (flags preset) over launches in a row:
+    (average us per launch, TFLOP/s)."""
+    import torch
+    pieces, wb = wl.a2a_pieces(cfg, "gauss")
+    dp = [dev_bf16(p_) for p_ in pieces]
+    w = dev_bf16(wb)
+    y = torch.empty((cfg.m, cfg.n), device="cuda")
+    ws = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    flags = torch.full((cfg.R,), 1 << 30, dtype=torch.int32, device="cuda")
+    for e in range(3):
+        fo.fo_a2a_gemm(dp, w, y, fo.Schedule(nchunks=cfg.R, epoch=1 + e, arrived=flags), ws)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(torch.cuda.current_stream())
+    for e in range(launches):
+        fo.fo_a2a_gemm(dp, w, y, fo.Schedule(nchunks=cfg.R, epoch=10 + e, arrived=flags), ws)
+    b.record(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / launches
+    return us, 2.0 * cfg.m * cfg.n * cfg.k / us / 1e6
+
+
+def measure_tail_a2a(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LINK_BW, spread=None):
+    """Exposed tail of the Flash All-to-All GEMM: the peers' pieces land by
+    emulated pairwise-exchange arrivals (piece local-s at step s); the tail is
+    the time from the last landing to the last output tile written.
+      flashoverlap: one launch that multiplies each piece once it landed;
+      naive: wait for every piece, then the same launch."""
+    import torch
+    pieces, wb = wl.a2a_pieces(cfg, "gauss")
+    staging = [dev_bf16(p_) for p_ in pieces]
+    inbox = [t.clone() for t in staging]
+    w = dev_bf16(wb)
+    y = torch.empty((cfg.m, cfg.n), device="cuda")
+    P, local = cfg.R, cfg.local
+    order = [(local - s_) % P for s_ in range(1, P)]
+    nbytes = cfg.m * (cfg.k // P) * 2
+    flags = torch.zeros(P, dtype=torch.int32, device="cuda")
+    es = torch.zeros(P + 2, dtype=torch.int64, device="cuda")
+    gs = torch.zeros(2 * P + 2, dtype=torch.int64, device="cuda")
+    ws = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    side = side_stream()
+    main = torch.cuda.current_stream()
+    tails, spans = [], []
+    for rep in range(reps + 1):
+        e = 400 + rep
+        gs.zero_()
+        torch.cuda.synchronize()
+        if schedule == "naive":
+            _emulate(fo, [inbox[q] for q in order], [staging[q] for q in order], order, nbytes, flags, e, es,
+                     side, link_bw)
+            ev = torch.cuda.Event()
+            ev.record(side)
+            main.wait_event(ev)
+            fo.fo_a2a_gemm(inbox, w, y, fo.Schedule(nchunks=P, epoch=e, stamps=gs), ws)
+        else:
+            _emulate(fo, [inbox[q] for q in order], [staging[q] for q in order], order, nbytes, flags, e, es,
+                     side, link_bw, gate=gs[2 * P:2 * P + 1])
+            fo.fo_a2a_gemm(inbox, w, y, fo.Schedule(nchunks=P, epoch=e, arrived=flags, stamps=gs,
+                                                    timeout_ns=5_000_000_000), ws)
+        torch.cuda.synchronize()
+        e_st = es.cpu().numpy().astype(np.int64)
+        g_st = gs.cpu().numpy().astype(np.int64)
+        last = max(e_st[1 + q] for q in order)
+        if rep > 0:
+            tails.append(ticks_to_us(g_st[2 * P + 1] - last, hz))
+            spans.append(ticks_to_us(last - e_st[0], hz))
+    _spread(spread, tails)
+    return float(np.median(tails)), float(np.median(spans))
+
+
 def link_sweep(fo, hz, bws=(50e9, 153e9, 400e9, 1000e9)):
     """End-to-end time (first release to output complete) and exposed tail at
     several per-link bandwidths.  The data are copied in before the timed
@@ -748,6 +821,11 @@ def main():
         for cfg in (wl.CFG5,):
             tf, ms = gemm_rate(fo, cfg)
             out["qkv_ag_gemm_cfg5"] = {"us": round(ms * 1e3, 1), "tflops": round(tf, 1)}
+        us, tf = a2a_rate(fo, wl.CFG6)
+        out["a2a_gemm_ulysses_cfg6"] = {"us": round(us, 2), "tflops": round(tf, 1),
+                                        "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                                        "timing": "HIP events around 30 launches in a row, pieces landed"}
+        log(f"a2a ulysses: {us:.1f} us, {tf:.0f} TFLOP/s")
         gbps, ms = reduce_rate(fo, wl.CFG4)
         out["dp_reduce_cfg4"] = {"us": round(ms * 1e3, 1), "gbps": round(gbps, 1),
                                  "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
@@ -794,6 +872,19 @@ def main():
             row["reps"] = sp["reps"]
         tails["cfg3_gemm_rs_reduce"] = row
         log(f"tail cfg3: {row}")
+        c6 = wl.CFG6
+        row = {"piece_gemm_at_70pct_peak_us": round(2.0 * c6.m * c6.n * (c6.k // c6.R) /
+                                                    (0.7 * PEAK_BF16_TFLOPS * 1e12) * 1e6, 2)}
+        for s_ in ("flashoverlap", "naive"):
+            sp = {}
+            t, span = measure_tail_a2a(fo, c6, hz, s_, spread=sp)
+            row[s_ + "_us"] = round(t, 2)
+            row[s_ + "_p10_p90_us"] = [sp["p10"], sp["p90"]]
+            row["last_arrival_us"] = round(span, 1)
+            row["reps"] = sp["reps"]
+        row["tail_over_piece_gemm_at_70pct"] = round(row["flashoverlap_us"] / row["piece_gemm_at_70pct_peak_us"], 3)
+        tails["cfg6_ulysses_a2a_gemm"] = row
+        log(f"tail cfg6: {row}")
         row = {}
         for s_ in ("flashoverlap", "naive"):
             sp = {}

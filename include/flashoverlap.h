@@ -231,6 +231,38 @@ fo_status fo_gemm_rs_ring(const void *x, const void *w, float *partial, uint32_t
                           int64_t m, int64_t n, int64_t k, const fo_schedule *s,
                           void *ws, size_t ws_bytes, void *stream);
 
+/* Flash All-to-All GEMM (technical summary §2: Flash All-to-All, the
+ * extension of the decomposed primitives to Ulysses parallelism; §1: Ulysses
+ * parallelism needs all-to-all).  The all-to-all after head-parallel
+ * attention hands this rank, from every rank q, its sequence rows of q's
+ * heads: piece q, a column block of the output projection's input.  Computes
+ *   y = [piece 0 | piece 1 | ... | piece P-1] * W
+ *     = sum over q of piece[q] * (columns [q*k/P, (q+1)*k/P) of W)
+ * with each piece's share multiplied once its flag shows it landed.
+ *   pieces  host [P] array of device bf16 [m][k/P] pointers (each piece
+ *           contiguous, as its message lands); P = s->nchunks.
+ *   w       device bf16 [n][k] (the K x N weight, K contiguous).
+ *   y       device [m][n], y_dtype FO_F32 or FO_BF16 (nearest even).
+ *   s       order: the order in which every output tile adds the pieces
+ *           (it fixes the bits); NULL = the local piece, then local-1,
+ *           local-2, ... (the order a pairwise-exchange all-to-all delivers
+ *           them).  arrived[q] gates piece q (never read for local; NULL =
+ *           every piece present); a piece is read only after its flag shows
+ *           the epoch, with one system-scope acquire per workgroup.  mode is
+ *           not used; split must be NULL or all 1.  stamps, optional, [2P+2]:
+ *           [2P] kernel start, [2P+1] last output tile written.
+ *   ws      device workspace of at least 4096 bytes, zero-filled once (a
+ *           fo_ag_gemm workspace serves; calls sharing it must not overlap).
+ * Each output element is summed in fp32 from bf16 MFMA products, piece by
+ * piece in `order` and k ascending inside a piece: a given order gives the
+ * same bits whatever the landing times.  Sizes: k % P == 0, (k/P) % 8 == 0,
+ * k <= 2^21, m and n at most 2^30.  Errors: NULL, SHAPE, ALIGN, DTYPE, ORDER,
+ * SCHEDULE, WORKSPACE, ALIAS (y overlapping w or a piece), HIP;
+ * FO_ERR_TIMEOUT in *status when a flag wait exceeds its bound. */
+fo_status fo_a2a_gemm(const void *const *pieces, const void *w, void *y, fo_dtype y_dtype,
+                      int64_t m, int64_t n, int64_t k, const fo_schedule *s,
+                      void *ws, size_t ws_bytes, void *stream);
+
 /* Chunk reduce-add (technical summary §1 DP reduce-scatter, §2 Flash-RS).
  *   srcs  host [R] array of device fp32 pointers, n elements each.
  *   dst   device, n elements of dst_dtype (FO_F32 or FO_BF16).

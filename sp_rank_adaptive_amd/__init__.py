@@ -28,7 +28,7 @@ FO_MAX_CHUNKS = 64
 
 FO_NOALLOC_SCRATCH_BYTES = 64 << 20
 
-EXPORTS = ("fo_workspace_bytes", "fo_ag_gemm", "fo_ag_gemm_noalloc", "fo_gemm_rs", "fo_gemm_rs_reduce", "fo_gemm_rs_ring", "fo_chunk_reduce",
+EXPORTS = ("fo_workspace_bytes", "fo_ag_gemm", "fo_ag_gemm_noalloc", "fo_a2a_gemm", "fo_gemm_rs", "fo_gemm_rs_reduce", "fo_gemm_rs_ring", "fo_chunk_reduce",
            "fo_emulate_arrivals", "fo_emulate_arrivals_gated", "fo_plan_ag_schedule", "fo_device_info", "fo_status_string",
            "fo_last_hip_error")
 
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.fo_ag_gemm.argtypes = [P, P, P, i32, i64, i64, i64, S, P, sz, P]
     L.fo_ag_gemm_noalloc.restype = i32
     L.fo_ag_gemm_noalloc.argtypes = [P, P, P, i32, i64, i64, i64, S, P]
+    L.fo_a2a_gemm.restype = i32
+    L.fo_a2a_gemm.argtypes = [P, P, P, i32, i64, i64, i64, S, P, sz, P]
     L.fo_gemm_rs.restype = i32
     L.fo_gemm_rs.argtypes = [P, P, P, P, i64, i64, i64, S, P, sz, P]
     L.fo_gemm_rs_reduce.restype = i32
@@ -231,6 +233,22 @@ def fo_ag_gemm_noalloc(x, w, y, sched: Schedule, stream=None, *, raise_on_error=
     del keep
     if raise_on_error:
         _check(st, "fo_ag_gemm_noalloc")
+    return st
+
+
+def fo_a2a_gemm(pieces, w, y, sched: Schedule, ws, stream=None, *, raise_on_error=True) -> int:
+    """y = [pieces[0] | ... | pieces[P-1]] * W, each piece [m, k/P] bf16
+    multiplied once it has landed (w [n, k] bf16, y [m, n] fp32 or bf16)."""
+    P = len(pieces)
+    m, kp = pieces[0].shape
+    n, k = w.shape
+    arr = (ctypes.c_void_p * P)(*[_ptr(t) for t in pieces])
+    s, keep = sched._c()
+    st = lib().fo_a2a_gemm(arr, _ptr(w), _ptr(y), _dtype_code(y), m, n, k, ctypes.byref(s), _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream(stream))
+    del keep
+    if raise_on_error:
+        _check(st, "fo_a2a_gemm")
     return st
 
 

@@ -484,6 +484,92 @@ fo_status fo_ag_gemm_noalloc(const void *x, const void *w, void *y, fo_dtype y_d
                   nullptr, true);
 }
 
+fo_status fo_a2a_gemm(const void *const *pieces, const void *w, void *y, fo_dtype y_dtype, int64_t m,
+                      int64_t n, int64_t k, const fo_schedule *s, void *ws, size_t ws_bytes, void *stream) {
+  if (y_dtype != FO_F32 && y_dtype != FO_BF16) return FO_ERR_DTYPE;
+  if (!pieces || !w || !y || !s) return FO_ERR_NULL;
+  fo_status st = check_schedule(s);
+  if (st != FO_OK) return st;
+  const int P = s->nchunks;
+  for (int q = 0; q < P; ++q)
+    if (!pieces[q]) return FO_ERR_NULL;
+  if (m <= 0 || n <= 0 || k <= 0 || k % P != 0) return FO_ERR_SHAPE;
+  if (m > (int64_t)1 << 30 || n > (int64_t)1 << 30 || k > kMaxK) return FO_ERR_SHAPE;
+  const int64_t kp = k / P;
+  if (kp % 8 != 0 || !aligned16(w)) return FO_ERR_ALIGN;
+  for (int q = 0; q < P; ++q)
+    if (!aligned16(pieces[q])) return FO_ERR_ALIGN;
+  const bool bf = y_dtype == FO_BF16;
+  if (!aligned16(y) && !bf) return FO_ERR_ALIGN;
+  if (s->split)
+    for (int q = 0; q < P; ++q)
+      if (s->split[q] != 1) return FO_ERR_SCHEDULE;
+  const size_t ybytes = (size_t)m * n * (bf ? 2 : 4);
+  if (overlaps(y, ybytes, w, (size_t)n * k * 2)) return FO_ERR_ALIAS;
+  for (int q = 0; q < P; ++q)
+    if (overlaps(y, ybytes, pieces[q], (size_t)m * kp * 2)) return FO_ERR_ALIAS;
+  if (!ws || ws_bytes < WS_HEADER_BYTES || !aligned16(ws)) return FO_ERR_WORKSPACE;
+
+  const DevInfo *I = dev_info();
+  if (!I) return FO_ERR_HIP;
+  A2aArgs a{};
+  for (int q = 0; q < P; ++q) a.piece[q] = static_cast<const uint16_t *>(pieces[q]);
+  a.w = static_cast<const uint16_t *>(w);
+  a.y = y;
+  a.y_bf16 = bf ? 1 : 0;
+  a.m = m; a.n = n; a.k = k;
+  a.kp = (int32_t)kp;
+  a.P = P;
+  a.local = s->local;
+  // default order: the piece already present, then the peers' pieces in the
+  // order pairwise exchange delivers them (local-1, local-2, ...)
+  if (s->order) {
+    for (int i = 0; i < P; ++i) a.order[i] = s->order[i];
+  } else {
+    for (int i = 0; i < P; ++i) a.order[i] = ((s->local - i) % P + P) % P;
+  }
+  a.tiles_m = (int32_t)((m + A2A_BM - 1) / A2A_BM);
+  a.tiles_n = (int32_t)((n + A2A_BN - 1) / A2A_BN);
+  {
+    // the rectangle shape whose operand rows per XCD are fewest
+    const int shapes[4][2] = {{1, 8}, {2, 4}, {4, 2}, {8, 1}};
+    int64_t best = -1;
+    for (const auto &sh : shapes) {
+      const int gm = sh[0], gn = sh[1];
+      int64_t cost = (int64_t)((a.tiles_m + gm - 1) / gm) * A2A_BM + (int64_t)((a.tiles_n + gn - 1) / gn) * A2A_BN;
+      if (gm > a.tiles_m || gn > a.tiles_n) cost += (int64_t)1 << 40;   // empty rectangles
+      if (best < 0 || cost < best) { best = cost; a.gm = gm; a.gn = gn; }
+    }
+    for (int g = 0; g < XCDS; ++g) {
+      const int i = g / a.gn, j = g % a.gn;
+      const int rows = (i + 1) * a.tiles_m / a.gm - i * a.tiles_m / a.gm;
+      const int cols = (j + 1) * a.tiles_n / a.gn - j * a.tiles_n / a.gn;
+      a.gtiles[g] = rows * cols;
+    }
+  }
+  // one workgroup per CU at most (the whole grid resident), none without a
+  // tile: each XCD's workgroups share its rectangle's tiles
+  const int full = I->cus;
+  const int cap = (s->max_workgroups > 0 && s->max_workgroups < full) ? s->max_workgroups : full;
+  int grid = 0;
+  for (int g = 0; g < XCDS; ++g) {
+    const int wgs_g = (cap - g + XCDS - 1) / XCDS;
+    const int use = a.gtiles[g] < wgs_g ? a.gtiles[g] : wgs_g;
+    // workgroup b sits on XCD b % 8: the grid must reach rank use - 1 on XCD g
+    if (use > 0 && (use - 1) * XCDS + g + 1 > grid) grid = (use - 1) * XCDS + g + 1;
+  }
+  a.grid = grid < 1 ? 1 : grid;
+  a.arrived = s->arrived;
+  a.epoch = s->epoch;
+  a.timeout_ticks = ns_to_ticks(s->timeout_ns ? s->timeout_ns : kDefaultTimeoutNs, I->wall_hz);
+  a.status = s->status;
+  a.stamps = s->stamps;
+  a.ws32 = static_cast<uint32_t *>(ws);
+  const hipError_t e = launch_a2a(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) { record(e); return FO_ERR_HIP; }
+  return FO_OK;
+}
+
 fo_status fo_gemm_rs(const void *x, const void *w, float *partial, uint32_t *done, int64_t m,
                      int64_t n, int64_t k, const fo_schedule *s, void *ws, size_t ws_bytes,
                      void *stream) {

@@ -97,6 +97,31 @@ struct ReduceArgs {
   uint64_t *stamps;
 };
 
+// All-to-all GEMM (fo_a2a_gemm): y = sum over pieces of piece[q] times the
+// column block q of W, each piece's k-range taken in `order` once it landed.
+struct A2aArgs {
+  const uint16_t *piece[FO_MAX_CHUNKS];   // bf16 [m][kp] each, indexed by piece id
+  const uint16_t *w;                      // bf16 [n][k], k = P * kp
+  void *y;                                // [m][n] fp32 or bf16
+  int32_t y_bf16;
+  int64_t m, n, k;
+  int32_t kp;                             // k extent of one piece
+  int32_t P, local;
+  int32_t order[FO_MAX_CHUNKS];           // accumulation order of the pieces
+  int32_t tiles_m, tiles_n, gm, gn;       // tile grid, cut into gm x gn rectangles
+  int32_t gtiles[XCDS];                   // tiles per rectangle (one per XCD)
+  int32_t grid;
+  const uint32_t *arrived;                // device [P] or null
+  uint32_t epoch;
+  uint64_t timeout_ticks;
+  int32_t *status;
+  uint64_t *stamps;                       // [2P+2]: [2P] start, [2P+1] last tile written
+  uint32_t *ws32;                         // counters (the workspace header)
+};
+
+constexpr int A2A_BM = 128, A2A_BN = 256;   // output tile of the all-to-all GEMM
+hipError_t launch_a2a(const A2aArgs &a, hipStream_t stream);
+
 // Tile configuration chosen for a problem (host).
 TileCfg choose_tile(int64_t mc, int64_t n, int64_t k, int R, int grid, bool leave_room);
 size_t partial_slot_bytes(const TileCfg &t);

@@ -289,3 +289,32 @@ def test_ag_gemm_noalloc_validation(L):
     s8, keep8 = sched(R=8)
     assert fo.fo_workspace_bytes(65536, 8192, 4096, 8) > fo.FO_NOALLOC_SCRATCH_BYTES
     assert na(A, A, A2, fo.FO_F32, 65536, 8192, 4096, ctypes.byref(s8), None) == fo.FO_ERR_WORKSPACE
+
+
+def test_a2a_gemm_validation(L):
+    R = 4
+    pcs = [A + 0x100000 * q for q in range(R)]
+
+    def a2(pieces=pcs, w=A2, y=A2 + 0x8000000, dt=fo.FO_F32, m=256, n=512, k=512, s=None, ws=WS, wsb=4096):
+        if s is None:
+            s, a2.keep = sched(R)
+        arr = None if pieces is None else (ctypes.c_void_p * R)(*pieces)
+        return L.fo_a2a_gemm(arr, w, y, dt, m, n, k, ctypes.byref(s) if s is not False else None, ws, wsb, None)
+    assert a2(pieces=None) == fo.FO_ERR_NULL
+    assert a2(pieces=[A, None, A, A]) == fo.FO_ERR_NULL
+    assert a2(w=None) == fo.FO_ERR_NULL
+    assert a2(s=False) == fo.FO_ERR_NULL
+    assert a2(dt=3) == fo.FO_ERR_DTYPE
+    assert a2(k=510) == fo.FO_ERR_SHAPE                     # k % P
+    assert a2(k=(1 << 21) + 32) == fo.FO_ERR_SHAPE
+    assert a2(k=48) == fo.FO_ERR_ALIGN                      # (k/P) % 8
+    assert a2(pieces=[A, A + 8, A, A]) == fo.FO_ERR_ALIGN
+    assert a2(y=A2 + 4) == fo.FO_ERR_ALIGN
+    assert a2(y=A2) == fo.FO_ERR_ALIAS                      # y overlaps w
+    assert a2(y=pcs[3]) == fo.FO_ERR_ALIAS                  # y overlaps a piece
+    assert a2(ws=None) == fo.FO_ERR_WORKSPACE
+    assert a2(wsb=1024) == fo.FO_ERR_WORKSPACE
+    s, keep = sched(R, split=[1, 2, 1, 1])
+    assert a2(s=s) == fo.FO_ERR_SCHEDULE
+    s, keep = sched(R, order=[0, 0, 1, 2])
+    assert a2(s=s) == fo.FO_ERR_ORDER
