@@ -383,3 +383,86 @@ def test_ulysses_all_to_all_equals_collective(orc, P, mode):
             scale = (np.abs(of) @ np.abs(wf).T)[r * sp:(r + 1) * sp]
             assert np.all(np.abs(ys[r] - rows) <= 1e-12 * scale + 1e-300)
             assert np.all(np.abs(orc.a2a_gemm(pieces, w) - rows) <= 1e-12 * scale + 1e-300)
+
+
+# ---- Query-Split Attention -----------------------------------------------------
+
+def qkv_case(S, H, d, seed, std=1.0):
+    return wl.bf16_operand((S, 3 * H * d), "gauss", std, seed)
+
+
+def test_bf16_fast_decode_matches_c_decode(orc):
+    allb = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = allb[((allb >> 7) & 0xFF) != 0xFF][::13]
+    assert np.array_equal(orc.bf16_to_f64_fast(finite), orc.bf16_to_f64(finite))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("S,H,d", [(64, 2, 16), (48, 1, 128), (96, 3, 32)])
+def test_attention_vs_torch_sdpa_float64(orc, causal, S, H, d):
+    """The plain definition against torch's scaled_dot_product_attention on
+    the CPU in float64 (an independent library routine)."""
+    import torch
+    from oracle import attention as at
+    qkv = qkv_case(S, H, d, 1300 + S + d)
+    x = orc.bf16_to_f64(qkv)
+    t = torch.from_numpy(x)
+    q = t[:, :H * d].reshape(S, H, d).transpose(0, 1)
+    k = t[:, H * d:2 * H * d].reshape(S, H, d).transpose(0, 1)
+    v = t[:, 2 * H * d:].reshape(S, H, d).transpose(0, 1)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal)
+    ref = ref.transpose(0, 1).reshape(S, H * d).numpy()
+    got = at.attention(qkv, H, d, causal)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_attention_closed_forms(orc):
+    """Zero queries give equal weights: every output row is the mean of the
+    value rows it sees (all of them, or the prefix 0..i when causal); one key
+    whose score dominates selects its value row."""
+    from oracle import attention as at
+    S, H, d = 40, 2, 16
+    qkv = qkv_case(S, H, d, 1401)
+    qkv[:, :H * d] = 0
+    v = orc.bf16_to_f64(qkv[:, 2 * H * d:])
+    full = at.attention(qkv, H, d, False)
+    assert np.allclose(full, np.broadcast_to(v.mean(axis=0), (S, H * d)), rtol=0, atol=1e-14)
+    cum = np.cumsum(v, axis=0) / np.arange(1, S + 1)[:, None]
+    assert np.allclose(at.attention(qkv, H, d, True), cum, rtol=0, atol=1e-14)
+    qkv = np.zeros((S, 3 * H * d), dtype=np.uint16)
+    one = wl.f32_to_bf16_bits(np.array([4.0], dtype=np.float32))[0]
+    big = wl.f32_to_bf16_bits(np.array([64.0], dtype=np.float32))[0]
+    qkv[:, 0] = one                       # head 0 queries: 4 e_0
+    qkv[17, H * d] = big                  # head 0, key 17: 64 e_0 (score 64)
+    qkv[:, 2 * H * d:] = wl.bf16_operand((S, H * d), "gauss", 1.0, 1402)
+    got = at.attention(qkv, H, d, False)
+    vrow = orc.bf16_to_f64(qkv[17, 2 * H * d:2 * H * d + d])
+    assert np.allclose(got[:, :d], np.broadcast_to(vrow, (S, d)), rtol=1e-20, atol=1e-20)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_query_split_blocks_equal_plain(orc, causal):
+    """The query-split decomposition (per query chunk, per key chunk blocks
+    merged with their maxima and sums) equals the plain definition, whatever
+    order the key chunks are merged in."""
+    from oracle import attention as at
+    S, H, d, R = 64, 2, 32, 4
+    qkv = qkv_case(S, H, d, 1501 + causal)
+    plain = at.attention(qkv, H, d, causal)
+    for order in itertools.permutations(range(R)):
+        got = at.attention_blocks(qkv, H, d, causal, R, order)
+        assert np.max(np.abs(got - plain)) <= 1e-13
+
+
+def test_attention_key_permutation_invariance(orc):
+    """Without a mask, permuting the tokens of K and V together leaves every
+    output row unchanged (softmax attention is a set function of the keys)."""
+    from oracle import attention as at
+    S, H, d = 32, 2, 16
+    qkv = qkv_case(S, H, d, 1601)
+    perm = rng(1602).permutation(S)
+    moved = qkv.copy()
+    moved[:, H * d:] = qkv[perm][:, H * d:]
+    a = at.attention(qkv, H, d, False)
+    b = at.attention(moved, H, d, False)
+    assert np.max(np.abs(a - b)) <= 1e-13

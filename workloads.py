@@ -70,7 +70,27 @@ CFG5 = GemmCfg(5, "long_seq_qkv_ag_gemm_tp16", "ag", 16384, 1280, 8192, 16)
 # is the 4096 x 4096 output projection.
 CFG6 = GemmCfg(6, "ulysses_out_proj_a2a_up8", "a2a", 2048, 4096, 4096, 8)
 
-CONFIGS = {1: CFG1, 2: CFG2, 3: CFG3, 4: CFG4, 5: CFG5, 6: CFG6}
+@dataclass(frozen=True)
+class AttnCfg:
+    """Query-split attention share: the QKV projection's output for S tokens
+    and H local heads of dimension d, arriving in R sequence chunks."""
+    cfg: int
+    name: str
+    S: int
+    H: int
+    d: int
+    R: int
+    local: int = 0
+    causal: bool = True
+    std: float = 1.0
+
+
+# Query-split attention, one rank's share of the summary's setting (hidden
+# size 4096, TP = 4): 8 of 32 heads of 128, a 4K-token causal sequence in 4
+# chunks of 1024 tokens (this rank's and three that arrive).
+CFG7 = AttnCfg(7, "tp4_query_split_attention", 4096, 8, 128, 4)
+
+CONFIGS = {1: CFG1, 2: CFG2, 3: CFG3, 4: CFG4, 5: CFG5, 6: CFG6, 7: CFG7}
 
 # tensor ids used in seeds
 T_X, T_W, T_INC, T_SRC, T_ORDER = 1, 2, 3, 10, 50
@@ -136,6 +156,13 @@ def a2a_pieces(c: GemmCfg, mode: str, m: int | None = None):
     x, w = gemm_inputs(c, mode, m=m)
     kp = c.k // c.R
     return [np.ascontiguousarray(x[:, q * kp:(q + 1) * kp]) for q in range(c.R)], w
+
+
+def qkv_input(c: AttnCfg, mode: str, S: int | None = None) -> np.ndarray:
+    """bf16 bits of the attention input qkv [S, 3*H*d] (queries, keys,
+    values of every head, one row per token)."""
+    S = c.S if S is None else S
+    return bf16_operand((S, 3 * c.H * c.d), mode, c.std, seed_for(c.cfg, T_X))
 
 
 def incoming_partials(c: GemmCfg, mode: str, rows: int | None = None):
