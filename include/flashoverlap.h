@@ -263,6 +263,41 @@ fo_status fo_a2a_gemm(const void *const *pieces, const void *w, void *y, fo_dtyp
                       int64_t m, int64_t n, int64_t k, const fo_schedule *s,
                       void *ws, size_t ws_bytes, void *stream);
 
+/* Query-Split Attention (technical summary §2: attention decomposed into
+ * scores, softmax and weighted sum so that more computation overlaps the
+ * communication).  For every head h:
+ *   O_h = softmax(Q_h K_h^T / sqrt(d) [+ causal mask]) V_h
+ * where the rows of Q, K and V (the QKV projection's output, one row per
+ * token) arrive in R sequence chunks (chunk c = rows [c*S/R, (c+1)*S/R)).
+ * The work is cut into blocks (head, 128 queries, key chunk), each released
+ * once the chunks order[0..s] it needs have landed (s = the later of its two
+ * chunks' positions in `order`), so blocks on landed chunks run while the
+ * rest is in flight; each query tile's blocks are merged in key-chunk order.
+ *   qkv     device bf16 [S][3*H*d]: per row the queries of heads 0..H-1 (d
+ *           each), then their keys, then their values.
+ *   o       device [S][H*d], o_dtype FO_F32 or FO_BF16 (nearest even).
+ *   head_dim must be 128; (S/R) % 128 == 0; 1 <= R <= 16.
+ *   causal  1: token i attends to tokens 0..i; 0: to every token.
+ *   s       order: stage order of the chunks (NULL = local, local-1,
+ *           local-2, ...: the order a ring delivers them); arrived[c] gates
+ *           chunk c (NULL = all present); split NULL or all 1; mode unused.
+ *           stamps, optional, [2R+2]: [2R] start, [2R+1] last output row
+ *           written.
+ *   ws      device workspace of fo_qsa_workspace_bytes(S, H, d, R) bytes,
+ *           zero-filled once (every call leaves its counters zero).
+ * Scores are bf16 MFMA products accumulated in fp32; the softmax runs in
+ * fp32 (base-2 exponentials); the weighted sum multiplies fp16
+ * probabilities by the values converted to fp16 (values must lie within
+ * fp16's range) with fp32 accumulation.  The bits depend on the inputs and R
+ * only, never on the order or the landing times.  Errors: NULL, SHAPE,
+ * ALIGN, DTYPE, ORDER, SCHEDULE, WORKSPACE, ALIAS (o or ws overlapping qkv,
+ * ws overlapping o), HIP; FO_ERR_TIMEOUT in *status when a flag wait
+ * exceeds its bound. */
+size_t fo_qsa_workspace_bytes(int64_t seq, int32_t heads, int32_t head_dim, int32_t nchunks);
+fo_status fo_qsa_attention(const void *qkv, void *o, fo_dtype o_dtype, int64_t seq, int32_t heads,
+                           int32_t head_dim, int32_t causal, const fo_schedule *s,
+                           void *ws, size_t ws_bytes, void *stream);
+
 /* Chunk reduce-add (technical summary §1 DP reduce-scatter, §2 Flash-RS).
  *   srcs  host [R] array of device fp32 pointers, n elements each.
  *   dst   device, n elements of dst_dtype (FO_F32 or FO_BF16).

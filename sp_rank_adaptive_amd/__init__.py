@@ -28,7 +28,8 @@ FO_MAX_CHUNKS = 64
 
 FO_NOALLOC_SCRATCH_BYTES = 64 << 20
 
-EXPORTS = ("fo_workspace_bytes", "fo_ag_gemm", "fo_ag_gemm_noalloc", "fo_a2a_gemm", "fo_gemm_rs", "fo_gemm_rs_reduce", "fo_gemm_rs_ring", "fo_chunk_reduce",
+EXPORTS = ("fo_workspace_bytes", "fo_ag_gemm", "fo_ag_gemm_noalloc", "fo_a2a_gemm", "fo_qsa_workspace_bytes", "fo_qsa_attention",
+           "fo_gemm_rs", "fo_gemm_rs_reduce", "fo_gemm_rs_ring", "fo_chunk_reduce",
            "fo_emulate_arrivals", "fo_emulate_arrivals_gated", "fo_plan_ag_schedule", "fo_device_info", "fo_status_string",
            "fo_last_hip_error")
 
@@ -80,6 +81,10 @@ def lib() -> ctypes.CDLL:
     L.fo_ag_gemm_noalloc.argtypes = [P, P, P, i32, i64, i64, i64, S, P]
     L.fo_a2a_gemm.restype = i32
     L.fo_a2a_gemm.argtypes = [P, P, P, i32, i64, i64, i64, S, P, sz, P]
+    L.fo_qsa_workspace_bytes.restype = sz
+    L.fo_qsa_workspace_bytes.argtypes = [i64, i32, i32, i32]
+    L.fo_qsa_attention.restype = i32
+    L.fo_qsa_attention.argtypes = [P, P, i32, i64, i32, i32, i32, S, P, sz, P]
     L.fo_gemm_rs.restype = i32
     L.fo_gemm_rs.argtypes = [P, P, P, P, i64, i64, i64, S, P, sz, P]
     L.fo_gemm_rs_reduce.restype = i32
@@ -249,6 +254,23 @@ def fo_a2a_gemm(pieces, w, y, sched: Schedule, ws, stream=None, *, raise_on_erro
     del keep
     if raise_on_error:
         _check(st, "fo_a2a_gemm")
+    return st
+
+
+def fo_qsa_workspace_bytes(seq: int, heads: int, head_dim: int, nchunks: int) -> int:
+    return int(lib().fo_qsa_workspace_bytes(seq, heads, head_dim, nchunks))
+
+
+def fo_qsa_attention(qkv, o, heads: int, head_dim: int, causal: bool, sched: Schedule, ws, stream=None, *,
+                     raise_on_error=True) -> int:
+    """Query-split attention: qkv [S, 3*H*d] bf16 -> o [S, H*d] fp32 or bf16."""
+    seq = qkv.shape[0]
+    s, keep = sched._c()
+    st = lib().fo_qsa_attention(_ptr(qkv), _ptr(o), _dtype_code(o), seq, heads, head_dim, int(bool(causal)),
+                                ctypes.byref(s), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    del keep
+    if raise_on_error:
+        _check(st, "fo_qsa_attention")
     return st
 
 

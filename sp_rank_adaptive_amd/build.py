@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libflashoverlap.so")
-SOURCES = ["fo_api.hip", "fo_gemm.hip", "fo_a2a.hip", "fo_reduce.hip", "fo_emulate.hip", "fo_plan.hip"]
+SOURCES = ["fo_api.hip", "fo_gemm.hip", "fo_a2a.hip", "fo_qsa.hip", "fo_reduce.hip", "fo_emulate.hip", "fo_plan.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

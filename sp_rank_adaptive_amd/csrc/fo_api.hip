@@ -3,6 +3,7 @@
 // Declarations, argument meaning and error behaviour: include/flashoverlap.h.
 #include <hip/hip_runtime.h>
 
+#include <math.h>
 #include <mutex>
 #include <stdio.h>
 #include <stdlib.h>
@@ -566,6 +567,122 @@ fo_status fo_a2a_gemm(const void *const *pieces, const void *w, void *y, fo_dtyp
   a.stamps = s->stamps;
   a.ws32 = static_cast<uint32_t *>(ws);
   const hipError_t e = launch_a2a(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) { record(e); return FO_ERR_HIP; }
+  return FO_OK;
+}
+
+namespace {
+
+// Query-split attention workspace: counters, then one partial slot per
+// (head, query tile, key chunk).
+struct QsaPlan {
+  size_t part_offset, total;
+};
+
+QsaPlan qsa_plan(int64_t seq, int64_t heads, int32_t R) {
+  const int64_t tiles = seq / QSA_BQ;
+  QsaPlan p{};
+  p.part_offset = ((size_t)(QSA_DONE + heads * tiles) * sizeof(uint32_t) + 255) & ~(size_t)255;
+  p.total = p.part_offset + (size_t)heads * tiles * R * (QSA_BQ * QSA_D + 2 * QSA_BQ) * sizeof(float);
+  return p;
+}
+
+fo_status qsa_shape(int64_t seq, int32_t heads, int32_t head_dim, int32_t R) {
+  if (R < 1 || R > QSA_MAX_CHUNKS) return FO_ERR_SHAPE;
+  if (seq <= 0 || heads <= 0 || head_dim != QSA_D || seq % R != 0) return FO_ERR_SHAPE;
+  const int64_t chunk = seq / R;
+  if (chunk % QSA_BQ != 0) return FO_ERR_SHAPE;
+  // a chunk of qkv rows is addressed with 32-bit byte offsets
+  if (chunk * 3 * (int64_t)heads * QSA_D * 2 >= ((int64_t)1 << 31) || seq > ((int64_t)1 << 30)) return FO_ERR_SHAPE;
+  return FO_OK;
+}
+
+}  // namespace
+
+size_t fo_qsa_workspace_bytes(int64_t seq, int32_t heads, int32_t head_dim, int32_t nchunks) {
+  if (qsa_shape(seq, heads, head_dim, nchunks) != FO_OK) return 0;
+  return qsa_plan(seq, heads, nchunks).total;
+}
+
+fo_status fo_qsa_attention(const void *qkv, void *o, fo_dtype o_dtype, int64_t seq, int32_t heads,
+                           int32_t head_dim, int32_t causal, const fo_schedule *s, void *ws, size_t ws_bytes,
+                           void *stream) {
+  if (o_dtype != FO_F32 && o_dtype != FO_BF16) return FO_ERR_DTYPE;
+  if (!qkv || !o || !s) return FO_ERR_NULL;
+  fo_status st = check_schedule(s);
+  if (st != FO_OK) return st;
+  const int R = s->nchunks;
+  st = qsa_shape(seq, heads, head_dim, R);
+  if (st != FO_OK) return st;
+  if (causal != 0 && causal != 1) return FO_ERR_SCHEDULE;
+  if (s->split)
+    for (int c = 0; c < R; ++c)
+      if (s->split[c] != 1) return FO_ERR_SCHEDULE;
+  const bool bf = o_dtype == FO_BF16;
+  if (!aligned16(qkv) || !aligned16(o)) return FO_ERR_ALIGN;
+  const size_t obytes = (size_t)seq * heads * QSA_D * (bf ? 2 : 4);
+  if (overlaps(o, obytes, qkv, (size_t)seq * 3 * heads * QSA_D * 2)) return FO_ERR_ALIAS;
+  const QsaPlan plan = qsa_plan(seq, heads, R);
+  if (!ws || ws_bytes < plan.total || !aligned16(ws)) return FO_ERR_WORKSPACE;
+  if (overlaps(ws, plan.total, o, obytes) || overlaps(ws, plan.total, qkv, (size_t)seq * 3 * heads * QSA_D * 2))
+    return FO_ERR_ALIAS;
+
+  const DevInfo *I = dev_info();
+  if (!I) return FO_ERR_HIP;
+  QsaArgs a{};
+  a.qkv = static_cast<const uint16_t *>(qkv);
+  a.o = o;
+  a.o_bf16 = bf ? 1 : 0;
+  a.S = (int32_t)seq;
+  a.H = heads;
+  a.R = R;
+  a.causal = causal;
+  a.chunk = (int32_t)(seq / R);
+  a.tiles = a.chunk / QSA_BQ;
+  a.local = s->local;
+  // default order: the local chunk, then the others in ring landing order
+  if (s->order) {
+    for (int i = 0; i < R; ++i) a.order[i] = s->order[i];
+  } else {
+    for (int i = 0; i < R; ++i) a.order[i] = ((s->local - i) % R + R) % R;
+  }
+  // Stage s: the (query chunk, key chunk) pairs whose later chunk in `order`
+  // is order[s]: the new chunk's queries against the earlier chunks' keys
+  // and the earlier queries against its keys, then the new chunk with
+  // itself.  With the causal mask, pairs whose keys all follow the queries
+  // are empty and left out.
+  int np = 0;
+  const int per_pair = heads * a.tiles;
+  for (int sg = 0; sg < R; ++sg) {
+    a.stage_pair0[sg] = np;
+    const int cs = a.order[sg];
+    auto add = [&](int qc, int kc) {
+      if (causal && kc > qc) return;
+      a.pair_q[np] = (int8_t)qc;
+      a.pair_k[np] = (int8_t)kc;
+      ++np;
+    };
+    for (int p = 0; p < sg; ++p) {
+      add(cs, a.order[p]);
+      add(a.order[p], cs);
+    }
+    add(cs, cs);
+    a.stage_units[sg] = (np - a.stage_pair0[sg]) * per_pair;
+  }
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)QSA_D));
+  const int64_t blocks = (int64_t)np * per_pair;
+  const int full = 2 * I->cus;   // two workgroups per CU
+  const int cap = (s->max_workgroups > 0 && s->max_workgroups < full) ? s->max_workgroups : full;
+  a.grid = (int32_t)(blocks < cap ? blocks : cap);
+  if (a.grid < 1) a.grid = 1;
+  a.arrived = s->arrived;
+  a.epoch = s->epoch;
+  a.timeout_ticks = ns_to_ticks(s->timeout_ns ? s->timeout_ns : kDefaultTimeoutNs, I->wall_hz);
+  a.status = s->status;
+  a.stamps = s->stamps;
+  a.ws32 = static_cast<uint32_t *>(ws);
+  a.part = reinterpret_cast<float *>(static_cast<char *>(ws) + plan.part_offset);
+  const hipError_t e = launch_qsa(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) { record(e); return FO_ERR_HIP; }
   return FO_OK;
 }

@@ -122,6 +122,37 @@ struct A2aArgs {
 constexpr int A2A_BM = 128, A2A_BN = 256;   // output tile of the all-to-all GEMM
 hipError_t launch_a2a(const A2aArgs &a, hipStream_t stream);
 
+// Query-split attention (fo_qsa_attention).  A block is (head, 128-query
+// tile, key chunk); blocks are released in stages (stage s opens once the
+// chunks order[0..s] have landed).
+constexpr int QSA_MAX_CHUNKS = 16;
+constexpr int QSA_BQ = 128, QSA_BKV = 64, QSA_D = 128;
+constexpr int QSA_DONE = 1024;                  // word offset of the per-(head, tile) block counters
+struct QsaArgs {
+  const uint16_t *qkv;                          // bf16 [S][3*H*d]
+  void *o;                                      // [S][H*d] fp32 or bf16
+  int32_t o_bf16;
+  int32_t S, H, R, causal;
+  int32_t chunk;                                // rows per chunk
+  int32_t tiles;                                // query tiles per chunk
+  int32_t local;
+  int32_t order[QSA_MAX_CHUNKS];
+  int32_t stage_units[QSA_MAX_CHUNKS];          // blocks released by stage s
+  int32_t stage_pair0[QSA_MAX_CHUNKS];          // first pair of stage s in pair_q / pair_k
+  int8_t pair_q[QSA_MAX_CHUNKS * QSA_MAX_CHUNKS];  // (query chunk, key chunk) pairs by stage
+  int8_t pair_k[QSA_MAX_CHUNKS * QSA_MAX_CHUNKS];
+  float scale_log2;                             // log2(e) / sqrt(d)
+  int32_t grid;
+  const uint32_t *arrived;
+  uint32_t epoch;
+  uint64_t timeout_ticks;
+  int32_t *status;
+  uint64_t *stamps;                             // [2R+2]: [2R] start, [2R+1] last output written
+  uint32_t *ws32;                               // counters, then the partial slots
+  float *part;                                  // per (head, query tile, key chunk): O [BQ][d], m [BQ], l [BQ]
+};
+hipError_t launch_qsa(const QsaArgs &a, hipStream_t stream);
+
 // Tile configuration chosen for a problem (host).
 TileCfg choose_tile(int64_t mc, int64_t n, int64_t k, int R, int grid, bool leave_room);
 size_t partial_slot_bytes(const TileCfg &t);

@@ -1,0 +1,472 @@
+// Query-split attention for gfx950: O = softmax(scale * Q K^T [+ causal
+// mask]) V per head, computed in blocks released as the sequence chunks land.
+//
+// Query-Split Attention (gist.science technical summary §2: attention
+// decomposed into scores, softmax and weighted sum, so that more of it
+// overlaps the communication).  Under sequence-parallel all-gather the rows
+// of Q, K and V (the QKV projection's output for each token) arrive chunk by
+// chunk.  The work is cut into blocks (head, 128-query tile, key chunk):
+// every block needs its query chunk and its key chunk only, so blocks on
+// chunks that have landed run while the rest is in flight, and the queries of
+// the chunk that lands last are spread over all their key chunks instead of
+// one long unit.  Each block leaves its row maxima, sums of exponentials and
+// unnormalised weighted sums; the block that completes a query tile merges
+// its tile's blocks in key-chunk order (so the bits never depend on landing
+// times) and writes the output rows.
+//
+// Layout and schedule
+//  - 4 waves per workgroup, 32 queries each; two workgroups per CU.  A key
+//    tile of 64 rows is copied into LDS by the buffer-load DMA path
+//    (16-byte pieces XOR-swizzled by row); the value tile goes through
+//    registers into LDS transposed, as fp16, so each lane reads its value
+//    fragments as two 8-byte pieces.
+//  - Scores are computed transposed, S^T = K Q^T (bf16 MFMA, fp32
+//    accumulate), so each lane holds one query's scores for 4 keys of every
+//    16-key block: the softmax needs one cross-lane step per tile, and the
+//    probabilities are already laid out as the second operand of
+//    O^T = V^T P^T (fp16 MFMA, fp32 accumulate), whose rows for a query sit in
+//    that query's lane.  Both operands of O^T take the keys of a 32-key
+//    k-step in the same permuted order (4 from each of two 16-key blocks).
+//  - Blocks are released in stages: stage s holds the blocks whose later
+//    chunk is order[s], and opens once the chunks order[0..s] have landed.
+//    Wave 0 claims the next block of the lowest open stage with one
+//    fetch-add; a workgroup acquires (system scope) the first time it uses a
+//    peer's chunk.
+#include "fo_device.hpp"
+#include "fo_internal.hpp"
+#include "fo_tile.hpp"
+
+namespace fo {
+
+namespace {
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int QS_THREADS = 256;
+constexpr int QS_WAVES = 4;
+constexpr int K_ROWB = QSA_D * 2;                  // 256 bytes per key row
+constexpr int K_TILE = QSA_BKV * K_ROWB;           // 16 KiB
+constexpr int VT_ROWB = 144;                       // 64 fp16 keys + 16 bytes of padding
+constexpr int VT_TILE = QSA_D * VT_ROWB;           // 18 KiB
+constexpr int K_STAGES = 3;                        // key tiles in the LDS ring
+constexpr int QS_LDS = K_STAGES * K_TILE + VT_TILE;
+constexpr int SLOT_FLOATS = QSA_BQ * QSA_D + 2 * QSA_BQ;   // O [BQ][d], m [BQ], l [BQ]
+constexpr int QS_EXITED = 576, QS_COMBINED = 577, QS_ABORT = 578;
+constexpr float NEG_BIG = -1.0e30f;
+
+struct Blk {
+  int h, qt, qc, kc;   // head, query tile over the whole sequence, query chunk, key chunk; qt < 0: stop
+};
+
+__device__ __forceinline__ void store_wt4(float *p, float v) {
+  asm volatile("global_store_dword %0, %1, off sc0 sc1" :: "v"(p), "v"(v) : "memory");
+}
+
+// Loads of data another workgroup wrote through during this launch, at
+// system-coherent cache policy (sc0 sc1), without a fence.  The resource is
+// the slot's (wave-uniform); the offset is per lane.
+__device__ __forceinline__ f32x4 load_coherent16(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 1 | 2));
+}
+
+__device__ __forceinline__ float load_coherent4(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 1 | 2));
+}
+
+// Wave 0 (all lanes) claims the next block: the lowest open stage that has
+// blocks left.  Stage s is open once order[0..s] have all landed.  Waits
+// (bounded) while blocks are left only in stages that are not open.
+__device__ Blk qsa_claim(const QsaArgs &a, uint32_t &acquired, uint64_t &wait_from) {
+  const int lane = threadIdx.x & 63;
+  const int R = a.R;
+  for (;;) {
+    bool ok = false, left = false;
+    if (lane < R) {
+      const int c = a.order[lane];
+      ok = a.arrived == nullptr || c == a.local || epoch_reached(load_relaxed(a.arrived + c), a.epoch);
+      left = load_relaxed(a.ws32 + lane) < (uint32_t)a.stage_units[lane];
+    }
+    const uint64_t landed = __ballot(ok);
+    const uint64_t lm = __ballot(left);
+    if (lm == 0ull) return Blk{0, -1, 0, 0};                       // every block claimed
+    const int open = (~landed == 0ull) ? 64 : __builtin_ctzll(~landed);
+    const uint64_t om = open >= 64 ? lm : (lm & ((1ull << open) - 1ull));
+    if (om) {
+      const int s = __builtin_ctzll(om);
+      uint32_t u = 0;
+      if (lane == 0) u = fetch_add_relaxed(a.ws32 + s, 1u);
+      u = __builtin_amdgcn_readfirstlane(u);
+      if (u >= (uint32_t)a.stage_units[s]) continue;                 // lost the race: look again
+      const int per_pair = a.H * a.tiles;
+      const int pi = a.stage_pair0[s] + (int)u / per_pair;
+      const int rem = (int)u - ((int)u / per_pair) * per_pair;
+      Blk b;
+      b.h = rem / a.tiles;
+      b.qc = a.pair_q[pi];
+      b.kc = a.pair_k[pi];
+      b.qt = b.qc * a.tiles + (rem - b.h * a.tiles);
+      // first use of a peer's chunk by this workgroup: its rows were written
+      // by a copy engine during the launch
+      const uint32_t need = (1u << b.qc) | (1u << b.kc);
+      if (a.arrived != nullptr && (need & ~acquired)) {
+        uint32_t peers = need & ~acquired & ~(1u << a.local);
+        if (peers) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+        acquired |= need;
+      }
+      return b;
+    }
+    if (wait_from == 0) wait_from = now_ticks();
+    bool out = false;
+    if (lane == 0) out = load_relaxed(a.ws32 + QS_ABORT) != 0u || now_ticks() - wait_from > a.timeout_ticks;
+    if (__ballot(out)) {
+      if (lane == 0) {
+        if (a.status) __hip_atomic_store(a.status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(a.ws32 + QS_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      return Blk{0, -2, 0, 0};
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// One block: the 128 queries of tile b.qt against the keys of chunk b.kc, for
+// head b.h; leaves the tile's row maxima m, sums l and unnormalised weighted
+// sums O (fp32, written through) in the block's slot.
+__device__ __forceinline__ void qsa_block(const QsaArgs &a, char *lds, const Blk &b) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  const int HD = a.H * QSA_D;
+  const int64_t RS = 3 * (int64_t)HD;                     // qkv row stride (elements)
+  const int q0 = b.qt * QSA_BQ;
+  const int kbase = b.kc * a.chunk;
+  const bool diag = a.causal && b.kc == b.qc;
+  const int nkt_all = a.chunk / QSA_BKV;
+  // with the causal mask, key tiles past the tile's last query are empty
+  const int nkt = diag ? (q0 + QSA_BQ - 1 - kbase) / QSA_BKV + 1 : nkt_all;
+
+  // Query fragments (second operand of S^T = K Q^T): lane (g, li) holds
+  // query row q0 + 32 wave + 16 qb + li, head dims 32 ks + 8 g .. + 8.
+  bf16x8 qf[2][4];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const uint16_t *qrow = a.qkv + (int64_t)(q0 + wave * 32 + qb * 16 + li) * RS + b.h * QSA_D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[qb][ks] = *reinterpret_cast<const bf16x8 *>(qrow + ks * 32);
+  }
+
+  // Key tile copies: thread t fills 16-byte slot t of each of 4 rounds (16
+  // key rows per round); slot t holds row t / 16 of the round, physical piece
+  // t % 16, i.e. logical piece (t % 16) ^ (row % 16).
+  const __amdgpu_buffer_rsrc_t rsk =
+      uniform_rsrc(a.qkv + (int64_t)kbase * RS + HD + b.h * QSA_D, (int)((int64_t)a.chunk * RS * 2));
+  const int ksl = tid & 255;
+  const int k_voff = (int)(((ksl >> 4) * RS + (((ksl & 15) ^ (ksl >> 4)) * 8)) * 2);
+  const uint32_t k_lds0 = lds_addr(lds) + (uint32_t)(__builtin_amdgcn_readfirstlane(wave) * 1024);
+  auto issue_k = [&](int kt) {
+    const uint32_t base = k_lds0 + (uint32_t)((kt % K_STAGES) * K_TILE);
+#pragma unroll
+    for (int rd = 0; rd < 4; ++rd)
+      dma16(base + (uint32_t)(rd * 4096), k_voff, rsk, (int)((int64_t)(kt * QSA_BKV + rd * 16) * RS * 2));
+  };
+  // Value tile: thread items idx = tid, tid + 256 cover key pairs kp = idx % 32
+  // and head-dimension groups e = idx / 32 (8 values each).
+  // Two register sets: the loads of tile kt + 2 go out while tile kt is
+  // multiplied, and set kt % 2 is written to LDS once tile kt - 1 is done.
+  const uint16_t *vbase = a.qkv + (int64_t)kbase * RS + 2 * HD + b.h * QSA_D;
+  bf16x8 vr[2][2][2];
+  auto load_v = [&](int kt, auto setc) {
+    constexpr int st = decltype(setc)::value;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int idx = tid + it * QS_THREADS;
+      const int kp = idx & 31, e = idx >> 5;
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        vr[st][it][r] = *reinterpret_cast<const bf16x8 *>(vbase + (int64_t)(kt * QSA_BKV + 2 * kp + r) * RS + 8 * e);
+    }
+  };
+  auto store_vt = [&](auto setc) {
+    constexpr int st = decltype(setc)::value;
+    char *vt = lds + K_STAGES * K_TILE;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int idx = tid + it * QS_THREADS;
+      const int kp = idx & 31, e = idx >> 5;
+#pragma unroll
+      for (int dc = 0; dc < 8; ++dc) {
+        const _Float16 lo = (_Float16)(float)vr[st][it][0][dc];
+        const _Float16 hi = (_Float16)(float)vr[st][it][1][dc];
+        const uint32_t word = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        *reinterpret_cast<uint32_t *>(vt + (8 * e + dc) * VT_ROWB + 4 * kp) = word;
+      }
+    }
+  };
+
+  f32x4 o[8][2];
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {NEG_BIG, NEG_BIG}, l[2] = {0.f, 0.f};
+
+  // Pipeline: the K copy and V loads of tile kt + 2 are issued at the start
+  // of tile kt; V^T of tile kt + 1 is written after tile kt's weighted sum.
+  // Each wave issues 8 vector-memory operations per tile (4 copies, 4 loads),
+  // which complete in order.
+  __syncthreads();                 // the previous block's last tile is done with the buffers
+  issue_k(0);
+  load_v(0, std::integral_constant<int, 0>{});
+  if (nkt > 1) {
+    issue_k(1);
+    load_v(1, std::integral_constant<int, 1>{});
+    wait_vm<8>();
+  } else {
+    wait_vm<0>();
+  }
+  store_vt(std::integral_constant<int, 0>{});
+  __syncthreads();
+  auto tile = [&](int kt, auto setc) {
+    constexpr int vs = decltype(setc)::value;   // kt % 2
+    if (kt + 2 < nkt) {
+      issue_k(kt + 2);
+      load_v(kt + 2, setc);        // set kt % 2 was written to LDS before tile kt
+    }
+    const char *K = lds + (kt % K_STAGES) * K_TILE;
+    const char *VT = lds + K_STAGES * K_TILE;
+    // S^T = K Q^T: st[kb][qb], keys 16 kb + 4 g + v, query 16 qb + li
+    f32x4 st[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(K + (kb * 16 + li) * K_ROWB + (((ks * 4 + g) ^ li) << 4));
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : st[kb][qb], 0, 0, 0);
+      }
+    }
+    // online softmax per query (scores in log2 units)
+    f16x8 pf[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qrow = q0 + wave * 32 + qb * 16 + li;
+      float mx = NEG_BIG;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float s = st[kb][qb][v] * a.scale_log2;
+          if (diag && kbase + kt * QSA_BKV + kb * 16 + 4 * g + v > qrow) s = -__builtin_inff();
+          st[kb][qb][v] = s;
+          mx = fmaxf(mx, s);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m[qb], mx);
+      const float f = __builtin_amdgcn_exp2f(m[qb] - mnew);
+      m[qb] = mnew;
+      float sum = 0.f;
+      _Float16 p16[4][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float p = __builtin_amdgcn_exp2f(st[kb][qb][v] - mnew);
+          sum += p;
+          p16[kb][v] = (_Float16)p;
+        }
+      l[qb] = l[qb] * f + sum;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) o[db][qb] *= f;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+        pf[qb][k2] = f16x8{p16[2 * k2][0], p16[2 * k2][1], p16[2 * k2][2], p16[2 * k2][3],
+                           p16[2 * k2 + 1][0], p16[2 * k2 + 1][1], p16[2 * k2 + 1][2], p16[2 * k2 + 1][3]};
+    }
+    // O^T += V^T P^T: value rows 16 db + li, keys 4 g + 0..3 of blocks 2 k2
+    // and 2 k2 + 1 (the same key order as pf)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const char *row = VT + (db * 16 + li) * VT_ROWB;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const f16x4 lo = *reinterpret_cast<const f16x4 *>(row + ((2 * k2) * 16 + 4 * g) * 2);
+        const f16x4 hi = *reinterpret_cast<const f16x4 *>(row + ((2 * k2 + 1) * 16 + 4 * g) * 2);
+        const f16x8 vf = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qb][k2], o[db][qb], 0, 0, 0);
+      }
+    }
+    if (kt + 1 < nkt) {
+      __syncthreads();             // every wave is done with V^T of tile kt
+      if (kt + 2 < nkt) wait_vm<8>();   // tile kt + 1's copies and loads have landed
+      else wait_vm<0>();
+      store_vt(std::integral_constant<int, 1 - vs>{});
+      __syncthreads();             // K and V^T of tile kt + 1 visible
+    }
+  };
+  for (int kt = 0; kt < nkt; kt += 2) {
+    tile(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < nkt) tile(kt + 1, std::integral_constant<int, 1>{});
+  }
+
+  // the block's slot: O rows by query (value dims 16 db + 4 g + v in lane
+  // (g, li) of query 16 qb + li), then m and l per query
+  const int QT = a.S / QSA_BQ;
+  float *slot = a.part + ((int64_t)(b.h * QT + b.qt) * a.R + b.kc) * SLOT_FLOATS;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = wave * 32 + qb * 16 + li;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) store_wt16(slot + r * QSA_D + db * 16 + 4 * g, o[db][qb]);
+    float lt = l[qb];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (g == 0) {
+      store_wt4(slot + QSA_BQ * QSA_D + r, m[qb]);
+      store_wt4(slot + QSA_BQ * QSA_D + QSA_BQ + r, lt);
+    }
+  }
+}
+
+// Merge of a query tile's blocks (key chunks 0 .. nb-1, in that order): per
+// query, M = max m, L = sum 2^(m - M) l, O = sum (2^(m - M) / L) O.  The
+// maxima and sums go through LDS (the block's buffers are idle here), then
+// each thread merges 16-byte pieces of output rows, all its loads in flight
+// together.
+__device__ __forceinline__ void qsa_combine(const QsaArgs &a, char *lds, int h, int qt, int nb) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int QT = a.S / QSA_BQ;
+  const float *slot0 = a.part + (int64_t)(h * QT + qt) * a.R * SLOT_FLOATS;
+  float *s_m = reinterpret_cast<float *>(lds);                     // [nb][BQ]
+  float *s_l = s_m + QSA_MAX_CHUNKS * QSA_BQ;                      // [nb][BQ]
+  __syncthreads();   // the block's last tile is done with LDS
+  for (int idx = tid; idx < nb * QSA_BQ; idx += QS_THREADS) {
+    const int j = idx / QSA_BQ, r = idx - (idx / QSA_BQ) * QSA_BQ;
+    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(slot0 + (int64_t)j * SLOT_FLOATS, SLOT_FLOATS * 4);
+    s_m[idx] = load_coherent4(rs, (QSA_BQ * QSA_D + r) * 4);
+    s_l[idx] = load_coherent4(rs, (QSA_BQ * QSA_D + QSA_BQ + r) * 4);
+  }
+  __syncthreads();
+  if (tid < QSA_BQ) {
+    float M = NEG_BIG;
+    for (int j = 0; j < nb; ++j) M = fmaxf(M, s_m[j * QSA_BQ + tid]);
+    float L = 0.f;
+    for (int j = 0; j < nb; ++j) {
+      const float w = __builtin_amdgcn_exp2f(s_m[j * QSA_BQ + tid] - M);
+      s_m[j * QSA_BQ + tid] = w;
+      L += w * s_l[j * QSA_BQ + tid];
+    }
+    for (int j = 0; j < nb; ++j) s_m[j * QSA_BQ + tid] /= L;     // the weights
+  }
+  __syncthreads();
+  const int HD = a.H * QSA_D;
+  constexpr int PIECES = QSA_BQ * (QSA_D / 4);                     // 16-byte output pieces
+  constexpr int PER = PIECES / QS_THREADS;
+  f32x4 acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < nb; ++j) {
+    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(slot0 + (int64_t)j * SLOT_FLOATS, SLOT_FLOATS * 4);
+    f32x4 t[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) t[k] = load_coherent16(rs, (tid + k * QS_THREADS) * 16);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int r = (tid + k * QS_THREADS) / (QSA_D / 4);
+      acc[k] += s_m[j * QSA_BQ + r] * t[k];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int idx = tid + k * QS_THREADS;
+    const int r = idx / (QSA_D / 4), c4 = idx - r * (QSA_D / 4);
+    const int64_t off = (int64_t)(qt * QSA_BQ + r) * HD + h * QSA_D + 4 * c4;
+    if (a.o_bf16) {
+      const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[k][0]) | ((uint32_t)f32_to_bf16_rne(acc[k][1]) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[k][2]) | ((uint32_t)f32_to_bf16_rne(acc[k][3]) << 16);
+      *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.o) + off) = u32x2{lo, hi};
+    } else {
+      *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.o) + off) = acc[k];
+    }
+  }
+}
+
+// Two workgroups per CU under a register cap: on gfx950 the attribute counts
+// pairs of the unified register file, so 120 caps each wave at 240 and the
+// two waves of a SIMD leave 32 of each lane's 512 registers free, where the
+// one-wave kernels of a copy-engine emulator still fit beside the grid.
+__global__ void __launch_bounds__(QS_THREADS, 2) __attribute__((amdgpu_num_vgpr(120))) qsa_kernel(QsaArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[QS_LDS];
+  __shared__ Blk s_blk;
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  asm volatile("" :: "v"(lds) : "memory");
+  if (blockIdx.x == 0 && tid == 0 && a.stamps) store_u64_relaxed(a.stamps + 2 * a.R, now_ticks());
+  uint32_t acquired = 0;
+  uint64_t wait_from = 0;
+  for (;;) {
+    if (wave == 0) {
+      const Blk b = qsa_claim(a, acquired, wait_from);
+      if (lane == 0) s_blk = b;
+    }
+    __syncthreads();
+    Blk b = s_blk;
+    b.h = __builtin_amdgcn_readfirstlane(b.h);
+    b.qt = __builtin_amdgcn_readfirstlane(b.qt);
+    b.qc = __builtin_amdgcn_readfirstlane(b.qc);
+    b.kc = __builtin_amdgcn_readfirstlane(b.kc);
+    if (b.qt < 0) break;
+    qsa_block(a, lds, b);
+    // count the block once its stores are acknowledged; the block that
+    // completes the tile merges it
+    wait_stores();
+    __syncthreads();
+    const int nb = a.causal ? b.qc + 1 : a.R;
+    if (tid == 0) {
+      uint32_t *ctr = a.ws32 + QSA_DONE + b.h * (a.S / QSA_BQ) + b.qt;
+      const uint32_t old = fetch_add_relaxed(ctr, 1u);
+      s_last = old == (uint32_t)(nb - 1);
+      if (s_last) store_relaxed_agent(ctr, 0u);   // the tile's last user: back to zero
+    }
+    __syncthreads();
+    if (s_last) {
+      qsa_combine(a, lds, b.h, b.qt, nb);
+      if (a.stamps) {
+        __syncthreads();
+        if (tid == 0) {
+          const uint32_t t = fetch_add_relaxed(a.ws32 + QS_COMBINED, 1u);
+          if (t == (uint32_t)(a.H * (a.S / QSA_BQ) - 1)) store_u64_relaxed(a.stamps + 2 * a.R + 1, now_ticks());
+        }
+      }
+    }
+  }
+  // the last workgroup to leave returns the counters to zero (after an abort
+  // the tiles' block counters too: their tiles were left unfinished)
+  if (tid == 0) {
+    const uint32_t e = fetch_add_relaxed(a.ws32 + QS_EXITED, 1u);
+    if (e == (uint32_t)(a.grid - 1)) {
+      if (load_relaxed_agent(a.ws32 + QS_ABORT) != 0u)
+        for (int t = 0; t < a.H * (a.S / QSA_BQ); ++t) store_relaxed_agent(a.ws32 + QSA_DONE + t, 0u);
+      for (int s = 0; s < a.R; ++s) store_relaxed_agent(a.ws32 + s, 0u);
+      store_relaxed_agent(a.ws32 + QS_COMBINED, 0u);
+      store_relaxed_agent(a.ws32 + QS_ABORT, 0u);
+      store_relaxed_agent(a.ws32 + QS_EXITED, 0u);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_qsa(const QsaArgs &a, hipStream_t stream) {
+  hipLaunchKernelGGL(qsa_kernel, dim3(a.grid), dim3(QS_THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace fo

@@ -318,3 +318,33 @@ def test_a2a_gemm_validation(L):
     assert a2(s=s) == fo.FO_ERR_SCHEDULE
     s, keep = sched(R, order=[0, 0, 1, 2])
     assert a2(s=s) == fo.FO_ERR_ORDER
+
+
+def test_qsa_validation(L):
+    R, S, H, d = 4, 512, 2, 128
+    wsb = fo.fo_qsa_workspace_bytes(S, H, d, R)
+    assert wsb > 0
+    assert fo.fo_qsa_workspace_bytes(S, H, 64, R) == 0          # head_dim must be 128
+    assert fo.fo_qsa_workspace_bytes(500, H, d, R) == 0         # S % R
+    assert fo.fo_qsa_workspace_bytes(S, H, d, 17) == 0          # at most 16 chunks
+    assert fo.fo_qsa_workspace_bytes(4 * 64, H, d, 4) == 0      # chunk of 64 rows < 128
+
+    def qa(qkv=A, o=A2, dt=fo.FO_F32, seq=S, heads=H, hd=d, causal=1, s=None, ws=WS, n=wsb):
+        if s is None:
+            s, qa.keep = sched(R)
+        return L.fo_qsa_attention(qkv, o, dt, seq, heads, hd, causal,
+                                  ctypes.byref(s) if s is not False else None, ws, n, None)
+    assert qa(qkv=None) == fo.FO_ERR_NULL
+    assert qa(s=False) == fo.FO_ERR_NULL
+    assert qa(dt=2) == fo.FO_ERR_DTYPE
+    assert qa(hd=64) == fo.FO_ERR_SHAPE
+    assert qa(seq=640) == fo.FO_ERR_SHAPE                    # chunk 160 not a multiple of 128
+    assert qa(causal=2) == fo.FO_ERR_SCHEDULE
+    assert qa(qkv=A + 8) == fo.FO_ERR_ALIGN
+    assert qa(o=A + 4096) == fo.FO_ERR_ALIAS                 # o inside qkv
+    assert qa(ws=None) == fo.FO_ERR_WORKSPACE
+    assert qa(n=wsb - 16) == fo.FO_ERR_WORKSPACE
+    s, keep = sched(R, split=[1, 1, 2, 1])
+    assert qa(s=s) == fo.FO_ERR_SCHEDULE
+    s, keep = sched(R, order=[1, 1, 2, 3])
+    assert qa(s=s) == fo.FO_ERR_ORDER

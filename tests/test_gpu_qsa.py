@@ -1,0 +1,182 @@
+"""GPU parity of fo_qsa_attention (Query-Split Attention) against the fp64
+attention oracle, through the C ABI: causal and not, every chunk order (same
+bits), bf16 output, large-score inputs, emulated SDMA arrivals of the QKV
+rows into NaN-poisoned rows (ring order and out of order), the flag timeout,
+and the TP=4 attention share at full size (every output element)."""
+import itertools
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from helpers import bf16_bits_to_f64, check_tolerance, dev_bf16, host, log
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+_EP = [60000]
+_SIDE = []
+D = 128
+
+
+def epoch():
+    _EP[0] += 1
+    return _EP[0]
+
+
+def side_stream():
+    if not _SIDE:
+        _SIDE.append(torch.cuda.Stream())
+    return _SIDE[0]
+
+
+@pytest.fixture(scope="module")
+def fo():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sp_rank_adaptive_amd as fo
+    fo.lib()
+    side_stream()
+    return fo
+
+
+@pytest.fixture(scope="module")
+def att():
+    from oracle import attention
+    return attention
+
+
+def run(fo, qkv_b, H, R, causal, o_dtype=torch.float32, ws=None, **sched):
+    S = qkv_b.shape[0]
+    qkv = dev_bf16(qkv_b)
+    o = torch.full((S, H * D), float("nan"), dtype=o_dtype, device="cuda")
+    if ws is None:
+        ws = torch.zeros(fo.fo_qsa_workspace_bytes(S, H, D, R), dtype=torch.uint8, device="cuda")
+    fo.fo_qsa_attention(qkv, o, H, D, causal, fo.Schedule(nchunks=R, epoch=epoch(), **sched), ws)
+    torch.cuda.synchronize()
+    return host(o), ws
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("S,H,R", [(512, 2, 4), (256, 1, 1), (768, 3, 3), (1024, 2, 8)])
+def test_qsa_parity(fo, orc, att, causal, S, H, R):
+    log(f"case: qsa S={S} H={H} R={R} causal={causal}")
+    qkv = wl.bf16_operand((S, 3 * H * D), "gauss", 1.0, 18000 + S + H + R)
+    ref = att.attention(qkv, H, D, causal)
+    y, ws = run(fo, qkv, H, R, causal)
+    check_tolerance(y, ref, what="qsa")
+    assert int(ws[:4096].sum()) == 0, "counters not returned to zero"
+    y2, _ = run(fo, qkv, H, R, causal, ws=ws, arrived=torch.full((R,), 1 << 30, dtype=torch.int32, device="cuda"))
+    assert np.array_equal(y, y2), "preset flags changed the bits"
+
+
+def test_qsa_every_order_same_bits_and_bf16(fo, orc, att):
+    S, H, R = 512, 2, 4
+    qkv = wl.bf16_operand((S, 3 * H * D), "gauss", 1.0, 18100)
+    ref = att.attention(qkv, H, D, True)
+    base, ws = run(fo, qkv, H, R, True)
+    flags = torch.full((R,), 1 << 30, dtype=torch.int32, device="cuda")
+    for order in itertools.permutations(range(R)):
+        y, _ = run(fo, qkv, H, R, True, ws=ws, order=list(order), local=order[0], arrived=flags)
+        assert np.array_equal(y, base), f"order {order} changed the bits"
+    y, _ = run(fo, qkv, H, R, True, o_dtype=torch.bfloat16, ws=ws)
+    check_tolerance(bf16_bits_to_f64(y), ref, frob_ref=bf16_bits_to_f64(orc.f64_to_bf16(ref)), what="bf16 out")
+
+
+def test_qsa_large_scores(fo, orc, att):
+    """Integer inputs in [-3, 3]: scores up to about 80, nearly one-hot
+    softmax rows; the running maximum keeps every exponential in range."""
+    S, H, R = 512, 2, 4
+    qkv = wl.bf16_operand((S, 3 * H * D), "int", 1.0, 18200)
+    for causal in (True, False):
+        ref = att.attention(qkv, H, D, causal)
+        y, _ = run(fo, qkv, H, R, causal)
+        check_tolerance(y, ref, what=f"int inputs causal={causal}")
+
+
+def qsa_emulated(fo, qkv_b, H, R, local, arrival, release_ns, causal=True, order=None):
+    """fo_qsa_attention with the peers' chunks of QKV rows copied by SDMA at
+    release_ns[i] (chunk arrival[i]) into rows filled with NaN first."""
+    S = qkv_b.shape[0]
+    c = S // R
+    staging = dev_bf16(qkv_b)
+    qkv = staging.clone()
+    o = torch.full((S, H * D), float("nan"), device="cuda")
+    flags = torch.zeros(R, dtype=torch.int32, device="cuda")
+    es = torch.zeros(R + 2, dtype=torch.int64, device="cuda")
+    gs = torch.zeros(2 * R + 2, dtype=torch.int64, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(fo.fo_qsa_workspace_bytes(S, H, D, R), dtype=torch.uint8, device="cuda")
+    e = epoch()
+    for q in arrival:
+        qkv[q * c:(q + 1) * c].fill_(float("nan"))
+    torch.cuda.synchronize()
+    side = side_stream()
+    with torch.cuda.stream(side):
+        fo.fo_emulate_arrivals([qkv[q * c:(q + 1) * c] for q in arrival], [staging[q * c:(q + 1) * c] for q in arrival],
+                               [int(t) for t in release_ns], arrival, flags, e, es, stream=side,
+                               gate=gs[2 * R:2 * R + 1])
+    fo.fo_qsa_attention(qkv, o, H, D, causal, fo.Schedule(nchunks=R, local=local, order=order, arrived=flags,
+                                                          epoch=e, stamps=gs, status=status,
+                                                          timeout_ns=5_000_000_000), ws)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "flag wait timed out"
+    assert int(ws[:4096].sum()) == 0
+    st = host(gs).astype(np.int64)
+    last = max(host(es).astype(np.int64)[1 + q] for q in arrival)
+    assert st[2 * R + 1] >= last, "output completed before the last landing"
+    return host(o)
+
+
+@pytest.mark.parametrize("local", [0, 2])
+def test_qsa_emulated_arrivals(fo, orc, att, local):
+    S, H, R = 1024, 2, 4
+    qkv = wl.bf16_operand((S, 3 * H * D), "gauss", 1.0, 18300 + local)
+    ref = att.attention(qkv, H, D, True)
+    ring = [(local - s) % R for s in range(1, R)]
+    log(f"case: qsa emulated ring arrivals, local {local}")
+    base, _ = run(fo, qkv, H, R, True)
+    y = qsa_emulated(fo, qkv, H, R, local, ring, [15_000 * (i + 1) for i in range(R - 1)])
+    check_tolerance(y, ref, what="emulated ring")
+    assert np.array_equal(y, base), "landing times changed the bits"
+    shuffled = wl.seeded_permutation(ring, 40 + local)
+    log(f"case: qsa emulated out-of-order arrivals {shuffled}")
+    y = qsa_emulated(fo, qkv, H, R, local, shuffled, [10_000 * (i + 1) for i in range(R - 1)])
+    assert np.array_equal(y, base), "out-of-order landings changed the bits"
+
+
+def test_qsa_timeout_from_unset_flag(fo):
+    S, H, R = 512, 1, 4
+    qkv = dev_bf16(wl.bf16_operand((S, 3 * H * D), "gauss", 1.0, 18400))
+    flags = torch.zeros(R, dtype=torch.int32, device="cuda")
+    e = epoch()
+    flags.fill_(e)
+    flags[3] = 0
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(fo.fo_qsa_workspace_bytes(S, H, D, R), dtype=torch.uint8, device="cuda")
+    o = torch.zeros((S, H * D), device="cuda")
+    fo.fo_qsa_attention(qkv, o, H, D, True, fo.Schedule(nchunks=R, epoch=e, arrived=flags, status=status,
+                                                        timeout_ns=2_000_000), ws)
+    torch.cuda.synchronize()
+    assert int(status.item()) == fo.FO_ERR_TIMEOUT
+    counters = (1024 + H * (S // 128)) * 4          # stage, exit and per-tile counters
+    assert int(ws[:counters].sum()) == 0, "counters not returned to zero after the abort"
+    flags.fill_(epoch())
+    fo.fo_qsa_attention(qkv, o, H, D, True, fo.Schedule(nchunks=R, epoch=_EP[0], arrived=flags), ws)
+    torch.cuda.synchronize()
+
+
+def test_qsa_tp4_share_full_size(fo, orc, att):
+    """8 heads of 128, 4096 causal tokens in 4 chunks: every output element
+    within the bar, all landed and with emulated 50 GB/s ring arrivals."""
+    c = wl.CFG7
+    qkv = wl.qkv_input(c, "gauss")
+    log("oracle: qsa tp4 share")
+    ref = att.attention(qkv, c.H, c.d, c.causal)
+    y, _ = run(fo, qkv, c.H, c.R, c.causal)
+    check_tolerance(y, ref, what="tp4 share")
+    ring = [(c.local - s) % c.R for s in range(1, c.R)]
+    rel = wl.ring_release_ns((c.S // c.R) * 3 * c.H * c.d * 2, c.R - 1)
+    y2 = qsa_emulated(fo, qkv, c.H, c.R, c.local, ring, rel, causal=c.causal)
+    assert np.array_equal(y, y2), "arrivals changed the bits"
