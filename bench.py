@@ -441,6 +441,78 @@ def measure_tail_a2a(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.L
     return float(np.median(tails)), float(np.median(spans))
 
 
+def qsa_rate(fo, cfg, launches=20):
+    """All-landed query-split attention over launches in a row: (average us,
+    TFLOP/s of the attention work: 4 S^2 d H, halved with the causal mask)."""
+    import torch
+    qkv = dev_bf16(wl.qkv_input(cfg, "gauss"))
+    o = torch.empty((cfg.S, cfg.H * cfg.d), device="cuda")
+    ws = torch.zeros(fo.fo_qsa_workspace_bytes(cfg.S, cfg.H, cfg.d, cfg.R), dtype=torch.uint8, device="cuda")
+    flags = torch.full((cfg.R,), 1 << 30, dtype=torch.int32, device="cuda")
+    sched = lambda e: fo.Schedule(nchunks=cfg.R, epoch=e, arrived=flags)
+    for e in range(3):
+        fo.fo_qsa_attention(qkv, o, cfg.H, cfg.d, cfg.causal, sched(1 + e), ws)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(torch.cuda.current_stream())
+    for e in range(launches):
+        fo.fo_qsa_attention(qkv, o, cfg.H, cfg.d, cfg.causal, sched(10 + e), ws)
+    b.record(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / launches
+    flops = 4.0 * cfg.S * cfg.S * cfg.d * cfg.H * (0.5 if cfg.causal else 1.0)
+    return us, flops / us / 1e6
+
+
+def measure_tail_qsa(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LINK_BW, spread=None):
+    """Exposed tail of query-split attention: the peers' chunks of QKV rows
+    land by emulated ring arrivals; the tail is the time from the last landing
+    to the last output row written.
+      flashoverlap: one launch whose blocks run as their chunks land;
+      naive: wait for every chunk, then the same launch."""
+    import torch
+    staging = dev_bf16(wl.qkv_input(cfg, "gauss"))
+    qkv = staging.clone()
+    o = torch.empty((cfg.S, cfg.H * cfg.d), device="cuda")
+    R, local, c = cfg.R, cfg.local, cfg.S // cfg.R
+    order = wl.ring_arrival_order(R, local)
+    nbytes = c * 3 * cfg.H * cfg.d * 2
+    flags = torch.zeros(R, dtype=torch.int32, device="cuda")
+    es = torch.zeros(R + 2, dtype=torch.int64, device="cuda")
+    gs = torch.zeros(2 * R + 2, dtype=torch.int64, device="cuda")
+    ws = torch.zeros(fo.fo_qsa_workspace_bytes(cfg.S, cfg.H, cfg.d, R), dtype=torch.uint8, device="cuda")
+    side = side_stream()
+    main = torch.cuda.current_stream()
+    tails, spans = [], []
+    for rep in range(reps + 1):
+        e = 500 + rep
+        gs.zero_()
+        torch.cuda.synchronize()
+        dsts = [qkv[q * c:(q + 1) * c] for q in order]
+        srcs = [staging[q * c:(q + 1) * c] for q in order]
+        if schedule == "naive":
+            _emulate(fo, dsts, srcs, order, nbytes, flags, e, es, side, link_bw)
+            ev = torch.cuda.Event()
+            ev.record(side)
+            main.wait_event(ev)
+            fo.fo_qsa_attention(qkv, o, cfg.H, cfg.d, cfg.causal, fo.Schedule(nchunks=R, epoch=e, stamps=gs), ws)
+        else:
+            _emulate(fo, dsts, srcs, order, nbytes, flags, e, es, side, link_bw, gate=gs[2 * R:2 * R + 1])
+            fo.fo_qsa_attention(qkv, o, cfg.H, cfg.d, cfg.causal,
+                                fo.Schedule(nchunks=R, epoch=e, arrived=flags, stamps=gs, timeout_ns=5_000_000_000),
+                                ws)
+        torch.cuda.synchronize()
+        e_st = es.cpu().numpy().astype(np.int64)
+        g_st = gs.cpu().numpy().astype(np.int64)
+        last = max(e_st[1 + q] for q in order)
+        if rep > 0:
+            tails.append(ticks_to_us(g_st[2 * R + 1] - last, hz))
+            spans.append(ticks_to_us(last - e_st[0], hz))
+    _spread(spread, tails)
+    return float(np.median(tails)), float(np.median(spans))
+
+
 def link_sweep(fo, hz, bws=(50e9, 153e9, 400e9, 1000e9)):
     """End-to-end time (first release to output complete) and exposed tail at
     several per-link bandwidths.  The data are copied in before the timed
@@ -826,6 +898,11 @@ def main():
                                         "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                                         "timing": "HIP events around 30 launches in a row, pieces landed"}
         log(f"a2a ulysses: {us:.1f} us, {tf:.0f} TFLOP/s")
+        us, tf = qsa_rate(fo, wl.CFG7)
+        out["qsa_attention_tp4_cfg7"] = {"us": round(us, 2), "tflops": round(tf, 1),
+                                         "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                                         "timing": "HIP events around 20 launches in a row, chunks landed"}
+        log(f"qsa attention: {us:.1f} us, {tf:.0f} TFLOP/s")
         gbps, ms = reduce_rate(fo, wl.CFG4)
         out["dp_reduce_cfg4"] = {"us": round(ms * 1e3, 1), "gbps": round(gbps, 1),
                                  "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
@@ -885,6 +962,16 @@ def main():
         row["tail_over_piece_gemm_at_70pct"] = round(row["flashoverlap_us"] / row["piece_gemm_at_70pct_peak_us"], 3)
         tails["cfg6_ulysses_a2a_gemm"] = row
         log(f"tail cfg6: {row}")
+        row = {}
+        for s_ in ("flashoverlap", "naive"):
+            sp = {}
+            t, span = measure_tail_qsa(fo, wl.CFG7, hz, s_, spread=sp)
+            row[s_ + "_us"] = round(t, 2)
+            row[s_ + "_p10_p90_us"] = [sp["p10"], sp["p90"]]
+            row["last_arrival_us"] = round(span, 1)
+            row["reps"] = sp["reps"]
+        tails["cfg7_query_split_attention"] = row
+        log(f"tail cfg7: {row}")
         row = {}
         for s_ in ("flashoverlap", "naive"):
             sp = {}

@@ -94,12 +94,14 @@ __device__ __forceinline__ void group_tile(const GemmArgs &a, int g, int tl, int
 
 // Reduce unit v of chunk c: wait (wave 0, all lanes) until the v / RED_SLICES-th
 // tile of the chunk is published on its ready list, then fill r.  A split
-// tile is published once all its splits are written; the tile counter reads S
-// only after all S splits counted themselves, and reading it, then an acquire
-// fence, orders this unit's reads of the partials after every split's
-// stores.  An unsplit tile (the fused shard units) is published by its only
-// unit after its written-through stores; the shard unit reads it with
-// coherent loads and needs no fence.  On abort or timeout r.c = -2.
+// tile is published once all its splits are written: every split unit waits
+// for its written-through stores before it counts itself, and the tile
+// counter reads S only after all S splits counted themselves.  The reduce
+// unit then reads the partials with system-coherent loads, which do not hit
+// a stale line in any cache, so it needs no fence (an acquire fence would
+// invalidate the XCD's whole L2 once per reduce unit).  An unsplit tile (the
+// fused shard units) is published by its only unit after its written-through
+// stores and read the same way.  On abort or timeout r.c = -2.
 __device__ __forceinline__ void take_reduce_unit(const GemmArgs &a, int c, uint32_t v, Unit &r) {
   const int lane = threadIdx.x & 63;
   uint32_t e = 0;
@@ -129,7 +131,6 @@ __device__ __forceinline__ void take_reduce_unit(const GemmArgs &a, int c, uint3
       while (load_relaxed_agent(ctr) < (uint32_t)a.split[c] && now_ticks() - t0 <= a.timeout_ticks)
         __builtin_amdgcn_s_sleep(1);
     }
-    fence_acquire_agent();
   }
   r.c = c;
   r.tm = tile / a.tiles_n;
@@ -454,7 +455,8 @@ __device__ __forceinline__ void put4(char *base, int64_t ld, int64_t row, int64_
 }
 
 // Reduce unit: row slice `slice` of split tile `tile` of chunk c, whose S
-// partials are all written; sums them in split order 0..S-1 and stores the
+// partials are all written (through to memory); reads them with
+// system-coherent loads, sums them in split order 0..S-1 and stores the
 // output rows.
 template <int BM, int BN, int NTT>
 __device__ __forceinline__ void reduce_unit(const GemmArgs &a, int c, int tile, int slice, int64_t row0,
@@ -470,13 +472,16 @@ __device__ __forceinline__ void reduce_unit(const GemmArgs &a, int c, int tile, 
   static_assert(BM % RED_SLICES == 0, "slices");
   const int r0 = slice * ROWS;
   const bool vec_ok = (N & 3) == 0;
+  // one resource over the tile's S partials (at most 8 x 256 x 256 fp32)
+  const __amdgpu_buffer_rsrc_t rp = uniform_rsrc(P, S * BM * BN * 4);
   for (int pc = tid; pc < ROWS * PPR; pc += NTT) {
     const int rr = r0 + pc / PPR, cc = pc - (pc / PPR) * PPR;
-    const size_t off = (size_t)rr * BN + (size_t)cc * 4;
+    const int off = (rr * BN + cc * 4) * 4;
     f32x4 t[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      if (q < S) t[q] = *reinterpret_cast<const f32x4 *>(P + (size_t)q * (BM * BN) + off);
+      if (q < S)
+        t[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, off + q * (BM * BN * 4), 0, 1 | 2));
     f32x4 sum = t[0];
 #pragma unroll
     for (int q = 1; q < 8; ++q)
