@@ -202,19 +202,25 @@ def _emulate(fo, dsts, srcs, order, nbytes, flags, e, es, side, link_bw, copy=Tr
 
 
 def measure_tail_ag(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LINK_BW, copy=True, split=None,
-                    spread=None):
+                    spread=None, sub=1):
     """Exposed tail of the AG-GEMM under emulated ring arrivals (us): time
     from the last chunk's landing to the last output written.
       flashoverlap: one persistent launch, ready-first claims over the flags;
       strict: the same launch taking chunks exactly in priority order;
       naive: wait for every chunk, then one GEMM launch;
-      sliced: one launch per chunk, each after a stream wait on its flag."""
+      sliced: one launch per chunk, each after a stream wait on its flag.
+    sub > 1 (flashoverlap): each peer's chunk is sent as `sub` messages of
+    m/(R*sub) rows over the same link, one after another (the last byte lands
+    when the whole chunk would have), and the launch sees R*sub chunks with
+    the local ones flagged present; split then indexes those chunks."""
     import torch
     xb, wb = wl.gemm_inputs(cfg, "gauss")
     staging = dev_bf16(xb)
     w = dev_bf16(wb)
     x = staging.clone()
     y = torch.empty((cfg.m, cfg.n), device="cuda")
+    if sub > 1:
+        return _tail_ag_sub(fo, cfg, hz, staging, x, w, y, sub, reps, link_bw, split, spread)
     mc = cfg.m // cfg.R
     order = wl.ring_arrival_order(cfg.R, cfg.local)
     nbytes = mc * cfg.k * 2
@@ -281,6 +287,57 @@ def measure_tail_ag(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LI
             spans.append(ticks_to_us(last_arrival - t_start, hz))
     _spread(spread, tails)
     return float(np.median(tails)), float(np.median(spans))
+
+
+def sub_chunk_schedule(R, local, sub, nbytes, link_bw=wl.LINK_BW):
+    """Ring arrivals with each peer chunk sent as `sub` messages: the launch's
+    chunks are the R*sub sub-chunks (sub-chunk j of chunk c is index c*sub+j).
+    Returns (priority order over the sub-chunks: peers' in landing order, then
+    the local ones; the peers' sub-chunks in landing order; their release
+    times in ns; the local sub-chunks)."""
+    ring = wl.ring_arrival_order(R, local)
+    step = nbytes / link_bw * 1e9
+    peers, rel = [], []
+    for s_, c in enumerate(ring):
+        for j in range(sub):
+            peers.append(c * sub + j)
+            rel.append(s_ * step + (j + 1) * step / sub)
+    locals_ = [local * sub + j for j in range(sub)]
+    return peers + locals_, peers, rel, locals_
+
+
+def _tail_ag_sub(fo, cfg, hz, staging, x, w, y, sub, reps, link_bw, split, spread):
+    import torch
+    R2 = cfg.R * sub
+    mc2 = cfg.m // R2
+    order, peers, rel, locals_ = sub_chunk_schedule(cfg.R, cfg.local, sub, (cfg.m // cfg.R) * cfg.k * 2, link_bw)
+    nb2 = mc2 * cfg.k * 2
+    iss = [r - nb2 / link_bw * 1e9 for r in rel]
+    flags = torch.zeros(R2, dtype=torch.int32, device="cuda")
+    es = torch.zeros(R2 + 2, dtype=torch.int64, device="cuda")
+    gs = torch.zeros(2 * R2 + 2, dtype=torch.int64, device="cuda")
+    ws = torch.zeros(fo.fo_workspace_bytes(cfg.m, cfg.n, cfg.k, R2), dtype=torch.uint8, device="cuda")
+    side = side_stream()
+    tails = []
+    for rep in range(reps + 1):
+        e = 700 + rep
+        gs.zero_()
+        for q in locals_:
+            flags[q] = e            # the local rows are present
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            fo.fo_emulate_arrivals([x[q * mc2:(q + 1) * mc2] for q in peers], [staging[q * mc2:(q + 1) * mc2] for q in peers],
+                                   rel, peers, flags, e, es, issue_ns=iss, stream=side, gate=gs[2 * R2:2 * R2 + 1])
+        fo.fo_ag_gemm(x, w, y, fo.Schedule(nchunks=R2, local=locals_[0], order=order, arrived=flags, epoch=e,
+                                           stamps=gs, timeout_ns=5_000_000_000, split=split), ws)
+        torch.cuda.synchronize()
+        e_st = es.cpu().numpy().astype(np.int64)
+        g_st = gs.cpu().numpy().astype(np.int64)
+        last = max(e_st[1 + q] for q in peers)
+        if rep > 0:
+            tails.append(ticks_to_us(g_st[2 * R2 + 1] - last, hz))
+    _spread(spread, tails)
+    return float(np.median(tails)), 0.0
 
 
 def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LINK_BW, copy=True, span=False,

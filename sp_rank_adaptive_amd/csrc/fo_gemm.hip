@@ -389,6 +389,59 @@ __device__ Unit claim_unit(const GemmArgs &a, ClaimState &st, int xg, int &rank_
       continue;   // lost the race for the last unit: look again
     }
     if (has_work == 0 && red_left == 0 && red_blocked == 0) { r.c = -1; return r; }   // every unit claimed
+    // Claim ahead: GEMM work is left only in chunks that have not landed.
+    // Take a unit of the first such chunk in priority order now (own XCD's
+    // group first) and wait for that chunk's flag alone, so the unit starts
+    // as soon as the chunk lands, without a walk over every counter after
+    // the landing.  The wait depends on the flag only (set from outside the
+    // launch), never on another workgroup.
+    if (has_work != 0 && a.arrived != nullptr) {
+      const int sidx = __builtin_ctzll(has_work);   // first position with GEMM work (not landed)
+      const int c = a.order[sidx];
+      if (!((landed >> sidx) & 1ull)) {
+        uint32_t u = 0;
+        int g_got = -1;
+        for (int t = 0; t < XCDS && g_got < 0; ++t) {
+          const int g = (xg + t) % XCDS;
+          if (group_units(a, c, g) == 0u) continue;
+          if (lane == 0) u = fetch_add_relaxed(a.ws32 + WS_CLAIM + c * XCDS + g, 1u);
+          u = __builtin_amdgcn_readfirstlane(u);
+          if (u < group_units(a, c, g)) g_got = g;
+        }
+        if (g_got >= 0) {
+          bool ok = true;
+          if (lane == 0) {
+            const uint64_t t0 = now_ticks();
+            while (!epoch_reached(load_relaxed(a.arrived + c), a.epoch)) {
+              if (load_relaxed(a.ws32 + WS_ABORT) || now_ticks() - t0 > a.timeout_ticks) { ok = false; break; }
+              __builtin_amdgcn_s_sleep(1);
+            }
+          }
+          if (!__builtin_amdgcn_readfirstlane((int)ok)) {
+            if (lane == 0) {
+              if (a.status) __hip_atomic_store(a.status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_SYSTEM);
+              __hip_atomic_store(a.ws32 + WS_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            r.c = -2;
+            return r;
+          }
+          if (!((st.acquired >> c) & 1ull)) {   // first use of the landed chunk
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+            st.acquired |= 1ull << c;
+          }
+          const int S = a.split[c];
+          const int tl = (int)u / S;
+          r.c = c;
+          r.sp = (int)u - tl * S;
+          group_tile(a, g_got, tl, r.tm, r.tn);
+          r.first = (g_got == 0 && u == 0);
+          r.red = 0;
+          return r;
+        }
+        continue;   // that chunk's units are all taken: look again
+      }
+    }
     // Work is left only in chunks that have not landed (or, in STRICT mode,
     // behind one), and only a landing can change that: other workgroups'
     // claims only remove work.  So until the landed set changes, only the
