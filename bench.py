@@ -570,6 +570,63 @@ def measure_tail_qsa(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.L
     return float(np.median(tails)), float(np.median(spans))
 
 
+def measure_sends(fo, cfg, hz, form="gemm_rs", reps=10, link_bw=wl.LINK_BW, schedule="flashoverlap"):
+    """Send side of the reduce-scatter: the 7 peer-destined fp32 partials of
+    the GEMM-RS share are sent by emulated SDMA copies, one link, each
+    occupying it for B / BW.
+      flashoverlap: each send starts once its chunk's done flag is released
+        (fo_emulate_sends enqueued on the side stream before the launch);
+      naive: the sends start after the launch has completed.
+    Returns medians (us) of: the launch's duration, the first send's start
+    after the launch start, and the last send's completion after the launch
+    end (the sends' exposed tail)."""
+    import torch
+    xb, wb = wl.gemm_inputs(cfg, "gauss")
+    x, w = dev_bf16(xb), dev_bf16(wb)
+    R, local = cfg.R, cfg.local
+    mc = cfg.m // R
+    part = torch.empty((cfg.m, cfg.n), device="cuda")
+    done = torch.zeros(R, dtype=torch.int32, device="cuda")
+    gs = torch.zeros(2 * R + 2, dtype=torch.int64, device="cuda")
+    ws = torch.zeros(fo.fo_workspace_bytes(cfg.m, cfg.n, cfg.k, R), dtype=torch.uint8, device="cuda")
+    peers = wl.ring_arrival_order(R, local)
+    inbox = [torch.empty((mc, cfg.n), device="cuda") for _ in peers]
+    st = torch.zeros(2 * len(peers), dtype=torch.int64, device="cuda")
+    shard = torch.empty((mc, cfg.n), dtype=torch.bfloat16, device="cuda")
+    inc = [None if q == local else torch.zeros((mc, cfg.n), device="cuda") for q in range(R)]
+    link_ns = [mc * cfg.n * 4 / link_bw * 1e9] * len(peers)
+    side = side_stream()
+    main = torch.cuda.current_stream()
+    g_len, first, tail = [], [], []
+    for rep in range(reps + 1):
+        e = 900 + rep
+        gs.zero_()
+        torch.cuda.synchronize()
+        enqueue = lambda: fo.fo_emulate_sends(done, e, inbox, [part[q * mc:(q + 1) * mc] for q in peers], peers,
+                                              link_ns, st, timeout_ns=5_000_000_000, stream=side)
+        if schedule != "naive":
+            with torch.cuda.stream(side):
+                enqueue()
+        if form == "fused":
+            fo.fo_gemm_rs_reduce(x, w, part, done, shard, inc, fo.Schedule(nchunks=R, epoch=e, stamps=gs), ws)
+        else:
+            fo.fo_gemm_rs(x, w, part, done, fo.Schedule(nchunks=R, epoch=e, stamps=gs), ws)
+        if schedule == "naive":
+            ev = torch.cuda.Event()
+            ev.record(main)
+            side.wait_event(ev)
+            with torch.cuda.stream(side):
+                enqueue()
+        torch.cuda.synchronize()
+        g = gs.cpu().numpy().astype(np.int64)
+        t = st.cpu().numpy().astype(np.int64)
+        if rep > 0:
+            g_len.append(ticks_to_us(g[2 * R + 1] - g[2 * R], hz))
+            first.append(ticks_to_us(t[0] - g[2 * R], hz))
+            tail.append(ticks_to_us(t[-1] - g[2 * R + 1], hz))
+    return float(np.median(g_len)), float(np.median(first)), float(np.median(tail))
+
+
 def link_sweep(fo, hz, bws=(50e9, 153e9, 400e9, 1000e9)):
     """End-to-end time (first release to output complete) and exposed tail at
     several per-link bandwidths.  The data are copied in before the timed
@@ -1006,6 +1063,16 @@ def main():
             row["reps"] = sp["reps"]
         tails["cfg3_gemm_rs_reduce"] = row
         log(f"tail cfg3: {row}")
+        row = {}
+        for bw in (50e9, 1000e9):
+            for form in ("gemm_rs", "fused"):
+                for sched in ("flashoverlap", "naive"):
+                    glen, first, tail = measure_sends(fo, c3, hz, form, link_bw=bw, schedule=sched)
+                    row[f"{form}_{sched}_{bw / 1e9:g}GBps"] = {"launch_us": round(glen, 2),
+                                                               "first_send_start_us": round(first, 2),
+                                                               "last_send_after_launch_end_us": round(tail, 2)}
+        tails["cfg3_peer_sends"] = row
+        log(f"sends cfg3: {row}")
         c6 = wl.CFG6
         row = {"piece_gemm_at_70pct_peak_us": round(2.0 * c6.m * c6.n * (c6.k // c6.R) /
                                                     (0.7 * PEAK_BF16_TFLOPS * 1e12) * 1e6, 2)}

@@ -351,6 +351,27 @@ fo_status fo_emulate_arrivals_gated(const uint64_t *gate, uint64_t gate_timeout_
                                     int32_t count, uint32_t *arrived, uint32_t epoch,
                                     uint64_t *stamps, void *stream);
 
+/* Emulated peer sends of the reduce-scatter (technical summary §2, Flash-RS:
+ * the partial outputs destined for peers are computed first so that their
+ * sends start while the rest is computed).  On `stream` (a side stream,
+ * normally), for each i in 0..count-1 in array order, one send after another
+ * (one link):
+ *   wait until done[chunk_id[i]] shows the epoch (the GEMM-RS launch released
+ *   that chunk's rows; bounded by timeout_ns, 0 = 10 s; a timeout writes
+ *   FO_ERR_TIMEOUT to *status if given and the send goes ahead), record
+ *   stamps[2i] = start; copy bytes[i] from src[i] to dst[i] on a DMA (SDMA)
+ *   engine; hold until link_ns[i] after the start (the modelled time on the
+ *   link) and after the copy; record stamps[2i+1] = completion.
+ *   done: device [R] flags written by fo_gemm_rs / fo_gemm_rs_reduce /
+ *   fo_gemm_rs_ring; dst, src, bytes, chunk_id, link_ns: host [count];
+ *   stamps: device [2*count] (device wall-clock ticks), required.
+ * Errors: NULL, SHAPE (count < 0), SCHEDULE (epoch 0, chunk id out of range,
+ * negative link time), HIP. */
+fo_status fo_emulate_sends(const uint32_t *done, uint32_t epoch, void *const *dst,
+                           const void *const *src, const size_t *bytes, const int32_t *chunk_id,
+                           const int64_t *link_ns, int32_t count, uint64_t timeout_ns,
+                           int32_t *status, uint64_t *stamps, void *stream);
+
 /* Schedule model for fo_ag_gemm (host only; euno.news "Methodology" step 3:
  * the scheduler models the dependency graph of pieces and sub-tasks;
  * technical summary §2: work on incoming data first, the local slice last).

@@ -30,7 +30,7 @@ FO_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("fo_workspace_bytes", "fo_ag_gemm", "fo_ag_gemm_noalloc", "fo_a2a_gemm", "fo_qsa_workspace_bytes", "fo_qsa_attention",
            "fo_gemm_rs", "fo_gemm_rs_reduce", "fo_gemm_rs_ring", "fo_chunk_reduce",
-           "fo_emulate_arrivals", "fo_emulate_arrivals_gated", "fo_plan_ag_schedule", "fo_device_info", "fo_status_string",
+           "fo_emulate_arrivals", "fo_emulate_arrivals_gated", "fo_emulate_sends", "fo_plan_ag_schedule", "fo_device_info", "fo_status_string",
            "fo_last_hip_error")
 
 
@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.fo_emulate_arrivals.argtypes = [P, P, P, P, P, P, i32, P, u32, P, P]
     L.fo_emulate_arrivals_gated.restype = i32
     L.fo_emulate_arrivals_gated.argtypes = [P, ctypes.c_uint64, P, P, P, P, P, P, i32, P, u32, P, P]
+    L.fo_emulate_sends.restype = i32
+    L.fo_emulate_sends.argtypes = [P, u32, P, P, P, P, P, i32, ctypes.c_uint64, P, P, P]
     L.fo_plan_ag_schedule.restype = i32
     L.fo_plan_ag_schedule.argtypes = [i64, i64, i64, i32, i32, P, ctypes.c_double, i32, P, P, P]
     L.fo_device_info.restype = i32
@@ -362,4 +364,22 @@ def fo_emulate_arrivals(dsts, srcs, release_ns, chunk_ids, arrived, epoch, stamp
         st = lib().fo_emulate_arrivals_gated(_ptr(gate), int(gate_timeout_ns), d, s, b, iss, rel, cid, cnt,
                                              _ptr(arrived), epoch, _ptr(stamps), _stream(stream))
         _check(st, "fo_emulate_arrivals_gated")
+    return st
+
+
+def fo_emulate_sends(done, epoch, dsts, srcs, chunk_ids, link_ns, stamps, nbytes=None, timeout_ns=0, status=None,
+                     stream=None) -> int:
+    """Enqueue emulated sends of finished chunks (flag wait, SDMA copy, link
+    hold) on `stream`, one after another."""
+    cnt = len(dsts)
+    if nbytes is None:
+        nbytes = [t.numel() * t.element_size() for t in srcs]
+    d = (ctypes.c_void_p * cnt)(*[_ptr(t) for t in dsts])
+    s = (ctypes.c_void_p * cnt)(*[_ptr(t) for t in srcs])
+    b = (ctypes.c_size_t * cnt)(*[int(v) for v in nbytes])
+    cid = (ctypes.c_int32 * cnt)(*[int(v) for v in chunk_ids])
+    ln = (ctypes.c_int64 * cnt)(*[int(v) for v in link_ns])
+    st = lib().fo_emulate_sends(_ptr(done), int(epoch), d, s, b, cid, ln, cnt, int(timeout_ns), _ptr(status),
+                                _ptr(stamps), _stream(stream))
+    _check(st, "fo_emulate_sends")
     return st

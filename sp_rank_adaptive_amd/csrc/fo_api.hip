@@ -818,6 +818,32 @@ fo_status fo_emulate_arrivals_gated(const uint64_t *gate, uint64_t gate_timeout_
   return FO_OK;
 }
 
+fo_status fo_emulate_sends(const uint32_t *done, uint32_t epoch, void *const *dst, const void *const *src,
+                           const size_t *bytes, const int32_t *chunk_id, const int64_t *link_ns, int32_t count,
+                           uint64_t timeout_ns, int32_t *status, uint64_t *stamps, void *stream) {
+  if (count < 0) return FO_ERR_SHAPE;
+  if (count == 0) return FO_OK;
+  if (!done || !dst || !src || !bytes || !chunk_id || !link_ns || !stamps) return FO_ERR_NULL;
+  if (epoch == 0) return FO_ERR_SCHEDULE;
+  for (int i = 0; i < count; ++i) {
+    if (chunk_id[i] < 0 || chunk_id[i] >= FO_MAX_CHUNKS || link_ns[i] < 0) return FO_ERR_SCHEDULE;
+    if (bytes[i] && (!dst[i] || !src[i])) return FO_ERR_NULL;
+  }
+  const DevInfo *I = dev_info();
+  if (!I) return FO_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint64_t tmo = ns_to_ticks(timeout_ns ? timeout_ns : kDefaultTimeoutNs, I->wall_hz);
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < count && e == hipSuccess; ++i) {
+    e = launch_emu_wait_flag(done + chunk_id[i], epoch, tmo, status, stamps + 2 * i, st);
+    if (e == hipSuccess && bytes[i]) e = hipMemcpyAsync(dst[i], src[i], bytes[i], hipMemcpyDeviceToDeviceNoCU, st);
+    if (e == hipSuccess) e = launch_emu_hold(stamps + 2 * i, ns_to_ticks((uint64_t)link_ns[i], I->wall_hz),
+                                             stamps + 2 * i + 1, st);
+  }
+  if (e != hipSuccess) { record(e); return FO_ERR_HIP; }
+  return FO_OK;
+}
+
 fo_status fo_device_info(int32_t *num_cus, int32_t *lds_bytes_per_cu, uint64_t *wall_clock_hz) {
   const DevInfo *I = dev_info();
   if (!I) return FO_ERR_HIP;

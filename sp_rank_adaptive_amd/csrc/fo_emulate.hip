@@ -50,6 +50,48 @@ __global__ void __launch_bounds__(64) emu_flag_kernel(const uint64_t *t0_slot, u
   sleep_until(t0, next_issue_ticks);
 }
 
+// Send side: waits (bounded) until *flag shows the epoch (a chunk the
+// producer has finished), then records the start of the send in
+// *start_slot; a timeout writes FO_ERR_TIMEOUT to *status (if given) and
+// still records the stamp, so the stream moves on.
+__global__ void __launch_bounds__(64) emu_wait_flag_kernel(const uint32_t *flag, uint32_t epoch, uint64_t timeout_ticks,
+                                                           int32_t *status, uint64_t *start_slot) {
+  if (threadIdx.x != 0) return;
+  const uint64_t t0 = now_ticks();
+  while (!epoch_reached(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM), epoch)) {
+    if (now_ticks() - t0 > timeout_ticks) {
+      if (status) __hip_atomic_store(status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  // the flag's release ordered the producer's written-through rows before
+  // it; the copy engine reads them after this kernel ends (stream order)
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+  store_u64_relaxed(start_slot, now_ticks());
+}
+
+// Send side: holds the stream until `link_ticks` after *start_slot (the
+// modelled time the message occupies the link), then records the send's
+// completion in *done_slot.
+__global__ void __launch_bounds__(64) emu_hold_kernel(const uint64_t *start_slot, uint64_t link_ticks, uint64_t *done_slot) {
+  if (threadIdx.x != 0) return;
+  const uint64_t t0 = __hip_atomic_load(start_slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  sleep_until(t0, link_ticks);
+  store_u64_relaxed(done_slot, now_ticks());
+}
+
+hipError_t launch_emu_wait_flag(const uint32_t *flag, uint32_t epoch, uint64_t timeout_ticks, int32_t *status,
+                                uint64_t *start_slot, hipStream_t s) {
+  hipLaunchKernelGGL(emu_wait_flag_kernel, dim3(1), dim3(64), 0, s, flag, epoch, timeout_ticks, status, start_slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_emu_hold(const uint64_t *start_slot, uint64_t link_ticks, uint64_t *done_slot, hipStream_t s) {
+  hipLaunchKernelGGL(emu_hold_kernel, dim3(1), dim3(64), 0, s, start_slot, link_ticks, done_slot);
+  return hipGetLastError();
+}
+
 hipError_t launch_emu_start(uint64_t *t0_slot, uint64_t wait_ticks, const uint64_t *gate,
                             uint64_t gate_ticks, hipStream_t s) {
   hipLaunchKernelGGL(emu_start_kernel, dim3(1), dim3(64), 0, s, t0_slot, wait_ticks, gate, gate_ticks);

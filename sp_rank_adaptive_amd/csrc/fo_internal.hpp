@@ -172,6 +172,10 @@ hipError_t launch_emu_flag(const uint64_t *t0_slot, uint64_t release_ticks,
                            uint64_t next_issue_ticks, uint32_t *flag, uint32_t epoch,
                            uint64_t *stamp_slot, hipStream_t s);
 
+hipError_t launch_emu_wait_flag(const uint32_t *flag, uint32_t epoch, uint64_t timeout_ticks, int32_t *status,
+                                uint64_t *start_slot, hipStream_t s);
+hipError_t launch_emu_hold(const uint64_t *start_slot, uint64_t link_ticks, uint64_t *done_slot, hipStream_t s);
+
 int device_num_cus();
 uint64_t device_wall_hz();
 

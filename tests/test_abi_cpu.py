@@ -348,3 +348,24 @@ def test_qsa_validation(L):
     assert qa(s=s) == fo.FO_ERR_SCHEDULE
     s, keep = sched(R, order=[1, 1, 2, 3])
     assert qa(s=s) == fo.FO_ERR_ORDER
+
+
+def test_emulate_sends_validation(L):
+    P = ctypes.c_void_p
+    d = (P * 1)(A)
+    s = (P * 1)(A2)
+    b = (ctypes.c_size_t * 1)(64)
+    cid = (ctypes.c_int32 * 1)(1)
+    ln = (ctypes.c_int64 * 1)(1000)
+    es = L.fo_emulate_sends
+    assert es(A, 1, d, s, b, cid, ln, 0, 0, None, A, None) == fo.FO_OK          # nothing to do
+    assert es(A, 1, d, s, b, cid, ln, -1, 0, None, A, None) == fo.FO_ERR_SHAPE
+    assert es(None, 1, d, s, b, cid, ln, 1, 0, None, A, None) == fo.FO_ERR_NULL
+    assert es(A, 1, d, s, b, cid, ln, 1, 0, None, None, None) == fo.FO_ERR_NULL   # stamps required
+    assert es(A, 0, d, s, b, cid, ln, 1, 0, None, A, None) == fo.FO_ERR_SCHEDULE  # epoch 0
+    bad = (ctypes.c_int32 * 1)(64)
+    assert es(A, 1, d, s, b, bad, ln, 1, 0, None, A, None) == fo.FO_ERR_SCHEDULE
+    neg = (ctypes.c_int64 * 1)(-5)
+    assert es(A, 1, d, s, b, cid, neg, 1, 0, None, A, None) == fo.FO_ERR_SCHEDULE
+    nul = (P * 1)(None)
+    assert es(A, 1, nul, s, b, cid, ln, 1, 0, None, A, None) == fo.FO_ERR_NULL
