@@ -202,7 +202,7 @@ def _emulate(fo, dsts, srcs, order, nbytes, flags, e, es, side, link_bw, copy=Tr
 
 
 def measure_tail_ag(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LINK_BW, copy=True, split=None,
-                    spread=None, sub=1):
+                    spread=None, sub=1, order=None):
     """Exposed tail of the AG-GEMM under emulated ring arrivals (us): time
     from the last chunk's landing to the last output written.
       flashoverlap: one persistent launch, ready-first claims over the flags;
@@ -220,7 +220,7 @@ def measure_tail_ag(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LI
     x = staging.clone()
     y = torch.empty((cfg.m, cfg.n), device="cuda")
     if sub > 1:
-        return _tail_ag_sub(fo, cfg, hz, staging, x, w, y, sub, reps, link_bw, split, spread)
+        return _tail_ag_sub(fo, cfg, hz, staging, x, w, y, sub, reps, link_bw, split, spread, order)
     mc = cfg.m // cfg.R
     order = wl.ring_arrival_order(cfg.R, cfg.local)
     nbytes = mc * cfg.k * 2
@@ -306,11 +306,12 @@ def sub_chunk_schedule(R, local, sub, nbytes, link_bw=wl.LINK_BW):
     return peers + locals_, peers, rel, locals_
 
 
-def _tail_ag_sub(fo, cfg, hz, staging, x, w, y, sub, reps, link_bw, split, spread):
+def _tail_ag_sub(fo, cfg, hz, staging, x, w, y, sub, reps, link_bw, split, spread, order=None):
     import torch
     R2 = cfg.R * sub
     mc2 = cfg.m // R2
-    order, peers, rel, locals_ = sub_chunk_schedule(cfg.R, cfg.local, sub, (cfg.m // cfg.R) * cfg.k * 2, link_bw)
+    order0, peers, rel, locals_ = sub_chunk_schedule(cfg.R, cfg.local, sub, (cfg.m // cfg.R) * cfg.k * 2, link_bw)
+    order = order0 if order is None else order
     nb2 = mc2 * cfg.k * 2
     iss = [r - nb2 / link_bw * 1e9 for r in rel]
     flags = torch.zeros(R2, dtype=torch.int32, device="cuda")
@@ -1053,6 +1054,23 @@ def main():
             row["planned_p10_p90_us"] = [sp["p10"], sp["p90"]]
             row["planned_tail_over_chunk_gemm_at_70pct"] = round(t / at70, 3)
             row["planned_tail_over_chunk_gemm"] = round(t / cg, 3)
+            # the streamed schedule: the model, calibrated on this shape's
+            # measured all-present launch and lone chunk, chooses how many
+            # messages each peer chunk is sent in and the last piece's split
+            all_us = launches["ag_gemm"][1] * 1e3 if cfg is c2 else gemm_rate(fo, cfg)[1] * 1e3
+            cal = fo.fo_plan_calibrate(cfg.m, cfg.n, cfg.k, cfg.R, all_us * 1e3, cg_per[1] * 1e3, 0.0)
+            sub, s_order, s_split, s_pred = fo.fo_plan_ag_stream(cfg.m, cfg.n, cfg.k, cfg.R, cfg.local,
+                                                                  wl.LINK_BW / 1e9, fo.FO_LINK_RING, calib=cal)
+            sp = {}
+            t, _ = measure_tail_ag(fo, cfg, hz, "flashoverlap", split=s_split, spread=sp, sub=sub, order=s_order)
+            last_piece = s_order[cfg.R * sub - sub - 1]
+            pred_end = min(v for v in s_pred[[1, 2, 4, 8].index(sub)] if v > 0)
+            row["streamed"] = {"messages_per_chunk": sub, "last_piece_split": s_split[last_piece],
+                               "tail_us": round(t, 2), "p10_p90_us": [sp["p10"], sp["p90"]],
+                               "predicted_tail_us": round(pred_end / 1e3 - row["last_arrival_us"], 2),
+                               "tail_over_chunk_gemm_at_70pct": round(t / at70, 3),
+                               "calibration": {"gemm_tflops": round(cal.gemm_tflops, 1),
+                                               "alone_speedup": round(cal.alone_speedup, 3)}}
             tails[key] = row
             log(f"tail {key}: {row}")
         row = {}

@@ -402,6 +402,80 @@ fo_status fo_plan_ag_schedule(int64_t m, int64_t n, int64_t k, int32_t nchunks, 
                               int32_t num_workgroups, int32_t *order_out, int32_t *split_out,
                               int64_t *predicted_ns);
 
+/* Calibration of the schedule model: measured facts of a launch shape on the
+ * device.  Fields <= 0 take the defaults (measured on MI355X on the TP=8 MLP
+ * up-projection share): 900 TFLOP/s, alone speed-up 1.8, 5 us from a flag
+ * store to a claim walk's first unit, 2 us to a held unit's first loads,
+ * 1.5 us of claim and bookkeeping per unit, 5 TB/s of HBM for the reduce. */
+typedef struct fo_plan_calib {
+  double gemm_tflops;         /* launch rate with every workgroup busy          */
+  double alone_speedup;       /* a workgroup alone vs its share of a busy GPU   */
+  double flag_latency_ns;     /* flag store -> first unit by a claim walk       */
+  double reserve_latency_ns;  /* flag store -> first loads of a held unit       */
+  double unit_fixed_ns;       /* claim and bookkeeping per unit                 */
+  double hbm_gbps;            /* HBM rate of the reduce passes (bytes per ns)   */
+} fo_plan_calib;
+
+/* Calibrates the schedule model for an m x n x k AG-GEMM in R chunks from
+ * measured launches (euno.news "Methodology" step 3; "Limitations": the
+ * model assumes uniform links, so it is fitted per shape and device):
+ *   all_present_ns   one launch with every chunk landed (required, > 4 us);
+ *   chunk_alone_ns   one chunk's rows alone, unsplit (<= 0: keep default
+ *                    alone speed-up);
+ *   tail_unsplit_ns  measured exposed tail with the last chunk unsplit and
+ *                    the GPU idle when it lands (<= 0: keep default latency).
+ * Host only; num_workgroups <= 0 asks the current device for its CUs.
+ * Errors: NULL, SHAPE, SCHEDULE, HIP. */
+fo_status fo_plan_calibrate(int64_t m, int64_t n, int64_t k, int32_t nchunks, double all_present_ns,
+                            double chunk_alone_ns, double tail_unsplit_ns, int32_t num_workgroups,
+                            fo_plan_calib *out);
+
+/* Link model (host only): when each message of the decomposed all-gather
+ * lands, for chunks of chunk_bytes over links of link_gbps (bytes per ns),
+ * each peer chunk streamed as `sub` messages.
+ *   FO_LINK_RING  one incoming link: the chunk of ring distance d is sent in
+ *                 [(d-1) T, d T] with T = chunk_bytes / link_gbps;
+ *   FO_LINK_MESH  one link per peer: every peer sends in [0, T].
+ * Message j of chunk c lands at the start of its chunk's window plus
+ * (j + 1) T / sub.  arrival_ns: host [R * sub], message c * sub + j; the
+ * local chunk's entries are 0.  Errors: NULL, SHAPE (R * sub > 64),
+ * SCHEDULE. */
+enum { FO_LINK_RING = 0, FO_LINK_MESH = 1 };
+fo_status fo_plan_link_arrivals(int32_t nchunks, int32_t local, int64_t chunk_bytes, double link_gbps,
+                                int32_t topology, int32_t sub, int64_t *arrival_ns);
+
+/* Streamed schedule for fo_ag_gemm (host only): chooses how many messages
+ * (1, 2, 4 or 8) each peer chunk of the AG-GEMM is streamed in, and the
+ * split of the piece that lands last, by the earliest predicted completion
+ * under the link model (more messages only when they win by more than
+ * 0.5 us: small pieces cost more per unit).  With sub messages the launch
+ * takes R * sub chunks of m / (R * sub) rows (piece c * sub + j = rows of
+ * message j of chunk c); the local chunk's pieces are present (flag them,
+ * and pass any one of them as local).
+ *   calib           NULL or a calibration (fo_plan_calibrate).
+ *   sub_out         the chosen number of messages per chunk.
+ *   order_out, split_out  host [64]: the first R * sub entries are the
+ *                   priority order and split vector for fo_schedule.
+ *   predicted_ns    host [16], optional: completion predicted for messages
+ *                   {1, 2, 4, 8} x split {1, 2, 4, 8} (row-major; -1 where
+ *                   not possible).
+ * Errors: NULL, SHAPE, SCHEDULE, HIP (no device when num_workgroups <= 0). */
+fo_status fo_plan_ag_stream(int64_t m, int64_t n, int64_t k, int32_t nchunks, int32_t local,
+                            double link_gbps, int32_t topology, const fo_plan_calib *calib,
+                            int32_t num_workgroups, int32_t *sub_out, int32_t *order_out,
+                            int32_t *split_out, int64_t *predicted_ns);
+
+/* Reduce-scatter form (host only; technical summary §2, Flash-RS): given
+ * when each peer's fp32 partial for the local chunk lands (arrival_ns host
+ * [R], the local entry ignored), predicts when the bf16 shard is complete
+ * for GEMM-RS then fo_chunk_reduce (0), fo_gemm_rs_reduce (1) and
+ * fo_gemm_rs_ring with the accumulated partial landing last (2), and picks
+ * the earliest (a later form only if it wins by more than 0.5 us).
+ * predicted_ns host [3], optional.  Errors: NULL, SHAPE, SCHEDULE, HIP. */
+fo_status fo_plan_rs_form(int64_t m, int64_t n, int64_t k, int32_t nchunks, int32_t local,
+                          const int64_t *arrival_ns, const fo_plan_calib *calib, int32_t num_workgroups,
+                          int32_t *form_out, int64_t *predicted_ns);
+
 /* Device facts used to interpret stamps and size launches. */
 fo_status fo_device_info(int32_t *num_cus, int32_t *lds_bytes_per_cu,
                          uint64_t *wall_clock_hz);

@@ -24,13 +24,15 @@ FO_ERR_ORDER, FO_ERR_SCHEDULE, FO_ERR_WORKSPACE, FO_ERR_HIP = 5, 6, 7, 8
 FO_ERR_TIMEOUT, FO_ERR_ALIAS = 9, 10
 FO_F32, FO_BF16 = 0, 1
 FO_SCHED_READY_FIRST, FO_SCHED_STRICT = 0, 1
+FO_LINK_RING, FO_LINK_MESH = 0, 1
 FO_MAX_CHUNKS = 64
 
 FO_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("fo_workspace_bytes", "fo_ag_gemm", "fo_ag_gemm_noalloc", "fo_a2a_gemm", "fo_qsa_workspace_bytes", "fo_qsa_attention",
            "fo_gemm_rs", "fo_gemm_rs_reduce", "fo_gemm_rs_ring", "fo_chunk_reduce",
-           "fo_emulate_arrivals", "fo_emulate_arrivals_gated", "fo_emulate_sends", "fo_plan_ag_schedule", "fo_device_info", "fo_status_string",
+           "fo_emulate_arrivals", "fo_emulate_arrivals_gated", "fo_emulate_sends", "fo_plan_ag_schedule", "fo_plan_calibrate", "fo_plan_link_arrivals",
+           "fo_plan_ag_stream", "fo_plan_rs_form", "fo_device_info", "fo_status_string",
            "fo_last_hip_error")
 
 
@@ -57,6 +59,18 @@ class _Sched(ctypes.Structure):
         ("split", ctypes.POINTER(ctypes.c_int32)),
         ("max_workgroups", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
+    ]
+
+
+class PlanCalib(ctypes.Structure):
+    """struct fo_plan_calib: measured facts of a launch shape (<= 0: default)."""
+    _fields_ = [
+        ("gemm_tflops", ctypes.c_double),
+        ("alone_speedup", ctypes.c_double),
+        ("flag_latency_ns", ctypes.c_double),
+        ("reserve_latency_ns", ctypes.c_double),
+        ("unit_fixed_ns", ctypes.c_double),
+        ("hbm_gbps", ctypes.c_double),
     ]
 
 
@@ -101,6 +115,16 @@ def lib() -> ctypes.CDLL:
     L.fo_emulate_sends.argtypes = [P, u32, P, P, P, P, P, i32, ctypes.c_uint64, P, P, P]
     L.fo_plan_ag_schedule.restype = i32
     L.fo_plan_ag_schedule.argtypes = [i64, i64, i64, i32, i32, P, ctypes.c_double, i32, P, P, P]
+    L.fo_plan_calibrate.restype = i32
+    L.fo_plan_calibrate.argtypes = [i64, i64, i64, i32, ctypes.c_double, ctypes.c_double, ctypes.c_double, i32,
+                                    ctypes.POINTER(PlanCalib)]
+    L.fo_plan_link_arrivals.restype = i32
+    L.fo_plan_link_arrivals.argtypes = [i32, i32, i64, ctypes.c_double, i32, i32, P]
+    L.fo_plan_ag_stream.restype = i32
+    L.fo_plan_ag_stream.argtypes = [i64, i64, i64, i32, i32, ctypes.c_double, i32, ctypes.POINTER(PlanCalib), i32,
+                                    P, P, P, P]
+    L.fo_plan_rs_form.restype = i32
+    L.fo_plan_rs_form.argtypes = [i64, i64, i64, i32, i32, P, ctypes.POINTER(PlanCalib), i32, P, P]
     L.fo_device_info.restype = i32
     L.fo_device_info.argtypes = [P, P, P]
     L.fo_status_string.restype = ctypes.c_char_p
@@ -195,6 +219,51 @@ def fo_plan_ag_schedule(m, n, k, nchunks, local, arrival_ns, gemm_tflops=0.0, nu
     _check(lib().fo_plan_ag_schedule(int(m), int(n), int(k), R, int(local), arr, float(gemm_tflops),
                                      int(num_workgroups), order, split, pred), "fo_plan_ag_schedule")
     return list(order), list(split), list(pred)
+
+
+def fo_plan_calibrate(m, n, k, nchunks, all_present_ns, chunk_alone_ns=0.0, tail_unsplit_ns=0.0,
+                      num_workgroups=0) -> PlanCalib:
+    """Calibration of the schedule model from measured launches."""
+    out = PlanCalib()
+    _check(lib().fo_plan_calibrate(int(m), int(n), int(k), int(nchunks), float(all_present_ns), float(chunk_alone_ns),
+                                   float(tail_unsplit_ns), int(num_workgroups), ctypes.byref(out)),
+           "fo_plan_calibrate")
+    return out
+
+
+def fo_plan_link_arrivals(nchunks, local, chunk_bytes, link_gbps, topology=FO_LINK_RING, sub=1):
+    """Landing time (ns) of every message c * sub + j (0 for the local chunk)."""
+    arr = (ctypes.c_int64 * (int(nchunks) * int(sub)))()
+    _check(lib().fo_plan_link_arrivals(int(nchunks), int(local), int(chunk_bytes), float(link_gbps), int(topology),
+                                       int(sub), arr), "fo_plan_link_arrivals")
+    return list(arr)
+
+
+def fo_plan_ag_stream(m, n, k, nchunks, local, link_gbps, topology=FO_LINK_RING, calib=None, num_workgroups=0):
+    """(sub, order, split, predicted): messages per peer chunk, and the order
+    and split vector over the R * sub pieces; predicted[i][j] = completion
+    with (1, 2, 4, 8)[i] messages and the last piece split (1, 2, 4, 8)[j]."""
+    sub = ctypes.c_int32()
+    order = (ctypes.c_int32 * FO_MAX_CHUNKS)()
+    split = (ctypes.c_int32 * FO_MAX_CHUNKS)()
+    pred = (ctypes.c_int64 * 16)()
+    _check(lib().fo_plan_ag_stream(int(m), int(n), int(k), int(nchunks), int(local), float(link_gbps), int(topology),
+                                   None if calib is None else ctypes.byref(calib), int(num_workgroups),
+                                   ctypes.byref(sub), order, split, pred), "fo_plan_ag_stream")
+    r2 = int(nchunks) * sub.value
+    return sub.value, list(order)[:r2], list(split)[:r2], [list(pred)[4 * i:4 * i + 4] for i in range(4)]
+
+
+def fo_plan_rs_form(m, n, k, nchunks, local, arrival_ns, calib=None, num_workgroups=0):
+    """(form, predicted): 0 GEMM-RS then reduce, 1 fused, 2 ring."""
+    R = int(nchunks)
+    arr = (ctypes.c_int64 * R)(*[int(v) for v in arrival_ns])
+    form = ctypes.c_int32()
+    pred = (ctypes.c_int64 * 3)()
+    _check(lib().fo_plan_rs_form(int(m), int(n), int(k), R, int(local), arr,
+                                 None if calib is None else ctypes.byref(calib), int(num_workgroups),
+                                 ctypes.byref(form), pred), "fo_plan_rs_form")
+    return form.value, list(pred)
 
 
 def fo_device_info():

@@ -342,3 +342,51 @@ def test_dp_reduce_full_int(fo, orc):
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     check_exact(host(d[local]), ref, "cfg4 emulated")
+
+
+def test_tp8_mlp_ag_streamed_planned_schedule_int(fo, orc):
+    """The schedule model's streamed plan at 50 GB/s ring links: each peer
+    chunk sent as `sub` messages (pieces of m / (R * sub) rows) landing by
+    SDMA into poisoned rows, the local pieces present, the plan's order and
+    split: every element exact, and again with every chunk sent as 8."""
+    c = wl.CFG2
+    xb, wb, ref = int_case(orc, c)
+    plans = [fo.fo_plan_ag_stream(c.m, c.n, c.k, c.R, c.local, 50.0, fo.FO_LINK_RING)[:3]]
+    sub8 = 8
+    land8 = fo.fo_plan_link_arrivals(c.R, c.local, c.m // c.R * c.k * 2, 50.0, fo.FO_LINK_RING, sub8)
+    peers8 = sorted((p for p in range(c.R * sub8) if p // sub8 != c.local), key=lambda p: land8[p])
+    split8 = [1] * (c.R * sub8)
+    split8[peers8[-1]] = 8
+    plans.append((sub8, peers8 + [c.local * sub8 + j for j in range(sub8)], split8))
+    for sub, order, split in plans:
+        R2 = c.R * sub
+        mc2 = c.m // R2
+        land = fo.fo_plan_link_arrivals(c.R, c.local, c.m // c.R * c.k * 2, 50.0, fo.FO_LINK_RING, sub)
+        locals_ = [c.local * sub + j for j in range(sub)]
+        peers = [p for p in order if p not in locals_]
+        staging = dev_bf16(xb)
+        w = dev_bf16(wb)
+        x = staging.clone()
+        for p in peers:
+            x[p * mc2:(p + 1) * mc2].fill_(float("nan"))
+        flags = torch.zeros(R2, dtype=torch.int32, device="cuda")
+        e = epoch()
+        flags[locals_] = e
+        es = torch.zeros(R2 + 2, dtype=torch.int64, device="cuda")
+        gs = torch.zeros(2 * R2 + 2, dtype=torch.int64, device="cuda")
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        ws = torch.zeros(fo.fo_workspace_bytes(c.m, c.n, c.k, R2), dtype=torch.uint8, device="cuda")
+        y = torch.full((c.m, c.n), float("nan"), device="cuda")
+        torch.cuda.synchronize()
+        log(f"case: cfg2 int streamed in {sub} messages, last piece split {max(split)}")
+        side = side_stream()
+        with torch.cuda.stream(side):
+            fo.fo_emulate_arrivals([x[p * mc2:(p + 1) * mc2] for p in peers], [staging[p * mc2:(p + 1) * mc2] for p in peers],
+                                   [land[p] for p in peers], peers, flags, e, es, stream=side, gate=gs[2 * R2:2 * R2 + 1])
+        fo.fo_ag_gemm(x, w, y, fo.Schedule(nchunks=R2, local=locals_[0], order=order, arrived=flags, epoch=e,
+                                           stamps=gs, status=status, split=split, timeout_ns=5_000_000_000), ws)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        assert int(ws[:4096].sum()) == 0
+        check_exact(host(y), ref, f"streamed in {sub}")
+        del x, y, staging

@@ -138,3 +138,104 @@ def test_long_sequence_share_at_slow_links():
     o, split, pred = fo.fo_plan_ag_schedule(cfg.m, cfg.n, cfg.k, cfg.R, cfg.local, arr, num_workgroups=GRID)
     assert o == order + [cfg.local]
     assert split[order[-1]] == 8 and chosen_is_earliest(8, pred)
+
+
+# ---- link model, streamed schedules, calibration, reduce-scatter form -------
+
+def test_link_arrivals_ring_and_mesh():
+    R, local, nbytes, bw = 8, 3, 4 << 20, 50.0          # 50 bytes per ns
+    T = nbytes / bw
+    ring = fo.fo_plan_link_arrivals(R, local, nbytes, bw, fo.FO_LINK_RING, 1)
+    for d in range(1, R):
+        c = (local - d) % R
+        assert abs(ring[c] - d * T) <= 1
+    assert ring[local] == 0
+    mesh = fo.fo_plan_link_arrivals(R, local, nbytes, bw, fo.FO_LINK_MESH, 1)
+    assert all(abs(mesh[c] - T) <= 1 for c in range(R) if c != local)
+    # streamed: the last message of a chunk lands when the whole chunk would
+    # have, the others evenly before it, in order
+    sub = 4
+    s = fo.fo_plan_link_arrivals(R, local, nbytes, bw, fo.FO_LINK_RING, sub)
+    for c in range(R):
+        if c == local:
+            assert s[c * sub:(c + 1) * sub] == [0] * sub
+            continue
+        pieces = s[c * sub:(c + 1) * sub]
+        assert abs(pieces[-1] - ring[c]) <= 1
+        assert all(b - a > 0 and abs((b - a) - T / sub) <= 2 for a, b in zip(pieces, pieces[1:]))
+    with pytest.raises(fo.FoError):
+        fo.fo_plan_link_arrivals(R, local, nbytes, bw, 7, 1)
+    with pytest.raises(fo.FoError):
+        fo.fo_plan_link_arrivals(16, 0, nbytes, bw, fo.FO_LINK_RING, 8)     # 128 pieces
+
+
+@pytest.mark.parametrize("bw", [50, 153, 400, 1000])
+@pytest.mark.parametrize("topo", [0, 1])
+def test_stream_plan_is_a_valid_schedule(bw, topo):
+    c = CFG2
+    sub, order, split, pred = fo.fo_plan_ag_stream(c.m, c.n, c.k, c.R, c.local, bw, topo, num_workgroups=GRID)
+    R2 = c.R * sub
+    assert sub in (1, 2, 4, 8)
+    assert sorted(order) == list(range(R2)) and len(split) == R2
+    local_pieces = list(range(c.local * sub, (c.local + 1) * sub))
+    assert order[-sub:] == local_pieces                        # the local pieces last
+    last = order[R2 - sub - 1]                                 # the piece that lands last
+    assert all(sp == 1 for p, sp in enumerate(split) if p != last)
+    # the pieces by landing time, as the link model delivers them
+    land = fo.fo_plan_link_arrivals(c.R, c.local, c.m // c.R * c.k * 2, bw, topo, sub)
+    t = [land[p] for p in order[:R2 - sub]]
+    assert t == sorted(t)
+    # the chosen schedule has the earliest prediction, up to the margins
+    chosen = pred[[1, 2, 4, 8].index(sub)][[1, 2, 4, 8].index(split[last])]
+    best = min(p for row in pred for p in row if p > 0)
+    assert 0 < chosen <= best + 1000
+
+
+def test_stream_plan_streams_on_slow_links_and_rows_must_allow_it():
+    c = CFG2
+    sub, _, _, pred = fo.fo_plan_ag_stream(c.m, c.n, c.k, c.R, c.local, 50, fo.FO_LINK_RING, num_workgroups=GRID)
+    assert sub > 1, "at 50 GB/s the GPU is idle at the last landing: streaming the chunks pays"
+    assert min(p for p in pred[[1, 2, 4, 8].index(sub)] if p > 0) < min(p for p in pred[0] if p > 0)
+    q = wl.CFG5                                                 # 16 chunks: 8 messages would need 128 pieces
+    _, _, _, pred5 = fo.fo_plan_ag_stream(q.m, q.n, q.k, q.R, q.local, 50, fo.FO_LINK_RING, num_workgroups=GRID)
+    assert pred5[3] == [-1, -1, -1, -1]
+    # one chunk cannot be streamed (nothing lands)
+    sub1, order1, split1, _ = fo.fo_plan_ag_stream(512, 256, 512, 1, 0, 50, fo.FO_LINK_RING, num_workgroups=GRID)
+    assert sub1 == 1 and order1 == [0] and split1 == [1]
+
+
+def test_calibration_from_measured_launches():
+    c = CFG2
+    cal = fo.fo_plan_calibrate(c.m, c.n, c.k, c.R, 64_000, 58_000, 30_000, GRID)
+    # the rate is the launch's flops over its time less start and end (4 us)
+    assert abs(cal.gemm_tflops - 2.0 * c.m * c.n * c.k / 60_000 / 1e3) < 1e-6
+    assert 1.0 <= cal.alone_speedup <= 4.0
+    assert cal.reserve_latency_ns >= 200
+    # a slower measured launch calibrates a lower rate, and the model then
+    # predicts later completions
+    slow = fo.fo_plan_calibrate(c.m, c.n, c.k, c.R, 128_000, 0, 0, GRID)
+    assert slow.gemm_tflops < cal.gemm_tflops
+    _, _, _, p_fast = fo.fo_plan_ag_stream(c.m, c.n, c.k, c.R, 0, 1000, fo.FO_LINK_RING, calib=cal,
+                                           num_workgroups=GRID)
+    _, _, _, p_slow = fo.fo_plan_ag_stream(c.m, c.n, c.k, c.R, 0, 1000, fo.FO_LINK_RING, calib=slow,
+                                           num_workgroups=GRID)
+    assert p_slow[0][0] > p_fast[0][0]
+    with pytest.raises(fo.FoError):
+        fo.fo_plan_calibrate(c.m, c.n, c.k, c.R, 1000, 0, 0, GRID)      # shorter than a launch's start
+
+
+def test_rs_form_choice_follows_the_landings():
+    c = wl.CFG3
+    part_ns_50 = (c.m // c.R) * c.n * 4 / 50            # one partial at 50 GB/s
+    slow = [0] + [int(part_ns_50 * d) for d in range(c.R - 1, 0, -1)]
+    form, pred = fo.fo_plan_rs_form(c.m, c.n, c.k, c.R, 0, slow, num_workgroups=GRID)
+    # every form ends after the last landing
+    assert all(p > max(slow) for p in pred)
+    # fast links: the partials land during the GEMM, and the ring form adds a
+    # single partial after it, so it is predicted first
+    fast = [0] + [int(part_ns_50 / 20 * d) for d in range(c.R - 1, 0, -1)]
+    form2, pred2 = fo.fo_plan_rs_form(c.m, c.n, c.k, c.R, 0, fast, num_workgroups=GRID)
+    assert form2 == 2 and pred2[2] < pred2[0]
+    assert pred2[1] <= pred2[0]                          # the fused form never waits for a second launch
+    with pytest.raises(fo.FoError):
+        fo.fo_plan_rs_form(c.m, c.n, c.k, c.R, 9, fast, num_workgroups=GRID)
