@@ -18,7 +18,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int RT = 256;  // threads per workgroup
-constexpr int RU = 2;    // vectors per thread per step
+constexpr int RU = 8;    // vectors per thread per step (128 bytes of each source in flight per lane)
 constexpr int KB = 8;    // sources whose loads are issued together
 
 // 16 bytes of a source that a copy engine wrote after this grid started, read
