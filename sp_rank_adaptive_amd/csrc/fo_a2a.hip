@@ -308,16 +308,24 @@ a2a_kernel(A2aArgs a) {
   }
 
   // Completion stamp: the workgroup that finishes the last tile records it.
-  // The last workgroup to leave returns the counters to zero.
+  // The last workgroup to leave returns the counters to zero; the exits are
+  // counted per XCD, then per XCD group, so they do not queue on one
+  // counter.  Without flags and stamps no counter is touched and nothing is
+  // counted.
   __syncthreads();
-  if (tid == 0) {
+  if (tid == 0 && (a.stamps || a.arrived)) {
     if (a.stamps && done_tiles > 0) {
       const int total = a.tiles_m * a.tiles_n;
       const uint32_t t = fetch_add_relaxed(a.ws32 + WS_TOTAL_DONE, (uint32_t)done_tiles);
       if ((int)(t + done_tiles) == total) store_u64_relaxed(a.stamps + 2 * a.P + 1, now_ticks());
     }
-    const uint32_t e = fetch_add_relaxed(a.ws32 + WS_EXITED, 1u);
-    if (e == (uint32_t)(a.grid - 1)) {
+    const int xcd = (int)(blockIdx.x % XCDS);
+    const int on_xcd = (a.grid - xcd + XCDS - 1) / XCDS;
+    const int xcds = a.grid < XCDS ? a.grid : XCDS;
+    bool last = fetch_add_relaxed(a.ws32 + WS_EXITED_X + xcd, 1u) == (uint32_t)(on_xcd - 1);
+    if (last) last = fetch_add_relaxed(a.ws32 + WS_EXITED, 1u) == (uint32_t)(xcds - 1);
+    if (last) {
+      for (int g = 0; g < XCDS; ++g) store_relaxed_agent(a.ws32 + WS_EXITED_X + g, 0u);
       store_relaxed_agent(a.ws32 + WS_TOTAL_DONE, 0u);
       store_relaxed_agent(a.ws32 + WS_ABORT, 0u);
       store_relaxed_agent(a.ws32 + WS_EXITED, 0u);

@@ -378,6 +378,9 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
     // claiming until no work is left.
     a.one_unit = (a.arrived != nullptr && ok && single) ? 1 : 0;
   }
+  // A launch whose claims are all static, with no reduce units, flags or
+  // stamps, touches no counter: its workgroups skip the exit count too.
+  a.no_counters = (a.static_rr != 0 && !fz && !done && !s->stamps) ? 1 : 0;
   if (fz) {
     // shard units are assigned statically (workgroup b takes b, b + grid,
     // ... of each chunk with shard units, in priority order) only when every

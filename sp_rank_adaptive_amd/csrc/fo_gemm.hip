@@ -1056,10 +1056,18 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
   // its exit; the last workgroup issues the resets after its own count has
   // returned.  No cache maintenance is needed, and none is paid: a release
   // fence here would write back the XCD's L2 once per workgroup.
-  if (tid == 0) {
-    const uint32_t e = fetch_add_relaxed(a.ws32 + WS_EXITED, 1u);
-    if (e == (uint32_t)(a.grid - 1)) {
+  // The count goes in two levels (the workgroups of each XCD, then the XCDs)
+  // so the exits do not queue on one counter; a launch that touched no
+  // counter (static claims only, no flags, stamps or reduce units) skips it.
+  if (tid == 0 && !a.no_counters) {
+    const int xcd = (int)(blockIdx.x % XCDS);
+    const int on_xcd = (a.grid - xcd + XCDS - 1) / XCDS;
+    const int xcds = a.grid < XCDS ? a.grid : XCDS;
+    bool last = fetch_add_relaxed(a.ws32 + WS_EXITED_X + xcd, 1u) == (uint32_t)(on_xcd - 1);
+    if (last) last = fetch_add_relaxed(a.ws32 + WS_EXITED, 1u) == (uint32_t)(xcds - 1);
+    if (last) {
       uint32_t *W = a.ws32;
+      for (int g = 0; g < XCDS; ++g) store_relaxed_agent(W + WS_EXITED_X + g, 0u);
       for (int c = 0; c < a.R; ++c) {
         for (int g = 0; g < XCDS; ++g) store_relaxed_agent(W + WS_CLAIM + c * XCDS + g, 0u);
         store_relaxed_agent(W + WS_CHUNK_DONE + c, 0u);

@@ -17,6 +17,7 @@ constexpr int WS_CHUNK_DONE = 512;           // [FO_MAX_CHUNKS] finished units p
 constexpr int WS_TOTAL_DONE = 576;           // finished units, all chunks
 constexpr int WS_EXITED = 577;               // workgroups that have left the loop
 constexpr int WS_ABORT = 578;                // set when a wait timed out
+constexpr int WS_EXITED_X = 584;             // [XCDS] workgroups of each XCD that have left the loop
 constexpr int WS_RED_CLAIM = 640;            // [FO_MAX_CHUNKS] reduce units claimed
 constexpr int WS_RED_READY = 704;            // [FO_MAX_CHUNKS] split tiles published
 constexpr int WS_TILE_CTR = 1024;            // split-K arrival counters, one per tile,
@@ -29,6 +30,8 @@ struct TileCfg {
   int bm, bn, stages;
 };
 
+// Arrays the first claim and the unit set-up read start on their own
+// 64-byte lines, so the first entries of each come in with one line.
 struct GemmArgs {
   const uint16_t *x;          // bf16 [m][k]
   const uint16_t *w;          // bf16 [n][k]
@@ -45,6 +48,7 @@ struct GemmArgs {
   int32_t total_units;
   int32_t grid;
   int32_t static_rr;          // every unit assigned statically: 1 round-robin per XCD, 2 one per workgroup
+  int32_t no_counters;        // static claims, no reduce units, no flags or stamps: no counter is touched
   int32_t all_unsplit;        // 1: no chunk is split
   int32_t one_unit;           // flags: a workgroup whose first claim succeeds leaves after it
   // Fused reduce of the local chunk (fo_gemm_rs_reduce): the local chunk's
@@ -62,7 +66,7 @@ struct GemmArgs {
   const uint32_t *inc_arrived;        // device [R] flags of the incoming partials, or null
   const float *inc[FO_MAX_CHUNKS];    // incoming partials [mc][n] fp32
   int32_t inc_chunk[FO_MAX_CHUNKS];   // chunk id of inc[i] (its flag)
-  int32_t gunits[XCDS];       // units per work-queue group over all chunks
+  alignas(64) int32_t gunits[XCDS];       // units per work-queue group over all chunks
   const uint32_t *arrived;    // device [R] or null
   uint32_t *done_flags;       // device [R] or null
   uint32_t epoch;
@@ -71,12 +75,12 @@ struct GemmArgs {
   uint64_t *stamps;
   uint32_t *ws32;             // counters
   float *partials;            // split-K partial tiles
-  int32_t order[FO_MAX_CHUNKS];
-  int32_t split[FO_MAX_CHUNKS];
-  int32_t units[FO_MAX_CHUNKS];     // tiles * split
+  alignas(64) int32_t order[FO_MAX_CHUNKS];
+  alignas(64) int32_t split[FO_MAX_CHUNKS];
+  alignas(64) int32_t units[FO_MAX_CHUNKS];     // tiles * split
   int32_t ctr_base[FO_MAX_CHUNKS];  // split chunk: first tile counter / ready slot; -1 if unsplit
   int32_t part_base[FO_MAX_CHUNKS]; // split chunk: first partial tile (tile*S + split)
-  int32_t kslice[FO_MAX_CHUNKS];    // k extent of one split (multiple of 64)
+  alignas(64) int32_t kslice[FO_MAX_CHUNKS];    // k extent of one split (multiple of 64)
   int32_t red_units[FO_MAX_CHUNKS]; // split chunk: tiles * RED_SLICES reduce units, else 0
   int32_t ready_off;                // word offset of the ready lists (after the tile counters)
 };

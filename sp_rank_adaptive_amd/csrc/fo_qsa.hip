@@ -52,7 +52,7 @@ constexpr int VT_TILE = QSA_D * VT_ROWB;           // 18 KiB
 constexpr int K_STAGES = 3;                        // key tiles in the LDS ring
 constexpr int QS_LDS = K_STAGES * K_TILE + VT_TILE;
 constexpr int SLOT_FLOATS = QSA_BQ * QSA_D + 2 * QSA_BQ;   // O [BQ][d], m [BQ], l [BQ]
-constexpr int QS_EXITED = 576, QS_COMBINED = 577, QS_ABORT = 578;
+constexpr int QS_EXITED = 576, QS_COMBINED = 577, QS_ABORT = 578, QS_EXITED_X = 584;
 constexpr float NEG_BIG = -1.0e30f;
 
 struct Blk {
@@ -449,9 +449,16 @@ __global__ void __launch_bounds__(QS_THREADS, 2) __attribute__((amdgpu_num_vgpr(
   }
   // the last workgroup to leave returns the counters to zero (after an abort
   // the tiles' block counters too: their tiles were left unfinished)
+  // (counted per XCD, then per XCD group, so the exits do not queue on one
+  // counter)
   if (tid == 0) {
-    const uint32_t e = fetch_add_relaxed(a.ws32 + QS_EXITED, 1u);
-    if (e == (uint32_t)(a.grid - 1)) {
+    const int xcd = (int)(blockIdx.x % XCDS);
+    const int on_xcd = (a.grid - xcd + XCDS - 1) / XCDS;
+    const int xcds = a.grid < XCDS ? a.grid : XCDS;
+    bool last = fetch_add_relaxed(a.ws32 + QS_EXITED_X + xcd, 1u) == (uint32_t)(on_xcd - 1);
+    if (last) last = fetch_add_relaxed(a.ws32 + QS_EXITED, 1u) == (uint32_t)(xcds - 1);
+    if (last) {
+      for (int g = 0; g < XCDS; ++g) store_relaxed_agent(a.ws32 + QS_EXITED_X + g, 0u);
       if (load_relaxed_agent(a.ws32 + QS_ABORT) != 0u)
         for (int t = 0; t < a.H * (a.S / QSA_BQ); ++t) store_relaxed_agent(a.ws32 + QSA_DONE + t, 0u);
       for (int s = 0; s < a.R; ++s) store_relaxed_agent(a.ws32 + s, 0u);
