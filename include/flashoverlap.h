@@ -273,6 +273,8 @@ fo_status fo_a2a_gemm(const void *const *pieces, const void *w, void *y, fo_dtyp
  * once the chunks order[0..s] it needs have landed (s = the later of its two
  * chunks' positions in `order`), so blocks on landed chunks run while the
  * rest is in flight; each query tile's blocks are merged in key-chunk order.
+ * Each stage first converts its new chunk's values to fp16 once (into the
+ * workspace, transposed), which the stage's blocks then copy as they lie.
  *   qkv     device bf16 [S][3*H*d]: per row the queries of heads 0..H-1 (d
  *           each), then their keys, then their values.
  *   o       device [S][H*d], o_dtype FO_F32 or FO_BF16 (nearest even).
@@ -283,8 +285,10 @@ fo_status fo_a2a_gemm(const void *const *pieces, const void *w, void *y, fo_dtyp
  *           chunk c (NULL = all present); split NULL or all 1; mode unused.
  *           stamps, optional, [2R+2]: [2R] start, [2R+1] last output row
  *           written.
- *   ws      device workspace of fo_qsa_workspace_bytes(S, H, d, R) bytes,
- *           zero-filled once (every call leaves its counters zero).
+ *   ws      device workspace of fo_qsa_workspace_bytes(S, H, d, R) bytes
+ *           (counters, per-block partial results, and the fp16 values:
+ *           H*S*d*2 bytes), zero-filled once (every call leaves its counters
+ *           zero).
  * Scores are bf16 MFMA products accumulated in fp32; the softmax runs in
  * fp32 (base-2 exponentials); the weighted sum multiplies fp16
  * probabilities by the values converted to fp16 (values must lie within

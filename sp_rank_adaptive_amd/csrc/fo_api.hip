@@ -579,14 +579,20 @@ namespace {
 // Query-split attention workspace: counters, then one partial slot per
 // (head, query tile, key chunk).
 struct QsaPlan {
-  size_t part_offset, total;
+  int64_t conv_off;
+  size_t part_offset, vt_offset, total;
 };
 
+// Workspace: counters (stage claims and the rest of the header, one per
+// query tile, one per (chunk, head) conversion), the partial slots, then the
+// fp16 value images.
 QsaPlan qsa_plan(int64_t seq, int64_t heads, int32_t R) {
   const int64_t tiles = seq / QSA_BQ;
   QsaPlan p{};
-  p.part_offset = ((size_t)(QSA_DONE + heads * tiles) * sizeof(uint32_t) + 255) & ~(size_t)255;
-  p.total = p.part_offset + (size_t)heads * tiles * R * (QSA_BQ * QSA_D + 2 * QSA_BQ) * sizeof(float);
+  p.conv_off = QSA_DONE + heads * tiles;
+  p.part_offset = ((size_t)(p.conv_off + (int64_t)R * heads) * sizeof(uint32_t) + 255) & ~(size_t)255;
+  p.vt_offset = p.part_offset + (size_t)heads * tiles * R * (QSA_BQ * QSA_D + 2 * QSA_BQ) * sizeof(float);
+  p.total = p.vt_offset + (size_t)heads * seq * QSA_D * sizeof(uint16_t);
   return p;
 }
 
@@ -656,6 +662,7 @@ fo_status fo_qsa_attention(const void *qkv, void *o, fo_dtype o_dtype, int64_t s
   // are empty and left out.
   int np = 0;
   const int per_pair = heads * a.tiles;
+  a.conv_units = heads * a.tiles;   // (head, pair of key tiles) of the chunk
   for (int sg = 0; sg < R; ++sg) {
     a.stage_pair0[sg] = np;
     const int cs = a.order[sg];
@@ -671,6 +678,10 @@ fo_status fo_qsa_attention(const void *qkv, void *o, fo_dtype o_dtype, int64_t s
     }
     add(cs, cs);
     a.stage_units[sg] = (np - a.stage_pair0[sg]) * per_pair;
+    // each stage opens with the conversion units of its new chunk; with the
+    // causal mask the stage's last pair is its diagonal one
+    a.stage_units[sg] += a.conv_units;
+    a.stage_big[sg] = causal ? a.stage_units[sg] - per_pair : a.stage_units[sg];
   }
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)QSA_D));
   const int64_t blocks = (int64_t)np * per_pair;
@@ -685,6 +696,8 @@ fo_status fo_qsa_attention(const void *qkv, void *o, fo_dtype o_dtype, int64_t s
   a.stamps = s->stamps;
   a.ws32 = static_cast<uint32_t *>(ws);
   a.part = reinterpret_cast<float *>(static_cast<char *>(ws) + plan.part_offset);
+  a.vt = reinterpret_cast<uint16_t *>(static_cast<char *>(ws) + plan.vt_offset);
+  a.conv_off = (int32_t)plan.conv_off;
   const hipError_t e = launch_qsa(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) { record(e); return FO_ERR_HIP; }
   return FO_OK;

@@ -44,23 +44,23 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int QS_THREADS = 256;
-constexpr int QS_WAVES = 4;
 constexpr int K_ROWB = QSA_D * 2;                  // 256 bytes per key row
 constexpr int K_TILE = QSA_BKV * K_ROWB;           // 16 KiB
-constexpr int VT_ROWB = 144;                       // 64 fp16 keys + 16 bytes of padding
-constexpr int VT_TILE = QSA_D * VT_ROWB;           // 18 KiB
-constexpr int K_STAGES = 3;                        // key tiles in the LDS ring
-constexpr int QS_LDS = K_STAGES * K_TILE + VT_TILE;
+constexpr int VT_ROWB = QSA_BKV * 2;               // 64 fp16 keys per value row
+constexpr int VT_TILE = QSA_D * VT_ROWB;           // 16 KiB
+constexpr int QS_LDS = 2 * K_TILE + 2 * VT_TILE;   // both tiles double-buffered
 constexpr int SLOT_FLOATS = QSA_BQ * QSA_D + 2 * QSA_BQ;   // O [BQ][d], m [BQ], l [BQ]
 constexpr int QS_EXITED = 576, QS_COMBINED = 577, QS_ABORT = 578, QS_EXITED_X = 584;
 constexpr float NEG_BIG = -1.0e30f;
+constexpr float RESCALE_LOG2 = 8.0f;   // lazy rescale threshold (log2 units)
 
 struct Blk {
   int h, qt, qc, kc;   // head, query tile over the whole sequence, query chunk, key chunk; qt < 0: stop
+  int conv;            // 1: conversion unit (chunk qc, head h, key tiles 2 kc and 2 kc + 1)
 };
 
 __device__ __forceinline__ void store_wt4(float *p, float v) {
-  asm volatile("global_store_dword %0, %1, off sc0 sc1" :: "v"(p), "v"(v) : "memory");
+  asm volatile("global_store_dword %0, %1, off sc0 sc1\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
 }
 
 // Loads of data another workgroup wrote through during this launch, at
@@ -74,38 +74,76 @@ __device__ __forceinline__ float load_coherent4(__amdgpu_buffer_rsrc_t rs, int o
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 1 | 2));
 }
 
-// Wave 0 (all lanes) claims the next block: the lowest open stage that has
-// blocks left.  Stage s is open once order[0..s] have all landed.  Waits
-// (bounded) while blocks are left only in stages that are not open.
+// Wave 0 (all lanes) claims the next block.  Stage s is open once
+// order[0..s] have all landed.  Among the open stages with blocks left it
+// takes the largest next block (a stage hands out its full pairs first, then
+// its diagonal blocks from the one with the most key tiles), the lowest stage
+// on ties: with several stages open the long blocks start first and the
+// short ones fill in at the end.  Waits (bounded) while blocks are left only
+// in stages that are not open.
 __device__ Blk qsa_claim(const QsaArgs &a, uint32_t &acquired, uint64_t &wait_from) {
   const int lane = threadIdx.x & 63;
   const int R = a.R;
   for (;;) {
     bool ok = false, left = false;
+    int key = 0;
     if (lane < R) {
       const int c = a.order[lane];
       ok = a.arrived == nullptr || c == a.local || epoch_reached(load_relaxed(a.arrived + c), a.epoch);
-      left = load_relaxed(a.ws32 + lane) < (uint32_t)a.stage_units[lane];
+      const uint32_t u = load_relaxed(a.ws32 + lane);
+      left = u < (uint32_t)a.stage_units[lane];
+      const int big = a.stage_big[lane];
+      key = (int)u < a.conv_units ? 2 * a.tiles + 2
+            : (int)u < big ? 2 * a.tiles + 1 : 2 * (a.tiles - ((int)u - big) / a.H);
     }
     const uint64_t landed = __ballot(ok);
     const uint64_t lm = __ballot(left);
-    if (lm == 0ull) return Blk{0, -1, 0, 0};                       // every block claimed
+    if (lm == 0ull) return Blk{0, -1, 0, 0, 0};                    // every unit claimed
     const int open = (~landed == 0ull) ? 64 : __builtin_ctzll(~landed);
     const uint64_t om = open >= 64 ? lm : (lm & ((1ull << open) - 1ull));
     if (om) {
-      const int s = __builtin_ctzll(om);
+      int sel = ((om >> lane) & 1ull) ? (key << 6) | (63 - lane) : -1;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) sel = max(sel, __shfl_xor(sel, off));
+      const int s = 63 - (__builtin_amdgcn_readfirstlane(sel) & 63);
       uint32_t u = 0;
       if (lane == 0) u = fetch_add_relaxed(a.ws32 + s, 1u);
       u = __builtin_amdgcn_readfirstlane(u);
       if (u >= (uint32_t)a.stage_units[s]) continue;                 // lost the race: look again
       const int per_pair = a.H * a.tiles;
-      const int pi = a.stage_pair0[s] + (int)u / per_pair;
-      const int rem = (int)u - ((int)u / per_pair) * per_pair;
+      const int big = a.stage_big[s];
+      int pi, j;
       Blk b;
-      b.h = rem / a.tiles;
+      b.conv = 0;
+      if ((int)u < a.conv_units) {
+        // convert the new chunk's value rows (head u / tiles, key tiles of part u % tiles)
+        b.conv = 1;
+        b.qc = a.order[s];
+        b.h = (int)u / a.tiles;
+        b.kc = (int)u - b.h * a.tiles;
+        b.qt = 0;
+        if (a.arrived != nullptr && !((acquired >> b.qc) & 1u)) {
+          if (b.qc != a.local) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+          acquired |= 1u << b.qc;
+        }
+        return b;
+      }
+      if ((int)u < big) {
+        const int ub = (int)u - a.conv_units;
+        pi = a.stage_pair0[s] + ub / per_pair;
+        const int rem = ub - (ub / per_pair) * per_pair;
+        b.h = rem / a.tiles;
+        j = rem - b.h * a.tiles;
+      } else {
+        const int v = (int)u - big;
+        pi = a.stage_pair0[s] + (big - a.conv_units) / per_pair;
+        const int jj = v / a.H;
+        b.h = v - jj * a.H;
+        j = a.tiles - 1 - jj;
+      }
       b.qc = a.pair_q[pi];
       b.kc = a.pair_k[pi];
-      b.qt = b.qc * a.tiles + (rem - b.h * a.tiles);
+      b.qt = b.qc * a.tiles + j;
       // first use of a peer's chunk by this workgroup: its rows were written
       // by a copy engine during the launch
       const uint32_t need = (1u << b.qc) | (1u << b.kc);
@@ -124,9 +162,44 @@ __device__ Blk qsa_claim(const QsaArgs &a, uint32_t &acquired, uint64_t &wait_fr
         if (a.status) __hip_atomic_store(a.status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         __hip_atomic_store(a.ws32 + QS_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      return Blk{0, -2, 0, 0};
+      return Blk{0, -2, 0, 0, 0};
     }
     __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Conversion unit (c, h, p): the value rows of key tiles 2p and 2p + 1 of
+// chunk c, head h, converted to fp16 and transposed into the image a block
+// copies to LDS.  Per key tile the image is [d][64 keys]; 16-byte piece P of
+// row d holds the keys of k-group P = 4 k2 + g, in the order the score
+// fragments hold them (32 k2 + 4 g + 0..3, then 32 k2 + 16 + 4 g + 0..3),
+// and sits at piece P ^ (d % 8), so the fragment reads of 8 rows fall on 8
+// distinct bank groups.  Thread t: key tile 2p + t / 128, k-group t % 8,
+// head dims 8 ((t / 8) % 16) .. + 8.  Stores are written through.
+__device__ __forceinline__ void qsa_convert(const QsaArgs &a, int c, int h, int p) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int kg = tid & 7, dg = (tid >> 3) & 15;
+  const int k2 = kg >> 2, g = kg & 3;
+  const int HD = a.H * QSA_D;
+  const int64_t RS = 3 * (int64_t)HD;
+  const int kt = 2 * p + (tid >> 7);                               // key tile within the chunk
+  const int64_t row0 = (int64_t)c * a.chunk + (int64_t)kt * QSA_BKV;
+  const uint16_t *src = a.qkv + row0 * RS + 2 * HD + h * QSA_D + dg * 8;
+  bf16x8 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int key = 32 * k2 + 4 * g + (i < 4 ? i : 12 + i);
+    v[i] = *reinterpret_cast<const bf16x8 *>(src + (int64_t)key * RS);
+  }
+  uint16_t *dst = a.vt + ((int64_t)h * (a.S / QSA_BKV) + (int64_t)c * (a.chunk / QSA_BKV) + kt) * (QSA_D * QSA_BKV);
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    f16x8 piece;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) piece[i] = (_Float16)(float)v[i][d];
+    const int row = dg * 8 + d;
+    store_wt16(dst + row * QSA_BKV + ((kg ^ d) << 3), __builtin_bit_cast(f32x4, piece));
   }
 }
 
@@ -157,52 +230,28 @@ __device__ __forceinline__ void qsa_block(const QsaArgs &a, char *lds, const Blk
     for (int ks = 0; ks < 4; ++ks) qf[qb][ks] = *reinterpret_cast<const bf16x8 *>(qrow + ks * 32);
   }
 
-  // Key tile copies: thread t fills 16-byte slot t of each of 4 rounds (16
-  // key rows per round); slot t holds row t / 16 of the round, physical piece
-  // t % 16, i.e. logical piece (t % 16) ^ (row % 16).
+  // Copies into LDS by the buffer-load DMA path, both tiles double-buffered
+  // (tile kt in buffer kt % 2).  Key tile: thread t fills 16-byte slot t of
+  // each of 4 rounds (16 key rows per round); slot t holds row t / 16 of the
+  // round, physical piece t % 16, i.e. logical piece (t % 16) ^ (row % 16).
+  // Value tile: the converted image, 16 KiB copied as it lies, at
+  // system-coherent cache policy (other workgroups wrote it in this launch).
   const __amdgpu_buffer_rsrc_t rsk =
       uniform_rsrc(a.qkv + (int64_t)kbase * RS + HD + b.h * QSA_D, (int)((int64_t)a.chunk * RS * 2));
-  const int ksl = tid & 255;
-  const int k_voff = (int)(((ksl >> 4) * RS + (((ksl & 15) ^ (ksl >> 4)) * 8)) * 2);
-  const uint32_t k_lds0 = lds_addr(lds) + (uint32_t)(__builtin_amdgcn_readfirstlane(wave) * 1024);
-  auto issue_k = [&](int kt) {
-    const uint32_t base = k_lds0 + (uint32_t)((kt % K_STAGES) * K_TILE);
+  const __amdgpu_buffer_rsrc_t rsv =
+      uniform_rsrc(a.vt + ((int64_t)b.h * (a.S / QSA_BKV) + (int64_t)b.kc * nkt_all) * (QSA_D * QSA_BKV),
+                   nkt_all * VT_TILE);
+  const int k_voff = (int)(((tid >> 4) * RS + (((tid & 15) ^ (tid >> 4)) * 8)) * 2);
+  const uint32_t lds_w = lds_addr(lds) + (uint32_t)(__builtin_amdgcn_readfirstlane(wave) * 1024);
+  auto issue = [&](int kt) {
+    const uint32_t kb = lds_w + (uint32_t)((kt & 1) * K_TILE);
+    const uint32_t vb = lds_w + (uint32_t)(2 * K_TILE + (kt & 1) * VT_TILE);
 #pragma unroll
     for (int rd = 0; rd < 4; ++rd)
-      dma16(base + (uint32_t)(rd * 4096), k_voff, rsk, (int)((int64_t)(kt * QSA_BKV + rd * 16) * RS * 2));
-  };
-  // Value tile: thread items idx = tid, tid + 256 cover key pairs kp = idx % 32
-  // and head-dimension groups e = idx / 32 (8 values each).
-  // Two register sets: the loads of tile kt + 2 go out while tile kt is
-  // multiplied, and set kt % 2 is written to LDS once tile kt - 1 is done.
-  const uint16_t *vbase = a.qkv + (int64_t)kbase * RS + 2 * HD + b.h * QSA_D;
-  bf16x8 vr[2][2][2];
-  auto load_v = [&](int kt, auto setc) {
-    constexpr int st = decltype(setc)::value;
+      dma16(kb + (uint32_t)(rd * 4096), k_voff, rsk, (int)((int64_t)(kt * QSA_BKV + rd * 16) * RS * 2));
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int idx = tid + it * QS_THREADS;
-      const int kp = idx & 31, e = idx >> 5;
-#pragma unroll
-      for (int r = 0; r < 2; ++r)
-        vr[st][it][r] = *reinterpret_cast<const bf16x8 *>(vbase + (int64_t)(kt * QSA_BKV + 2 * kp + r) * RS + 8 * e);
-    }
-  };
-  auto store_vt = [&](auto setc) {
-    constexpr int st = decltype(setc)::value;
-    char *vt = lds + K_STAGES * K_TILE;
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int idx = tid + it * QS_THREADS;
-      const int kp = idx & 31, e = idx >> 5;
-#pragma unroll
-      for (int dc = 0; dc < 8; ++dc) {
-        const _Float16 lo = (_Float16)(float)vr[st][it][0][dc];
-        const _Float16 hi = (_Float16)(float)vr[st][it][1][dc];
-        const uint32_t word = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-        *reinterpret_cast<uint32_t *>(vt + (8 * e + dc) * VT_ROWB + 4 * kp) = word;
-      }
-    }
+    for (int rd = 0; rd < 4; ++rd)
+      dma16_coherent(vb + (uint32_t)(rd * 4096), tid * 16, rsv, kt * VT_TILE + rd * 4096);
   };
 
   f32x4 o[8][2];
@@ -212,30 +261,18 @@ __device__ __forceinline__ void qsa_block(const QsaArgs &a, char *lds, const Blk
     for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m[2] = {NEG_BIG, NEG_BIG}, l[2] = {0.f, 0.f};
 
-  // Pipeline: the K copy and V loads of tile kt + 2 are issued at the start
-  // of tile kt; V^T of tile kt + 1 is written after tile kt's weighted sum.
-  // Each wave issues 8 vector-memory operations per tile (4 copies, 4 loads),
-  // which complete in order.
+  // Pipeline: tile kt + 1's copies go out at the start of tile kt, into the
+  // buffers tile kt - 1 used; one barrier per tile (tile kt + 1 landed, and
+  // every wave is done with tile kt's buffers).
   __syncthreads();                 // the previous block's last tile is done with the buffers
-  issue_k(0);
-  load_v(0, std::integral_constant<int, 0>{});
-  if (nkt > 1) {
-    issue_k(1);
-    load_v(1, std::integral_constant<int, 1>{});
-    wait_vm<8>();
-  } else {
-    wait_vm<0>();
-  }
-  store_vt(std::integral_constant<int, 0>{});
+  issue(0);
+  wait_vm<0>();
   __syncthreads();
-  auto tile = [&](int kt, auto setc) {
-    constexpr int vs = decltype(setc)::value;   // kt % 2
-    if (kt + 2 < nkt) {
-      issue_k(kt + 2);
-      load_v(kt + 2, setc);        // set kt % 2 was written to LDS before tile kt
-    }
-    const char *K = lds + (kt % K_STAGES) * K_TILE;
-    const char *VT = lds + K_STAGES * K_TILE;
+  auto tile = [&](int kt, auto maskc) {
+    constexpr bool MASK = decltype(maskc)::value;   // the tile crosses the diagonal
+    if (kt + 1 < nkt) issue(kt + 1);
+    const char *K = lds + (kt & 1) * K_TILE;
+    const char *VT = lds + 2 * K_TILE + (kt & 1) * VT_TILE;
     // S^T = K Q^T: st[kb][qb], keys 16 kb + 4 g + v, query 16 qb + li
     f32x4 st[4][2];
 #pragma unroll
@@ -248,70 +285,82 @@ __device__ __forceinline__ void qsa_block(const QsaArgs &a, char *lds, const Blk
           st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : st[kb][qb], 0, 0, 0);
       }
     }
-    // online softmax per query (scores in log2 units)
+    // Online softmax per query, in log2 units.  The maximum is taken over
+    // the raw scores (the scale is positive); the reference m a row's
+    // probabilities are taken against moves up only when the tile's maximum
+    // exceeds it by more than 2^8, so the weighted sums are rescaled only
+    // then (any reference gives the same softmax; probabilities stay below
+    // 2^8, well inside fp16).  The first tile always sets it.
     f16x8 pf[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int qrow = q0 + wave * 32 + qb * 16 + li;
       float mx = NEG_BIG;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          float s = st[kb][qb][v] * a.scale_log2;
-          if (diag && kbase + kt * QSA_BKV + kb * 16 + 4 * g + v > qrow) s = -__builtin_inff();
-          st[kb][qb][v] = s;
-          mx = fmaxf(mx, s);
+          float sv = st[kb][qb][v];
+          if constexpr (MASK) {
+            const int qrow = q0 + wave * 32 + qb * 16 + li;
+            if (kbase + kt * QSA_BKV + kb * 16 + 4 * g + v > qrow) sv = -__builtin_inff();
+            st[kb][qb][v] = sv;
+          }
+          mx = fmaxf(mx, sv);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[qb], mx);
-      const float f = __builtin_amdgcn_exp2f(m[qb] - mnew);
-      m[qb] = mnew;
+      const float mxs = mx * a.scale_log2;
+      const bool grow = mxs > m[qb] + RESCALE_LOG2;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float mnew = grow ? mxs : m[qb];
+        const float f = __builtin_amdgcn_exp2f(m[qb] - mnew);
+        m[qb] = mnew;
+        l[qb] *= f;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[db][qb] *= f;
+      }
+      const float nm = -m[qb];
       float sum = 0.f;
       _Float16 p16[4][4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float p = __builtin_amdgcn_exp2f(st[kb][qb][v] - mnew);
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][qb][v], a.scale_log2, nm));
           sum += p;
           p16[kb][v] = (_Float16)p;
         }
-      l[qb] = l[qb] * f + sum;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) o[db][qb] *= f;
+      l[qb] += sum;
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
         pf[qb][k2] = f16x8{p16[2 * k2][0], p16[2 * k2][1], p16[2 * k2][2], p16[2 * k2][3],
                            p16[2 * k2 + 1][0], p16[2 * k2 + 1][1], p16[2 * k2 + 1][2], p16[2 * k2 + 1][3]};
     }
-    // O^T += V^T P^T: value rows 16 db + li, keys 4 g + 0..3 of blocks 2 k2
-    // and 2 k2 + 1 (the same key order as pf)
+    // O^T += V^T P^T: value rows 16 db + li, the keys of k-group 4 k2 + g
+    // (the same key order as pf)
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const char *row = VT + (db * 16 + li) * VT_ROWB;
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        const f16x4 lo = *reinterpret_cast<const f16x4 *>(row + ((2 * k2) * 16 + 4 * g) * 2);
-        const f16x4 hi = *reinterpret_cast<const f16x4 *>(row + ((2 * k2 + 1) * 16 + 4 * g) * 2);
-        const f16x8 vf = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const f16x8 vf = *reinterpret_cast<const f16x8 *>(row + (((k2 * 4 + g) ^ (li & 7)) << 4));
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
           o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qb][k2], o[db][qb], 0, 0, 0);
       }
     }
     if (kt + 1 < nkt) {
-      __syncthreads();             // every wave is done with V^T of tile kt
-      if (kt + 2 < nkt) wait_vm<8>();   // tile kt + 1's copies and loads have landed
-      else wait_vm<0>();
-      store_vt(std::integral_constant<int, 1 - vs>{});
-      __syncthreads();             // K and V^T of tile kt + 1 visible
+      wait_vm<0>();                // tile kt + 1 landed
+      __syncthreads();             // ... for every wave; every wave is done with tile kt
     }
   };
-  for (int kt = 0; kt < nkt; kt += 2) {
-    tile(kt, std::integral_constant<int, 0>{});
-    if (kt + 1 < nkt) tile(kt + 1, std::integral_constant<int, 1>{});
+  // Key tiles that end before the block's first query need no mask; on the
+  // diagonal the last two tiles cross it.
+  const int nfree = diag ? (q0 - kbase) / QSA_BKV : nkt;
+  for (int kt = 0; kt < nfree; ++kt) tile(kt, std::false_type{});
+  if (diag) {
+    tile(nfree, std::true_type{});
+    tile(nfree + 1, std::true_type{});
   }
 
   // the block's slot: O rows by query (value dims 16 db + 4 g + v in lane
@@ -422,7 +471,30 @@ __global__ void __launch_bounds__(QS_THREADS, 2) __attribute__((amdgpu_num_vgpr(
     b.qt = __builtin_amdgcn_readfirstlane(b.qt);
     b.qc = __builtin_amdgcn_readfirstlane(b.qc);
     b.kc = __builtin_amdgcn_readfirstlane(b.kc);
+    b.conv = __builtin_amdgcn_readfirstlane(b.conv);
     if (b.qt < 0) break;
+    if (b.conv) {
+      // count the unit once its stores are acknowledged
+      qsa_convert(a, b.qc, b.h, b.kc);
+      wait_stores();
+      __syncthreads();
+      if (tid == 0) fetch_add_relaxed(a.ws32 + a.conv_off + b.qc * a.H + b.h, 1u);
+      continue;
+    }
+    // the key chunk's values for this head must all be converted (bounded wait)
+    if (tid == 0) {
+      const uint32_t *cc = a.ws32 + a.conv_off + b.kc * a.H + b.h;
+      const uint64_t t0 = now_ticks();
+      while (load_relaxed(cc) < (uint32_t)a.tiles) {
+        if (load_relaxed(a.ws32 + QS_ABORT) != 0u) break;
+        if (now_ticks() - t0 > a.timeout_ticks) {
+          if (a.status) __hip_atomic_store(a.status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          __hip_atomic_store(a.ws32 + QS_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
     qsa_block(a, lds, b);
     // count the block once its stores are acknowledged; the block that
     // completes the tile merges it
@@ -462,6 +534,7 @@ __global__ void __launch_bounds__(QS_THREADS, 2) __attribute__((amdgpu_num_vgpr(
       if (load_relaxed_agent(a.ws32 + QS_ABORT) != 0u)
         for (int t = 0; t < a.H * (a.S / QSA_BQ); ++t) store_relaxed_agent(a.ws32 + QSA_DONE + t, 0u);
       for (int s = 0; s < a.R; ++s) store_relaxed_agent(a.ws32 + s, 0u);
+      for (int t = 0; t < a.R * a.H; ++t) store_relaxed_agent(a.ws32 + a.conv_off + t, 0u);
       store_relaxed_agent(a.ws32 + QS_COMBINED, 0u);
       store_relaxed_agent(a.ws32 + QS_ABORT, 0u);
       store_relaxed_agent(a.ws32 + QS_EXITED, 0u);

@@ -64,12 +64,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // (wait_stores) before it counts itself, instead of a release fence that
 // writes back the whole L2 of its XCD.  The compiler does not track these
 // stores: every path that issues them ends in wait_stores.
+// The store reads its data registers after it issues, and the compiler,
+// which sees only an asm statement, may write those registers with the very
+// next instruction; the wait states after the store (the hardware's rule for
+// stores of more than 8 bytes asks for one) cover that window.
 __device__ __forceinline__ void store_wt16(void *p, const f32x4 &v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" :: "v"(p), "v"(v) : "memory");
+  asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
 }
 
 __device__ __forceinline__ void store_wt8(void *p, const u32x2 &v) {
-  asm volatile("global_store_dwordx2 %0, %1, off sc0 sc1" :: "v"(p), "v"(v) : "memory");
+  asm volatile("global_store_dwordx2 %0, %1, off sc0 sc1\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
 }
 
 __device__ __forceinline__ void wait_stores() {
@@ -82,6 +86,15 @@ __device__ __forceinline__ void wait_stores() {
 // (wait_vm) and a workgroup barrier follows them before any read.
 __device__ __forceinline__ void dma16(uint32_t m0, int voff, __amdgpu_buffer_rsrc_t rs, int soff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(rs),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory");
+}
+
+// dma16 at system-coherent cache policy (sc0 sc1): data other workgroups
+// wrote through during this launch is read from the coherence point, never
+// from a stale line of this XCD's L2.
+__device__ __forceinline__ void dma16_coherent(uint32_t m0, int voff, __amdgpu_buffer_rsrc_t rs, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen sc0 sc1 lds"
                :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(rs),
                   "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory");
 }

@@ -47,6 +47,12 @@ def att():
     return attention
 
 
+def counter_bytes(S, H, R):
+    """The workspace's counter words: the header (stage claims, exits,
+    abort), one per (head, query tile), one per (chunk, head) conversion."""
+    return (1024 + H * (S // 128) + R * H) * 4
+
+
 def run(fo, qkv_b, H, R, causal, o_dtype=torch.float32, ws=None, **sched):
     S = qkv_b.shape[0]
     qkv = dev_bf16(qkv_b)
@@ -66,7 +72,7 @@ def test_qsa_parity(fo, orc, att, causal, S, H, R):
     ref = att.attention(qkv, H, D, causal)
     y, ws = run(fo, qkv, H, R, causal)
     check_tolerance(y, ref, what="qsa")
-    assert int(ws[:4096].sum()) == 0, "counters not returned to zero"
+    assert int(ws[:counter_bytes(S, H, R)].sum()) == 0, "counters not returned to zero"
     y2, _ = run(fo, qkv, H, R, causal, ws=ws, arrived=torch.full((R,), 1 << 30, dtype=torch.int32, device="cuda"))
     assert np.array_equal(y, y2), "preset flags changed the bits"
 
@@ -122,7 +128,7 @@ def qsa_emulated(fo, qkv_b, H, R, local, arrival, release_ns, causal=True, order
                                                           timeout_ns=5_000_000_000), ws)
     torch.cuda.synchronize()
     assert int(status.item()) == 0, "flag wait timed out"
-    assert int(ws[:4096].sum()) == 0
+    assert int(ws[:counter_bytes(S, H, R)].sum()) == 0
     st = host(gs).astype(np.int64)
     last = max(host(es).astype(np.int64)[1 + q] for q in arrival)
     assert st[2 * R + 1] >= last, "output completed before the last landing"
@@ -160,8 +166,7 @@ def test_qsa_timeout_from_unset_flag(fo):
                                                         timeout_ns=2_000_000), ws)
     torch.cuda.synchronize()
     assert int(status.item()) == fo.FO_ERR_TIMEOUT
-    counters = (1024 + H * (S // 128)) * 4          # stage, exit and per-tile counters
-    assert int(ws[:counters].sum()) == 0, "counters not returned to zero after the abort"
+    assert int(ws[:counter_bytes(S, H, R)].sum()) == 0, "counters not returned to zero after the abort"
     flags.fill_(epoch())
     fo.fo_qsa_attention(qkv, o, H, D, True, fo.Schedule(nchunks=R, epoch=_EP[0], arrived=flags), ws)
     torch.cuda.synchronize()
