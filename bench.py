@@ -506,8 +506,7 @@ def qsa_rate(fo, cfg, launches=20):
     qkv = dev_bf16(wl.qkv_input(cfg, "gauss"))
     o = torch.empty((cfg.S, cfg.H * cfg.d), device="cuda")
     ws = torch.zeros(fo.fo_qsa_workspace_bytes(cfg.S, cfg.H, cfg.d, cfg.R), dtype=torch.uint8, device="cuda")
-    flags = torch.full((cfg.R,), 1 << 30, dtype=torch.int32, device="cuda")
-    sched = lambda e: fo.Schedule(nchunks=cfg.R, epoch=e, arrived=flags)
+    sched = lambda e: fo.Schedule(nchunks=cfg.R, epoch=e)   # every chunk present: no flags
     for e in range(3):
         fo.fo_qsa_attention(qkv, o, cfg.H, cfg.d, cfg.causal, sched(1 + e), ws)
     torch.cuda.synchronize()

@@ -662,7 +662,7 @@ fo_status fo_qsa_attention(const void *qkv, void *o, fo_dtype o_dtype, int64_t s
   // are empty and left out.
   int np = 0;
   const int per_pair = heads * a.tiles;
-  a.conv_units = heads * a.tiles;   // (head, pair of key tiles) of the chunk
+  a.conv_units = heads * (a.chunk / QSA_BKV);   // (head, key tile) of the chunk
   for (int sg = 0; sg < R; ++sg) {
     a.stage_pair0[sg] = np;
     const int cs = a.order[sg];

@@ -42,6 +42,7 @@ namespace {
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int QS_THREADS = 256;
 constexpr int K_ROWB = QSA_D * 2;                  // 256 bytes per key row
@@ -51,6 +52,10 @@ constexpr int VT_TILE = QSA_D * VT_ROWB;           // 16 KiB
 constexpr int QS_LDS = 2 * K_TILE + 2 * VT_TILE;   // both tiles double-buffered
 constexpr int SLOT_FLOATS = QSA_BQ * QSA_D + 2 * QSA_BQ;   // O [BQ][d], m [BQ], l [BQ]
 constexpr int QS_EXITED = 576, QS_COMBINED = 577, QS_ABORT = 578, QS_EXITED_X = 584;
+constexpr int QS_GROUPS = 8;   // claim groups per stage (one per XCD)
+constexpr int QS_LINE = 32;    // words between the groups' counter lines: counter (g, s) at word 32 g + s
+constexpr int QS_NEXT = 579;   // every chunk present: next unit past the workgroups' first ones
+constexpr int QS_STATIC = 2;   // every chunk present: units each workgroup takes without a counter
 constexpr float NEG_BIG = -1.0e30f;
 constexpr float RESCALE_LOG2 = 8.0f;   // lazy rescale threshold (log2 units)
 
@@ -74,85 +79,164 @@ __device__ __forceinline__ float load_coherent4(__amdgpu_buffer_rsrc_t rs, int o
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 1 | 2));
 }
 
-// Wave 0 (all lanes) claims the next block.  Stage s is open once
-// order[0..s] have all landed.  Among the open stages with blocks left it
-// takes the largest next block (a stage hands out its full pairs first, then
-// its diagonal blocks from the one with the most key tiles), the lowest stage
-// on ties: with several stages open the long blocks start first and the
-// short ones fill in at the end.  Waits (bounded) while blocks are left only
-// in stages that are not open.
-__device__ Blk qsa_claim(const QsaArgs &a, uint32_t &acquired, uint64_t &wait_from) {
+// Wave 0 (all lanes) claims the next unit.  Stage s is open once
+// order[0..s] have all landed.  A stage's units are dealt to 8 groups
+// (unit u to group u % 8), one claim counter each; the counters of a group
+// share one 128-byte line (word 32 g + s), and the workgroups of the 8 XCDs
+// (group = workgroup % 8) claim in their own group, so a claim reads and
+// updates one line that an eighth of the workgroups use.  Among its group's
+// open stages with units left the claim takes the largest next unit (a stage
+// hands out its conversion units first, then its full pairs, then its
+// diagonal blocks from the one with the most key tiles), the lowest stage on
+// ties: with several stages open the long blocks start first and the short
+// ones fill in at the end.  With its group exhausted it takes from the other
+// groups the same way.  Waits (bounded) while units are left only in stages
+// that are not open.
+__device__ __forceinline__ int unit_key(const QsaArgs &a, int s, int u) {
+  const int big = a.stage_big[s];
+  const int key = u < a.conv_units ? 2 * a.tiles + 2 : u < big ? 2 * a.tiles + 1 : 2 * (a.tiles - (u - big) / a.H);
+  return min(key, (1 << 22) - 1);   // ranks only; keeps the packed rank below 2^31
+}
+
+// Unit u of stage s as a block (or a conversion unit); the first use of a
+// peer's chunk by this workgroup acquires (a copy engine wrote its rows
+// during the launch).
+__device__ __forceinline__ Blk decode_unit(const QsaArgs &a, int s, uint32_t u, uint32_t &acquired) {
+  const int per_pair = a.H * a.tiles;
+  const int big = a.stage_big[s];
+  int pi, j;
+  Blk b;
+  b.conv = 0;
+  if ((int)u < a.conv_units) {
+    // convert the new chunk's value rows (head u / key tiles, key tile u % key tiles)
+    const int nkt = a.chunk / QSA_BKV;
+    b.conv = 1;
+    b.qc = a.order[s];
+    b.h = (int)u / nkt;
+    b.kc = (int)u - b.h * nkt;
+    b.qt = 0;
+    if (a.arrived != nullptr && !((acquired >> b.qc) & 1u)) {
+      if (b.qc != a.local) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+      acquired |= 1u << b.qc;
+    }
+    return b;
+  }
+  if ((int)u < big) {
+    const int ub = (int)u - a.conv_units;
+    pi = a.stage_pair0[s] + ub / per_pair;
+    const int rem = ub - (ub / per_pair) * per_pair;
+    b.h = rem / a.tiles;
+    j = rem - b.h * a.tiles;
+  } else {
+    const int v = (int)u - big;
+    pi = a.stage_pair0[s] + (big - a.conv_units) / per_pair;
+    const int jj = v / a.H;
+    b.h = v - jj * a.H;
+    j = a.tiles - 1 - jj;
+  }
+  b.qc = a.pair_q[pi];
+  b.kc = a.pair_k[pi];
+  b.qt = b.qc * a.tiles + j;
+  // first use of a peer's chunk by this workgroup: its rows were written
+  // by a copy engine during the launch
+  const uint32_t need = (1u << b.qc) | (1u << b.kc);
+  if (a.arrived != nullptr && (need & ~acquired)) {
+    uint32_t peers = need & ~acquired & ~(1u << a.local);
+    if (peers) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+    acquired |= need;
+  }
+  return b;
+}
+
+__device__ Blk qsa_claim(const QsaArgs &a, uint32_t &acquired, uint64_t &wait_from, int &taken) {
   const int lane = threadIdx.x & 63;
   const int R = a.R;
+  if (a.arrived == nullptr) {
+    // Every chunk present: one sequence over all stages, largest first (the
+    // conversion units, the full pairs, then the diagonal blocks from the
+    // most key tiles down).  A workgroup's first two units are its index in
+    // it and that plus the grid (no counter: the workgroups take them
+    // together at the start and after the conversions); the later ones,
+    // which finish at scattered times, come from one counter.
+    uint32_t G;
+    if (taken < QS_STATIC) {
+      G = blockIdx.x + (uint32_t)(taken * a.grid);
+    } else {
+      uint32_t k = 0;
+      if (lane == 0) k = fetch_add_relaxed(a.ws32 + QS_NEXT, 1u);
+      G = (uint32_t)(QS_STATIC * a.grid) + __builtin_amdgcn_readfirstlane(k);
+    }
+    ++taken;
+    const uint32_t nconv = (uint32_t)(R * a.conv_units);
+    if (G < nconv) return decode_unit(a, (int)(G / a.conv_units), G % a.conv_units, acquired);
+    G -= nconv;
+    for (int s = 0; s < R; ++s) {
+      const uint32_t nb = (uint32_t)(a.stage_big[s] - a.conv_units);
+      if (G < nb) return decode_unit(a, s, (uint32_t)a.conv_units + G, acquired);
+      G -= nb;
+    }
+    const uint32_t per_class = (uint32_t)(R * a.H);               // diagonal blocks of one size
+    if (a.causal && G < per_class * (uint32_t)a.tiles) {
+      const uint32_t jj = G / per_class, rem = G - jj * per_class;
+      const int s = (int)(rem / a.H), h = (int)(rem - (rem / a.H) * a.H);
+      return decode_unit(a, s, (uint32_t)a.stage_big[s] + jj * a.H + h, acquired);
+    }
+    return Blk{0, -1, 0, 0, 0};                                      // every unit taken
+  }
+  const int xg = (int)(blockIdx.x % QS_GROUPS);
   for (;;) {
-    bool ok = false, left = false;
-    int key = 0;
+    bool ok = false;
     if (lane < R) {
       const int c = a.order[lane];
       ok = a.arrived == nullptr || c == a.local || epoch_reached(load_relaxed(a.arrived + c), a.epoch);
-      const uint32_t u = load_relaxed(a.ws32 + lane);
-      left = u < (uint32_t)a.stage_units[lane];
-      const int big = a.stage_big[lane];
-      key = (int)u < a.conv_units ? 2 * a.tiles + 2
-            : (int)u < big ? 2 * a.tiles + 1 : 2 * (a.tiles - ((int)u - big) / a.H);
     }
     const uint64_t landed = __ballot(ok);
-    const uint64_t lm = __ballot(left);
-    if (lm == 0ull) return Blk{0, -1, 0, 0, 0};                    // every unit claimed
     const int open = (~landed == 0ull) ? 64 : __builtin_ctzll(~landed);
-    const uint64_t om = open >= 64 ? lm : (lm & ((1ull << open) - 1ull));
-    if (om) {
-      int sel = ((om >> lane) & 1ull) ? (key << 6) | (63 - lane) : -1;
+    // rank of a candidate (stage st, group g, next unit u): key, then lower
+    // stage, then lower group
+    auto rank = [&](int st, int g, int u) { return (unit_key(a, st, u) << 8) | (127 - (st * QS_GROUPS + g)); };
+    int best = -1;
+    bool own_left = false;
+    if (lane < R) {
+      const uint32_t k = load_relaxed(a.ws32 + QS_LINE * xg + lane);
+      const int u = (int)k * QS_GROUPS + xg;
+      if (u < a.stage_units[lane]) {
+        own_left = true;
+        if (lane < open) best = rank(lane, xg, u);
+      }
+    }
+    bool any_left = __ballot(own_left) != 0ull;
+    if (__ballot(best >= 0) == 0ull) {
+      // the own group has no open unit: look at every group
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) sel = max(sel, __shfl_xor(sel, off));
-      const int s = 63 - (__builtin_amdgcn_readfirstlane(sel) & 63);
-      uint32_t u = 0;
-      if (lane == 0) u = fetch_add_relaxed(a.ws32 + s, 1u);
-      u = __builtin_amdgcn_readfirstlane(u);
-      if (u >= (uint32_t)a.stage_units[s]) continue;                 // lost the race: look again
-      const int per_pair = a.H * a.tiles;
-      const int big = a.stage_big[s];
-      int pi, j;
-      Blk b;
-      b.conv = 0;
-      if ((int)u < a.conv_units) {
-        // convert the new chunk's value rows (head u / tiles, key tiles of part u % tiles)
-        b.conv = 1;
-        b.qc = a.order[s];
-        b.h = (int)u / a.tiles;
-        b.kc = (int)u - b.h * a.tiles;
-        b.qt = 0;
-        if (a.arrived != nullptr && !((acquired >> b.qc) & 1u)) {
-          if (b.qc != a.local) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
-          acquired |= 1u << b.qc;
+      for (int bt = 0; bt < (QSA_MAX_CHUNKS * QS_GROUPS + 63) / 64; ++bt) {
+        const int idx = bt * 64 + lane;
+        const int g = idx / QSA_MAX_CHUNKS, st = idx % QSA_MAX_CHUNKS;
+        bool left = false;
+        if (st < R && g < QS_GROUPS) {
+          const uint32_t k = load_relaxed(a.ws32 + QS_LINE * g + st);
+          const int u = (int)k * QS_GROUPS + g;
+          if (u < a.stage_units[st]) {
+            left = true;
+            if (st < open) best = max(best, rank(st, g, u));
+          }
         }
-        return b;
+        any_left = any_left || __ballot(left) != 0ull;
       }
-      if ((int)u < big) {
-        const int ub = (int)u - a.conv_units;
-        pi = a.stage_pair0[s] + ub / per_pair;
-        const int rem = ub - (ub / per_pair) * per_pair;
-        b.h = rem / a.tiles;
-        j = rem - b.h * a.tiles;
-      } else {
-        const int v = (int)u - big;
-        pi = a.stage_pair0[s] + (big - a.conv_units) / per_pair;
-        const int jj = v / a.H;
-        b.h = v - jj * a.H;
-        j = a.tiles - 1 - jj;
-      }
-      b.qc = a.pair_q[pi];
-      b.kc = a.pair_k[pi];
-      b.qt = b.qc * a.tiles + j;
-      // first use of a peer's chunk by this workgroup: its rows were written
-      // by a copy engine during the launch
-      const uint32_t need = (1u << b.qc) | (1u << b.kc);
-      if (a.arrived != nullptr && (need & ~acquired)) {
-        uint32_t peers = need & ~acquired & ~(1u << a.local);
-        if (peers) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
-        acquired |= need;
-      }
-      return b;
+    }
+    if (!any_left) return Blk{0, -1, 0, 0, 0};                     // every unit claimed
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) best = max(best, __shfl_xor(best, off));
+    best = __builtin_amdgcn_readfirstlane(best);
+    if (best >= 0) {
+      const int cand = 127 - (best & 127);
+      const int s = cand / QS_GROUPS, g = cand % QS_GROUPS;
+      uint32_t k = 0;
+      if (lane == 0) k = fetch_add_relaxed(a.ws32 + QS_LINE * g + s, 1u);
+      k = __builtin_amdgcn_readfirstlane(k);
+      const uint32_t u = k * QS_GROUPS + (uint32_t)g;
+      if (u >= (uint32_t)a.stage_units[s]) continue;                 // lost the race: look again
+      return decode_unit(a, s, u, acquired);
     }
     if (wait_from == 0) wait_from = now_ticks();
     bool out = false;
@@ -168,38 +252,37 @@ __device__ Blk qsa_claim(const QsaArgs &a, uint32_t &acquired, uint64_t &wait_fr
   }
 }
 
-// Conversion unit (c, h, p): the value rows of key tiles 2p and 2p + 1 of
-// chunk c, head h, converted to fp16 and transposed into the image a block
-// copies to LDS.  Per key tile the image is [d][64 keys]; 16-byte piece P of
-// row d holds the keys of k-group P = 4 k2 + g, in the order the score
-// fragments hold them (32 k2 + 4 g + 0..3, then 32 k2 + 16 + 4 g + 0..3),
-// and sits at piece P ^ (d % 8), so the fragment reads of 8 rows fall on 8
-// distinct bank groups.  Thread t: key tile 2p + t / 128, k-group t % 8,
-// head dims 8 ((t / 8) % 16) .. + 8.  Stores are written through.
-__device__ __forceinline__ void qsa_convert(const QsaArgs &a, int c, int h, int p) {
+// Conversion unit (c, h, t): the value rows of key tile t of chunk c, head
+// h, converted to fp16 and transposed into the image a block copies to LDS.
+// The image of a key tile is [d][64 keys]; 16-byte piece P of row d holds
+// the keys of k-group P = 4 k2 + g, in the order the score fragments hold
+// them (32 k2 + 4 g + 0..3, then 32 k2 + 16 + 4 g + 0..3), and sits at
+// piece P ^ (d % 8), so the fragment reads of 8 rows fall on 8 distinct bank
+// groups.  Thread i: k-group i % 8, head dims 4 (i / 8) .. + 4.  Stores are
+// written through.
+__device__ __forceinline__ void qsa_convert(const QsaArgs &a, int c, int h, int t) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
-  const int kg = tid & 7, dg = (tid >> 3) & 15;
+  const int kg = tid & 7, dg = tid >> 3;
   const int k2 = kg >> 2, g = kg & 3;
   const int HD = a.H * QSA_D;
   const int64_t RS = 3 * (int64_t)HD;
-  const int kt = 2 * p + (tid >> 7);                               // key tile within the chunk
-  const int64_t row0 = (int64_t)c * a.chunk + (int64_t)kt * QSA_BKV;
-  const uint16_t *src = a.qkv + row0 * RS + 2 * HD + h * QSA_D + dg * 8;
-  bf16x8 v[8];
+  const int64_t row0 = (int64_t)c * a.chunk + (int64_t)t * QSA_BKV;
+  const uint16_t *src = a.qkv + row0 * RS + 2 * HD + h * QSA_D + dg * 4;
+  bf16x4 v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int key = 32 * k2 + 4 * g + (i < 4 ? i : 12 + i);
-    v[i] = *reinterpret_cast<const bf16x8 *>(src + (int64_t)key * RS);
+    v[i] = *reinterpret_cast<const bf16x4 *>(src + (int64_t)key * RS);
   }
-  uint16_t *dst = a.vt + ((int64_t)h * (a.S / QSA_BKV) + (int64_t)c * (a.chunk / QSA_BKV) + kt) * (QSA_D * QSA_BKV);
+  uint16_t *dst = a.vt + ((int64_t)h * (a.S / QSA_BKV) + (int64_t)c * (a.chunk / QSA_BKV) + t) * (QSA_D * QSA_BKV);
 #pragma unroll
-  for (int d = 0; d < 8; ++d) {
+  for (int e = 0; e < 4; ++e) {
     f16x8 piece;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) piece[i] = (_Float16)(float)v[i][d];
-    const int row = dg * 8 + d;
-    store_wt16(dst + row * QSA_BKV + ((kg ^ d) << 3), __builtin_bit_cast(f32x4, piece));
+    for (int i = 0; i < 8; ++i) piece[i] = (_Float16)(float)v[i][e];
+    const int row = dg * 4 + e;
+    store_wt16(dst + row * QSA_BKV + ((kg ^ (row & 7)) << 3), __builtin_bit_cast(f32x4, piece));
   }
 }
 
@@ -459,10 +542,11 @@ __global__ void __launch_bounds__(QS_THREADS, 2) __attribute__((amdgpu_num_vgpr(
   asm volatile("" :: "v"(lds) : "memory");
   if (blockIdx.x == 0 && tid == 0 && a.stamps) store_u64_relaxed(a.stamps + 2 * a.R, now_ticks());
   uint32_t acquired = 0;
+  int taken = 0;
   uint64_t wait_from = 0;
   for (;;) {
     if (wave == 0) {
-      const Blk b = qsa_claim(a, acquired, wait_from);
+      const Blk b = qsa_claim(a, acquired, wait_from, taken);
       if (lane == 0) s_blk = b;
     }
     __syncthreads();
@@ -485,7 +569,7 @@ __global__ void __launch_bounds__(QS_THREADS, 2) __attribute__((amdgpu_num_vgpr(
     if (tid == 0) {
       const uint32_t *cc = a.ws32 + a.conv_off + b.kc * a.H + b.h;
       const uint64_t t0 = now_ticks();
-      while (load_relaxed(cc) < (uint32_t)a.tiles) {
+      while (load_relaxed(cc) < (uint32_t)(a.chunk / QSA_BKV)) {
         if (load_relaxed(a.ws32 + QS_ABORT) != 0u) break;
         if (now_ticks() - t0 > a.timeout_ticks) {
           if (a.status) __hip_atomic_store(a.status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -533,9 +617,11 @@ __global__ void __launch_bounds__(QS_THREADS, 2) __attribute__((amdgpu_num_vgpr(
       for (int g = 0; g < XCDS; ++g) store_relaxed_agent(a.ws32 + QS_EXITED_X + g, 0u);
       if (load_relaxed_agent(a.ws32 + QS_ABORT) != 0u)
         for (int t = 0; t < a.H * (a.S / QSA_BQ); ++t) store_relaxed_agent(a.ws32 + QSA_DONE + t, 0u);
-      for (int s = 0; s < a.R; ++s) store_relaxed_agent(a.ws32 + s, 0u);
+      for (int g = 0; g < QS_GROUPS; ++g)
+        for (int t = 0; t < a.R; ++t) store_relaxed_agent(a.ws32 + QS_LINE * g + t, 0u);
       for (int t = 0; t < a.R * a.H; ++t) store_relaxed_agent(a.ws32 + a.conv_off + t, 0u);
       store_relaxed_agent(a.ws32 + QS_COMBINED, 0u);
+      store_relaxed_agent(a.ws32 + QS_NEXT, 0u);
       store_relaxed_agent(a.ws32 + QS_ABORT, 0u);
       store_relaxed_agent(a.ws32 + QS_EXITED, 0u);
     }
