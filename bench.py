@@ -326,11 +326,13 @@ def _tail_ag_sub(fo, cfg, hz, staging, x, w, y, sub, reps, link_bw, split, sprea
         for q in locals_:
             flags[q] = e            # the local rows are present
         torch.cuda.synchronize()
+        # The launch goes first: with many messages the emulation's enqueue
+        # can block the host until its gate (this launch's start) opens.
+        fo.fo_ag_gemm(x, w, y, fo.Schedule(nchunks=R2, local=locals_[0], order=order, arrived=flags, epoch=e,
+                                           stamps=gs, timeout_ns=5_000_000_000, split=split), ws)
         with torch.cuda.stream(side):
             fo.fo_emulate_arrivals([x[q * mc2:(q + 1) * mc2] for q in peers], [staging[q * mc2:(q + 1) * mc2] for q in peers],
                                    rel, peers, flags, e, es, issue_ns=iss, stream=side, gate=gs[2 * R2:2 * R2 + 1])
-        fo.fo_ag_gemm(x, w, y, fo.Schedule(nchunks=R2, local=locals_[0], order=order, arrived=flags, epoch=e,
-                                           stamps=gs, timeout_ns=5_000_000_000, split=split), ws)
         torch.cuda.synchronize()
         e_st = es.cpu().numpy().astype(np.int64)
         g_st = gs.cpu().numpy().astype(np.int64)
@@ -1023,6 +1025,7 @@ def main():
         tails = {}
         for cfg, key in ((c2, "cfg2_ag_gemm"), (wl.CFG5, "cfg5_qkv_ag_gemm")):
             cg, cg_split, cg_per = chunk_gemm_us(fo, cfg)
+            log(f"  {key} chunk GEMM {cg:.1f} us (split {cg_split})")
             at70 = 2.0 * (cfg.m // cfg.R) * cfg.n * cfg.k / (0.7 * PEAK_BF16_TFLOPS * 1e12) * 1e6
             row = {"chunk_gemm_us": round(cg, 2), "chunk_gemm_split": cg_split, "chunk_gemm_us_per_split": cg_per,
                    "chunk_gemm_at_70pct_peak_us": round(at70, 2)}
@@ -1031,6 +1034,7 @@ def main():
                     continue
                 sp = {}
                 t, span = measure_tail_ag(fo, cfg, hz, sched, spread=sp)
+                log(f"  {key} {sched}: tail {t:.1f} us")
                 row[sched + "_us"] = round(t, 2)
                 row[sched + "_p10_p90_us"] = [sp["p10"], sp["p90"]]
                 row["last_arrival_us"] = round(span, 1)
@@ -1048,6 +1052,7 @@ def main():
             assert p_order == order + [cfg.local]   # the default priority
             sp = {}
             t, _ = measure_tail_ag(fo, cfg, hz, "flashoverlap", split=p_split, spread=sp)
+            log(f"  {key} planned split {p_split[order[-1]]}: tail {t:.1f} us")
             row["planned_split"] = p_split[order[-1]]
             row["planned_us"] = round(t, 2)
             row["planned_p10_p90_us"] = [sp["p10"], sp["p90"]]

@@ -112,9 +112,11 @@ typedef struct fo_schedule {
   int32_t         max_workgroups; /* 0 = auto.  GEMM calls cap it at one
                                      workgroup per CU (the persistent grid
                                      must be resident at once; larger values
-                                     act as the cap).  fo_chunk_reduce may
-                                     exceed it so no workgroup owns more than
-                                     1 GiB.                                    */
+                                     act as the cap).  fo_chunk_reduce: auto
+                                     is one workgroup per CU with `arrived`
+                                     (all resident while they wait) and 8
+                                     per CU without; it may exceed the value
+                                     so no workgroup owns more than 1 GiB.     */
   int32_t         reserved;
 } fo_schedule;
 
@@ -347,6 +349,10 @@ fo_status fo_emulate_arrivals(void *const *dst, const void *const *src,
  * there.  With gate = the consumer kernel's start stamp (stamps[2R] of a
  * GEMM call, zeroed before the call) the emulated peers start sending when
  * the consumer starts, however long the host takes to enqueue the arrivals.
+ * Each message is three operations on `stream`; with many messages the
+ * runtime's queue fills and this call blocks the host until operations
+ * retire, which the timer's gate holds back: enqueue the consumer before
+ * the arrivals (or the host waits out the gate's timeout).
  * gate NULL behaves as fo_emulate_arrivals.  Errors as fo_emulate_arrivals. */
 fo_status fo_emulate_arrivals_gated(const uint64_t *gate, uint64_t gate_timeout_ns,
                                     void *const *dst, const void *const *src,

@@ -775,11 +775,14 @@ fo_status fo_chunk_reduce(void *dst, fo_dtype dst_dtype, const float *const *src
   a.status = s->status;
   a.stamps = s->stamps;
 
-  // 8 workgroups of 256 threads per CU, 8 vectors of every source per lane
-  // per step: the most bytes in flight measured best (8 x 2^27 sources:
-  // 5.7 TB/s, against 5.1 with 4 workgroups and 2 vectors); their registers
-  // still leave wave slots for the emulator's one-wave kernels.
-  int grid = s->max_workgroups > 0 ? s->max_workgroups : I->cus * 8;
+  // 8 vectors of every source per lane per step: the most bytes in flight
+  // measured best (8 x 2^27 sources: 5.7 TB/s, against 5.1 with 2 vectors).
+  // Those registers leave room for one workgroup per CU (and for the
+  // emulator's one-wave kernels beside it).  Without flags the grid is 8
+  // workgroups per CU, run one after another on each CU; with flags every
+  // workgroup must be resident (each waits for its sources in passes), so
+  // the grid is one per CU.
+  int grid = s->max_workgroups > 0 ? s->max_workgroups : (a.arrived ? I->cus : I->cus * 8);
   const int64_t min_per = 256 * 8;   // one full step of the workgroup
   // a workgroup's range is addressed with 32-bit byte offsets (at most 1 GiB
   // per workgroup; the grid grows past max_workgroups if it must)

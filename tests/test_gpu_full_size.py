@@ -380,11 +380,13 @@ def test_tp8_mlp_ag_streamed_planned_schedule_int(fo, orc):
         torch.cuda.synchronize()
         log(f"case: cfg2 int streamed in {sub} messages, last piece split {max(split)}")
         side = side_stream()
+        # the launch first: enqueueing many gated messages can block the host
+        # until the gate (the launch's start) opens
+        fo.fo_ag_gemm(x, w, y, fo.Schedule(nchunks=R2, local=locals_[0], order=order, arrived=flags, epoch=e,
+                                           stamps=gs, status=status, split=split, timeout_ns=5_000_000_000), ws)
         with torch.cuda.stream(side):
             fo.fo_emulate_arrivals([x[p * mc2:(p + 1) * mc2] for p in peers], [staging[p * mc2:(p + 1) * mc2] for p in peers],
                                    [land[p] for p in peers], peers, flags, e, es, stream=side, gate=gs[2 * R2:2 * R2 + 1])
-        fo.fo_ag_gemm(x, w, y, fo.Schedule(nchunks=R2, local=locals_[0], order=order, arrived=flags, epoch=e,
-                                           stamps=gs, status=status, split=split, timeout_ns=5_000_000_000), ws)
         torch.cuda.synchronize()
         assert int(status.item()) == 0
         assert int(ws[:4096].sum()) == 0
