@@ -802,6 +802,27 @@ def reduce_rate(fo, cfg, reps=10):
     return nbytes / (ms * 1e-3) / 1e9, ms
 
 
+def library_gemm_us(m, n, k, launches=30):
+    """The vendor library's bf16 GEMM on the same shape (torch.matmul, X @ W^T
+    with W stored [n][k] as here, bf16 out): average us over launches in a
+    row.  A reference for what this GPU sustains on the shape, not the
+    product path."""
+    import torch
+    x = torch.randn(m, k, device="cuda", dtype=torch.bfloat16)
+    w = torch.randn(n, k, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        x @ w.t()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(launches):
+        x @ w.t()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / launches
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -899,6 +920,48 @@ def back_to_back_us(fo, path, which, launches=50):
     return a.elapsed_time(b) * 1e3 / launches
 
 
+def profile_kernels(fo, names, launches):
+    """Launch the named workloads `launches` times each (all inputs present)
+    and nothing else, for profiler runs."""
+    import torch
+    names = ["step", "reduce4", "a2a", "qsa"] if names == "all" else names.split(",")
+    for nm in names:
+        if nm == "step":
+            path = Path(fo)
+            for _ in range(launches):
+                path.step()
+        elif nm == "reduce4":
+            c4 = wl.CFG4
+            srcs = [torch.randn(c4.n, device="cuda") * 1e-3 for _ in range(c4.R)]
+            for i in range(launches):
+                fo.fo_chunk_reduce(srcs[0], srcs, fo.Schedule(nchunks=c4.R, epoch=1 + i))
+            torch.cuda.synchronize()
+            del srcs
+        elif nm == "a2a":
+            a2a_rate(fo, wl.CFG6, launches=launches)
+        elif nm == "qsa":
+            qsa_rate(fo, wl.CFG7, launches=launches)
+        else:
+            raise SystemExit(f"unknown workload {nm}")
+        torch.cuda.synchronize()
+        log(f"profiled workload {nm}: {launches} launches")
+
+
+def sustain(fo, seconds):
+    """The step's AG-GEMM back to back for `seconds` (clock sampling under load)."""
+    path = Path(fo)
+    t_end = time.perf_counter() + seconds
+    n = 0
+    next_log = time.perf_counter() + 1.0
+    while time.perf_counter() < t_end:
+        us = back_to_back_us(fo, path, "ag_gemm", launches=200)
+        n += 200
+        if time.perf_counter() >= next_log:
+            log(f"sustain: {n} AG-GEMM launches, {us:.1f} us each")
+            next_log += 1.0
+    log(f"sustain done: {n} launches in {seconds:.1f} s")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -913,6 +976,14 @@ def main():
                          "by their order: fo_ag_gemm, fo_gemm_rs, ...)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB copy (for scaling profiled byte counters)")
+    ap.add_argument("--profile-kernels", default="",
+                    help="launch only these workloads, --launches times each, for a profiler run: "
+                         "comma list of step (AG-GEMM, GEMM-RS, reduce of the TP=8 MLP share), reduce4 "
+                         "(DP gradient reduce), a2a (Ulysses all-to-all GEMM), qsa (TP=4 attention), or all")
+    ap.add_argument("--launches", type=int, default=5)
+    ap.add_argument("--sustain", type=float, default=0.0,
+                    help="launch the AG-GEMM of the step back to back for this many seconds (to sample "
+                         "the clocks under load), printing a line every second")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU's share of the path and runs on one GPU only; the "
@@ -927,6 +998,14 @@ def main():
     log(f"device: {torch.cuda.get_device_name(0)} CUs={cus} LDS/CU={lds} wall_clock={hz} Hz")
 
     side_stream()   # created first, so it gets a hardware queue of its own
+    if args.profile_kernels:
+        profile_kernels(fo, args.profile_kernels, args.launches)
+        if args.copy_calibration:
+            copy_calibration()
+        return
+    if args.sustain > 0:
+        sustain(fo, args.sustain)
+        return
     path = Path(fo)
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -957,6 +1036,9 @@ def main():
     d_flops, d_ms, d_what = launches[dom]
     achieved = d_flops / (d_ms * 1e-3) / 1e12
     log(f"back to back: ag {b2b['ag_gemm']:.1f} us, rs {b2b['gemm_rs']:.1f} us")
+    lib_ag = library_gemm_us(c2.m, c2.n, c2.k)
+    lib_rs = library_gemm_us(c3.m, c3.n, c3.k)
+    log(f"library GEMM on the same shapes: ag {lib_ag:.1f} us, rs {lib_rs:.1f} us")
     log(f"step {ms_step * 1e3:.1f} us: ag {ag_ms * 1e3:.1f} us, rs {rs_ms * 1e3:.1f} us, "
         f"reduce {red_ms * 1e3:.1f} us")
 
@@ -994,6 +1076,11 @@ def main():
             "kernel": f"gemm_kernel, {d_what} launch", "launch_us": round(d_ms * 1e3, 2),
             "flops_per_launch": d_flops,
             "timing": "HIP events around 50 launches in a row on the launch stream",
+        },
+        "library_reference": {
+            "what": "torch.matmul (hipBLASLt) bf16 GEMM on the same shapes, launches in a row",
+            "ag_gemm_shape_us": round(lib_ag, 2), "ag_gemm_shape_tflops": round(f_ag / lib_ag / 1e6, 1),
+            "gemm_rs_shape_us": round(lib_rs, 2), "gemm_rs_shape_tflops": round(f_rs / lib_rs / 1e6, 1),
         },
         "pages_context": {
             "training_time_reduction": "up to 25% shorter training time, no hardware added",

@@ -7,8 +7,13 @@
         ``bench.py --copy-calibration``, each counter scaled by what it reads
         for the plain copy of known size that run ends with
     python -m sp_rank_adaptive_amd.profsum counters DIR OUT.md --cmd "..."
-        MFMA busy fraction, bf16 MFMA flops and LDS bank-conflict rate per
-        GEMM launch from an SQ/GRBM counter run
+        MFMA busy fraction, bf16/fp16 MFMA flops, LDS bank-conflict rate and
+        VALU instructions per wave per GEMM launch from an SQ/GRBM counter run
+
+    traffic and counters take --kernel SUBSTR --label NAME to summarise
+    every dispatch whose kernel name holds SUBSTR instead of the bench
+    step's GEMMs; traffic then needs --algo-bytes N (algorithmic bytes per
+    launch) and --source FILE (the csrc file whose hash is recorded).
 
 In a ``bench.py`` step the GEMM launches come in the order fo_ag_gemm,
 fo_gemm_rs; the summaries name them by that order.
@@ -63,8 +68,15 @@ def _per_dispatch(rows):
     return [out[d] for d in sorted(out)]
 
 
-def _gemm_launches(disp):
-    """Counter dicts of the GEMM dispatches, grouped by launch name."""
+def _gemm_launches(disp, select=None):
+    """Counter dicts of the profiled dispatches, grouped by launch name: by
+    default the GEMM dispatches of bench steps (fo_ag_gemm, fo_gemm_rs in
+    turn); with select = (kernel-name substring, label), every dispatch whose
+    name holds the substring, under that label."""
+    if select is not None:
+        sub, label = select
+        hits = [(n, v) for n, v in disp if sub in n]
+        return {label: [v for _, v in hits]}, {label: hits[0][0] if hits else None}
     g = [v for n, v in disp if "gemm_kernel" in n]
     names = [n for n, _ in disp if "gemm_kernel" in n]
     res = {k: [] for k in LAUNCHES}
@@ -78,18 +90,27 @@ def _gemm_launches(disp):
 
 def cmd_stats(d, out_md, cmd):
     rows = _rows(_one(d, "_kernel_stats.csv"))
+    med = {}
+    hits = sorted(glob.glob(os.path.join(d, "**", "*_kernel_trace.csv"), recursive=True))
+    if hits:
+        per = {}
+        for r in _rows(hits[0]):
+            per.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        med = {k: statistics.median(v) for k, v in per.items()}
     lines = ["# Kernel durations (rocprofv3 --kernel-trace --stats)", "", "Command:", "",
              "```", cmd, "```", "",
-             "| kernel | calls | average us | min us | max us | share % |",
-             "|---|---:|---:|---:|---:|---:|"]
+             "| kernel | calls | average us | median us | min us | max us | share % |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
     for r in rows:
+        m = med.get(r["Name"])
         lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{(m / 1e3) if m is not None else float('nan'):.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.1f} |")
     _write(out_md, "\n".join(lines) + "\n")
 
 
-def cmd_traffic(fetch_dir, write_dir, out_json, out_md, cmd):
+def cmd_traffic(fetch_dir, write_dir, out_json, out_md, cmd, select=None, algo=None, src=GEMM_SRC):
     res = {}
     scale = {}
     for key, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -99,12 +120,15 @@ def cmd_traffic(fetch_dir, write_dir, out_json, out_md, cmd):
             raise SystemExit(f"{key}: no calibration copy in {d}")
         kib = statistics.median(copies)
         scale[key] = COPY_BYTES / (kib * 1024.0)
-        launches, kern = _gemm_launches(disp)
+        launches, kern = _gemm_launches(disp, select)
         for k, vals in launches.items():
             res.setdefault(k, {"kernel": kern.get(k)})
             res[k][key + "_KiB_median"] = statistics.median(v[key] for v in vals)
             res[k]["dispatches"] = len(vals)
-    out = {"kernel_source_sha256_16": source_hash(), "copy_bytes": COPY_BYTES,
+    algo_bytes = dict(ALGO_BYTES)
+    if select is not None:
+        algo_bytes[select[1]] = algo
+    out = {"kernel_source": os.path.basename(src), "kernel_source_sha256_16": source_hash(src), "copy_bytes": COPY_BYTES,
            "scale": {k: round(v, 5) for k, v in scale.items()}, "launches": {}}
     for k, r in res.items():
         fb = r["FETCH_SIZE_KiB_median"] * 1024 * scale["FETCH_SIZE"]
@@ -112,17 +136,17 @@ def cmd_traffic(fetch_dir, write_dir, out_json, out_md, cmd):
         out["launches"][k] = {"kernel": r["kernel"], "dispatches": r["dispatches"],
                               "fetch_bytes": int(fb), "write_bytes": int(wb),
                               "bytes_per_launch": int(fb + wb),
-                              "algorithmic_bytes": ALGO_BYTES[k],
-                              "over_algorithmic": round((fb + wb) / ALGO_BYTES[k], 3)}
+                              "algorithmic_bytes": algo_bytes[k],
+                              "over_algorithmic": round((fb + wb) / algo_bytes[k], 3)}
     out["command"] = cmd
     _write(out_json, json.dumps(out, indent=1) + "\n")
-    lines = ["# HBM traffic per GEMM launch (FETCH_SIZE, WRITE_SIZE)", "", "Command:", "",
+    lines = ["# HBM traffic per launch (FETCH_SIZE, WRITE_SIZE)", "", "Command:", "",
              "```", cmd, "```", "",
              f"Calibration: a {COPY_BYTES >> 20} MiB device copy reads as "
              f"{COPY_BYTES / scale['FETCH_SIZE'] / 1024:.0f} KiB FETCH_SIZE and "
              f"{COPY_BYTES / scale['WRITE_SIZE'] / 1024:.0f} KiB WRITE_SIZE, so the counters are "
              f"scaled by {scale['FETCH_SIZE']:.4f} and {scale['WRITE_SIZE']:.4f}.", "",
-             f"fo_gemm.hip sha256[:16] = `{out['kernel_source_sha256_16']}`", "",
+             f"{out['kernel_source']} sha256[:16] = `{out['kernel_source_sha256_16']}`", "",
              "| launch | kernel | fetch MiB | write MiB | total MiB | algorithmic MiB | ratio |",
              "|---|---|---:|---:|---:|---:|---:|"]
     for k, r in out["launches"].items():
@@ -132,18 +156,19 @@ def cmd_traffic(fetch_dir, write_dir, out_json, out_md, cmd):
     _write(out_md, "\n".join(lines) + "\n")
 
 
-def cmd_counters(d, out_md, cmd, simds=1024, clock_hz=2.4e9):
+def cmd_counters(d, out_md, cmd, simds=1024, clock_hz=2.4e9, select=None):
     disp = _per_dispatch(_rows(_one(d, "_counter_collection.csv")))
-    launches, kern = _gemm_launches(disp)
-    lines = ["# GEMM counters (MFMA busy, bf16 MFMA flops, LDS bank conflicts)", "", "Command:", "",
+    launches, kern = _gemm_launches(disp, select)
+    lines = ["# MFMA and LDS counters (MFMA busy, bf16/fp16 MFMA flops, LDS bank conflicts, VALU)", "", "Command:", "",
              "```", cmd, "```", "",
              "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x 2.4 GHz x dispatch duration in "
              "this counter run); bf16 flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; LDS conflict = "
              "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.  Each 16x16x32 bf16 MFMA counts 16 busy "
              "cycles, so the busy fraction equals the fraction of dense bf16 peak reached during "
              "the dispatch.", "",
-             "| launch | kernel | dispatch us | MFMA busy % | bf16 GFLOP | LDS conflict % | dispatches |",
-             "|---|---|---:|---:|---:|---:|---:|"]
+             "| launch | kernel | dispatch us | MFMA busy % | bf16 GFLOP | fp16 GFLOP | LDS conflict % | "
+             "VALU instr / wave | dispatches |",
+             "|---|---|---:|---:|---:|---:|---:|---:|---:|"]
     for k, vals in launches.items():
         if not vals:
             continue
@@ -151,9 +176,11 @@ def cmd_counters(d, out_md, cmd, simds=1024, clock_hz=2.4e9):
         dur = med(lambda v: v["_ns"])
         busy = med(lambda v: v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / (simds * clock_hz * v["_ns"] * 1e-9))
         fl = med(lambda v: v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0) * 512 / 1e9)
+        fl16 = med(lambda v: v.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0) * 512 / 1e9)
         conf = med(lambda v: v.get("SQ_LDS_BANK_CONFLICT", 0) / max(v.get("SQ_LDS_IDX_ACTIVE", 1), 1))
-        lines.append(f"| {k} | `{kern[k]}` | {dur / 1e3:.1f} | {100 * busy:.1f} | {fl:.2f} | "
-                     f"{100 * conf:.2f} | {len(vals)} |")
+        valu = med(lambda v: v.get("SQ_INSTS_VALU", 0) / max(v.get("SQ_WAVES", 1), 1))
+        lines.append(f"| {k} | `{kern[k]}` | {dur / 1e3:.1f} | {100 * busy:.1f} | {fl:.2f} | {fl16:.2f} | "
+                     f"{100 * conf:.2f} | {valu:.0f} | {len(vals)} |")
     _write(out_md, "\n".join(lines) + "\n")
 
 
@@ -163,20 +190,30 @@ def _write(path, text):
     print(f"wrote {path}")
 
 
+def _opt(argv, name):
+    if name in argv:
+        i = argv.index(name)
+        return argv[i + 1], argv[:i] + argv[i + 2:]
+    return None, argv
+
+
 def main(argv):
-    cmd = ""
-    if "--cmd" in argv:
-        i = argv.index("--cmd")
-        cmd = argv[i + 1]
-        argv = argv[:i] + argv[i + 2:]
+    cmd, argv = _opt(argv, "--cmd")
+    kernel, argv = _opt(argv, "--kernel")
+    label, argv = _opt(argv, "--label")
+    algo, argv = _opt(argv, "--algo-bytes")
+    src, argv = _opt(argv, "--source")
+    cmd = cmd or ""
+    select = (kernel, label or kernel) if kernel else None
     if not argv:
         raise SystemExit(__doc__)
     if argv[0] == "stats" and len(argv) == 3:
         cmd_stats(argv[1], argv[2], cmd)
     elif argv[0] == "traffic" and len(argv) == 5:
-        cmd_traffic(argv[1], argv[2], argv[3], argv[4], cmd)
+        cmd_traffic(argv[1], argv[2], argv[3], argv[4], cmd, select, int(algo) if algo else None,
+                    os.path.join(HERE, "csrc", src) if src else GEMM_SRC)
     elif argv[0] == "counters" and len(argv) == 3:
-        cmd_counters(argv[1], argv[2], cmd)
+        cmd_counters(argv[1], argv[2], cmd, select=select)
     else:
         raise SystemExit(__doc__)
 
