@@ -19,6 +19,7 @@ constexpr int kMaxDevices = 64;
 constexpr uint64_t kDefaultTimeoutNs = 10ull * 1000 * 1000 * 1000;
 constexpr int kMaxSplit = 8;
 constexpr int kMinSplitStages = 16;   // automatic split: k stages per split, at least
+constexpr int kMinSelfSplit = 4;     // split units sum their own slices only from this split up
 // Largest k: a tile's operand rows (at most 256 of them) are addressed with
 // 32-bit byte offsets, and an offset of 2^30 past a row block must lie beyond
 // it (it stands for "k past the end", which reads as zero).
@@ -224,18 +225,29 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
   a.mc = (int32_t)p.mc;
   a.tiles_m = p.tiles_m;
   a.tiles_n = p.tiles_n;
-  // Rectangles of each chunk's tile grid, one per XCD: the shape that
-  // minimises the operand rows one XCD streams over all R chunks (X rows of
-  // its row band in every chunk plus W rows of its column band).
+  // Rectangles of each chunk's tile grid, one per XCD: among the shapes
+  // whose largest rectangle holds the fewest tiles (an XCD with more tiles
+  // than the others makes its neighbours' workgroups steal one contended
+  // claim at a time), the one that minimises the operand rows one XCD
+  // streams over all R chunks (X rows of its row band in every chunk plus W
+  // rows of its column band).
   {
     const int shapes[4][2] = {{1, 8}, {2, 4}, {4, 2}, {8, 1}};
-    int64_t best = -1;
+    int64_t best[3] = {-1, -1, -1};   // empty rectangles, largest rectangle, cost
     for (const auto &sh : shapes) {
       const int gm = sh[0], gn = sh[1];
-      int64_t cost = (int64_t)R * ((p.tiles_m + gm - 1) / gm) * p.tile.bm +
-                     (int64_t)((p.tiles_n + gn - 1) / gn) * p.tile.bn;
-      if (gm > p.tiles_m || gn > p.tiles_n) cost += (int64_t)1 << 40;   // empty rectangles
-      if (best < 0 || cost < best) { best = cost; a.gm = gm; a.gn = gn; }
+      const int64_t key[3] = {(gm > p.tiles_m || gn > p.tiles_n) ? 1 : 0,
+                              (int64_t)((p.tiles_m + gm - 1) / gm) * ((p.tiles_n + gn - 1) / gn),
+                              (int64_t)R * ((p.tiles_m + gm - 1) / gm) * p.tile.bm +
+                                  (int64_t)((p.tiles_n + gn - 1) / gn) * p.tile.bn};
+      bool better = best[0] < 0;
+      for (int q = 0; q < 3 && !better; ++q) {
+        if (key[q] != best[q]) { better = key[q] < best[q]; break; }
+      }
+      if (better) {
+        for (int q = 0; q < 3; ++q) best[q] = key[q];
+        a.gm = gm; a.gn = gn;
+      }
     }
     for (int g = 0; g < XCDS; ++g) {
       const int i = g / a.gn, j = g % a.gn;
@@ -303,6 +315,37 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
       a.part_base[c] = -1;
     }
     total_units += a.units[c] + a.red_units[c];
+  }
+  // Split chunks without reduce units: each split unit sums its own row
+  // slices of its tile once the tile's splits are all written, so no
+  // workgroup claims a reduce unit on one shared counter after the GEMM
+  // units.  A unit then waits for the other splits of its tile.  The claimed
+  // units of each XCD group form a prefix of the group's split-fastest
+  // numbering, so at most S - 1 units per group and split chunk wait at a
+  // time; with at least XCDS x (sum of the splits) workgroups some workgroup
+  // is always free to claim the rest (and under round-robin assignment each
+  // XCD has at least S workgroups, so a tile spans at most two rounds).
+  // A split of 2 or 3 leaves each unit a third or more of its tile to sum,
+  // one round trip per few rows: there reduce units on the idle workgroups
+  // were faster (measured on the TP=8 MLP chunk alone), so every split
+  // chunk must be split at least kMinSelfSplit ways.
+  a.self_reduce = 0;
+  if (!fz) {
+    int64_t units = 0, split_sum = 0;
+    bool deep = true;
+    for (int c = 0; c < R; ++c) {
+      units += a.units[c];
+      if (a.split[c] > 1) {
+        split_sum += a.split[c];
+        deep = deep && a.split[c] >= kMinSelfSplit;
+      }
+    }
+    const int64_t g = units < grid_cap ? units : grid_cap;
+    if (split_sum > 0 && deep && g >= (int64_t)XCDS * split_sum && tile_self_reduce(p.tile)) {
+      a.self_reduce = 1;
+      total_units = units;
+      for (int c = 0; c < R; ++c) a.red_units[c] = 0;
+    }
   }
   if (fz) {
     // Direct form: the local chunk's tiles get shard units (RED_SLICES row
@@ -378,9 +421,10 @@ fo_status run_gemm(const void *x, const void *w, void *y, bool y_bf16, uint32_t 
     // claiming until no work is left.
     a.one_unit = (a.arrived != nullptr && ok && single) ? 1 : 0;
   }
-  // A launch whose claims are all static, with no reduce units, flags or
-  // stamps, touches no counter: its workgroups skip the exit count too.
-  a.no_counters = (a.static_rr != 0 && !fz && !done && !s->stamps) ? 1 : 0;
+  // A launch whose claims are all static, with no split chunks, reduce
+  // units, flags or stamps, touches no counter: its workgroups skip the exit
+  // count too.
+  a.no_counters = (a.static_rr != 0 && a.all_unsplit && !fz && !done && !s->stamps) ? 1 : 0;
   if (fz) {
     // shard units are assigned statically (workgroup b takes b, b + grid,
     // ... of each chunk with shard units, in priority order) only when every

@@ -546,6 +546,67 @@ __device__ __forceinline__ void reduce_unit(const GemmArgs &a, int c, int tile, 
   }
 }
 
+// Split unit sp of a split tile when split units reduce their own slices:
+// sums row slices sp, sp + S, ... (of RED_SLICES) over the tile's S partials
+// in split order 0..S-1, as reduce units would, and stores the output rows.
+// With own_lds the unit's own partial rows come from its LDS staging (row
+// stride SROW floats; the unit did not write them out), the other splits'
+// rows from memory with system-coherent loads.  Each thread issues the loads
+// of U pieces for every partial before it adds, so the slices cost a round
+// trip per U pieces rather than one per slice.  One instance for every S (a
+// switch over S instances displaced the k-loop's registers).
+template <int BM, int BN, int NTT, int SROW>
+__device__ __forceinline__ void reduce_own_slices(const GemmArgs &a, int c, int tile, int sp, int64_t row0,
+                                                  int64_t rowlim, int64_t col0, const float *stg, bool own_lds) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));   // computed per unit, not kept live across the loop
+  const int64_t N = a.n;
+  const int S = a.split[c];
+  const float *P = a.partials + ((size_t)a.part_base[c] + (size_t)tile * S) * (size_t)(BM * BN);
+  constexpr int ROWS = BM / RED_SLICES;
+  constexpr int PPR = BN / 4;                       // 16-byte pieces per row
+  constexpr int PPS = ROWS * PPR;                   // pieces per slice
+  constexpr int SMAX = 8;                           // largest split
+  constexpr int U = 2;                              // pieces per thread per batch (3 or more put
+                                                    // scratch traffic into the 128x224 k-loop)
+  const int npc = ((RED_SLICES - sp + S - 1) / S) * PPS;
+  const bool vec_ok = (N & 3) == 0;
+  const bool wt = a.done_flags != nullptr;
+  const __amdgpu_buffer_rsrc_t rp = uniform_rsrc(P, S * BM * BN * 4);
+  for (int base = tid; base < npc; base += U * NTT) {
+    f32x4 t[U][SMAX];
+    int rr[U], cc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int pc = base + u * NTT;
+      const int j = pc / PPS, w = pc - (pc / PPS) * PPS;
+      rr[u] = (sp + j * S) * ROWS + w / PPR;
+      cc[u] = w - (w / PPR) * PPR;
+      const int off = (rr[u] * BN + cc[u] * 4) * 4;
+#pragma unroll
+      for (int q = 0; q < SMAX; ++q) {
+        t[u][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (q < S && pc < npc && !(own_lds && q == sp))
+          t[u][q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, off + q * (BM * BN * 4), 0, 1 | 2));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int pc = base + u * NTT;
+      if (pc >= npc) continue;
+      const f32x4 own = own_lds ? *reinterpret_cast<const f32x4 *>(stg + rr[u] * SROW + cc[u] * 4)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 sum = (own_lds && sp == 0) ? own : t[u][0];
+#pragma unroll
+      for (int q = 1; q < SMAX; ++q)
+        if (q < S) sum = sum + ((own_lds && q == sp) ? own : t[u][q]);
+      const int64_t row = row0 + rr[u];
+      if (row < rowlim && col0 + cc[u] * 4 < N)
+        put4(reinterpret_cast<char *>(a.y), N, row, col0 + cc[u] * 4, N, a.y_bf16 != 0, vec_ok, wt, sum);
+    }
+  }
+}
+
 // Shard unit (fo_gemm_rs_reduce, fo_gemm_rs_ring): row slice `slice` of a
 // tile of chunk c, whose partial is in memory (written through by its unit).
 // Sums the partial and the incoming partials in summation order (fp32, left
@@ -974,6 +1035,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
       // split partials (read by reduce units on any XCD) and GEMM-RS output
       // (read by the consumer of the done flags) are written through
       const bool wt = !to_out || a.done_flags != nullptr || a.fused;
+      // a split unit that sums its own slices keeps them in the LDS staging
+      // (the whole tile is staged in one pass) instead of writing them out
+      const bool own_lds = HALVES == 1 && !to_out && a.self_reduce;
 #pragma unroll
       for (int h = 0; h < HALVES; ++h) {
         __syncthreads();
@@ -991,6 +1055,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
         __syncthreads();
         for (int cidx = etid; cidx < HROWS * CPR; cidx += NTT) {
           const int r = cidx / CPR, cc = cidx - (cidx / CPR) * CPR;
+          if constexpr (HALVES == 1)
+            if (own_lds && ((r / (BM / RED_SLICES)) % S) == sp) continue;   // kept in LDS for this unit's sum
           const int64_t row = rbase + h * HROWS + r;
           const int64_t col = cbase + cc * 4;
           if (row >= rlim || col >= clim) continue;
@@ -1015,11 +1081,46 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a) {
         // of the partials (see the reduce unit).
         wait_stores();
         __syncthreads();
+        // Split units sum their own slices in every layout but the one that
+        // needs every register in its k-loop (RV; the host enables it only
+        // where tile_self_reduce says so): there the wait and the sums
+        // displace the loop's registers.
+        constexpr bool SR = !RV;
+        bool ok = true;
         if (etid == 0) {
-          const uint32_t old = fetch_add_relaxed(a.ws32 + WS_TILE_CTR + a.ctr_base[c] + tile, 1u);
-          if (old == (uint32_t)(S - 1)) {
+          uint32_t *ctr = a.ws32 + WS_TILE_CTR + a.ctr_base[c] + tile;
+          const uint32_t old = fetch_add_relaxed(ctr, 1u);
+          if (SR && a.self_reduce) {
+            // wait for the tile's other splits (running or about to be
+            // claimed by a free workgroup: the claimed units of a group form
+            // a prefix of its split-fastest numbering, so at most S - 1
+            // units per group and split chunk can wait here, and the host
+            // enables this only with more workgroups than that)
+            if (old != (uint32_t)(S - 1)) {
+              const uint64_t t0 = now_ticks();
+              while (load_relaxed_agent(ctr) < (uint32_t)S) {
+                if (load_relaxed(a.ws32 + WS_ABORT) || now_ticks() - t0 > a.timeout_ticks) { ok = false; break; }
+                __builtin_amdgcn_s_sleep(1);
+              }
+              if (!ok) {
+                if (a.status) __hip_atomic_store(a.status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_SYSTEM);
+                __hip_atomic_store(a.ws32 + WS_ABORT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              }
+            }
+          } else if (old == (uint32_t)(S - 1)) {
             const uint32_t idx = fetch_add_relaxed(a.ws32 + WS_RED_READY + c, 1u);
             store_relaxed_agent(a.ws32 + a.ready_off + a.ctr_base[c] + idx, (uint32_t)(tile + 1));
+          }
+        }
+        if constexpr (SR) {
+          if (a.self_reduce) {
+            // The other splits' partials are in memory (thread 0 read the
+            // counter at S before the barrier; they are read with
+            // system-coherent loads): sum this split's row slices in split
+            // order 0..S-1, as a reduce unit would.
+            if (__syncthreads_or(!ok)) break;
+            reduce_own_slices<BM, BN, NTT, SROW>(a, c, tile, sp, row0, rowlim, col0, stg, own_lds);
           }
         }
       }
@@ -1175,6 +1276,10 @@ int64_t max_tiles_per_chunk(int64_t mc, int64_t n) {
 }
 
 size_t partial_slot_bytes(const TileCfg &t) { return (size_t)t.bm * t.bn * sizeof(float); }
+
+// Split units may sum their own slices (GemmArgs::self_reduce) in every
+// compiled layout but 256x256 (RV).
+bool tile_self_reduce(const TileCfg &t) { return !(t.bm == 256 && t.bn == 256); }
 
 hipError_t launch_gemm(const GemmArgs &a, const TileCfg &t, hipStream_t stream) {
   if (t.bm == 256 && t.bn == 256)

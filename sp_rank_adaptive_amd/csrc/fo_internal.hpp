@@ -51,6 +51,8 @@ struct GemmArgs {
   int32_t no_counters;        // static claims, no reduce units, no flags or stamps: no counter is touched
   int32_t all_unsplit;        // 1: no chunk is split
   int32_t one_unit;           // flags: a workgroup whose first claim succeeds leaves after it
+  int32_t self_reduce;        // split chunks have no reduce units: each split unit, once its tile's
+                              // splits are all written, sums row slices sp, sp + S, ... of the tile
   // Fused reduce of the local chunk (fo_gemm_rs_reduce): the local chunk's
   // reduce units sum its partial and the incoming partials into the shard.
   int32_t fused;                      // 1: red_units[c] > 0 are shard units
@@ -174,6 +176,8 @@ int64_t max_padded_tile_area(int64_t mc, int64_t n);
 int64_t max_tiles_per_chunk(int64_t mc, int64_t n);
 
 hipError_t launch_gemm(const GemmArgs &a, const TileCfg &t, hipStream_t stream);
+// Whether the layout of t lets split units sum their own slices (self_reduce).
+bool tile_self_reduce(const TileCfg &t);
 hipError_t launch_reduce(const ReduceArgs &a, int grid, hipStream_t stream);
 
 // Emulator kernels.

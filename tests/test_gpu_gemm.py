@@ -170,6 +170,47 @@ def test_ag_gemm_split_k_exact_and_deterministic(fo, orc):
     assert torch.equal(y1[0:128], y3[0:128]) and torch.equal(y1[256:384], y3[256:384])
 
 
+@pytest.mark.parametrize("R,split,grid", [
+    (1, [4], 0), (1, [8], 0), (1, [4], 32), (1, [4], 40), (1, [8], 72),
+    (4, [1, 4, 1, 8], 0), (4, [1, 4, 1, 8], 96),
+    (1, [2], 0), (4, [1, 4, 1, 2], 56),
+])
+def test_split_units_reduce_own_slices_int_exact(fo, orc, R, split, grid):
+    # With every split at least 4 and at least 8 x (sum of the splits)
+    # workgroups, each split unit sums its own row slices of its tile once
+    # the tile's splits are all written (no reduce units): static first
+    # claims, static round-robin with tiles that span two rounds (grid 40: 5
+    # workgroups per XCD, split 4) and dynamic claims over preset flags.  A
+    # split of 2 goes through reduce units.  Every element is written once
+    # and equals the oracle; the counters return to zero; two runs agree
+    # bitwise.
+    mc, n, k = 512, 1792, 1024
+    m = mc * R
+    xb = wl.bf16_operand((m, k), "int", 0.0, 12101 + R)
+    wb = wl.bf16_operand((n, k), "int", 0.0, 12102)
+    x, w = dev_bf16(xb), dev_bf16(wb)
+    ref = orc.gemm(xb, wb)
+    log(f"case: self-reduce {m}x{n}x{k} R={R} split={split} grid={grid}")
+    # several split chunks need more than the default partial-tile area
+    big = torch.zeros(4 * fo.fo_workspace_bytes(m, n, k, R), dtype=torch.uint8, device="cuda")
+    y, ws = run_ag(fo, x, w, R, ws=big, split=split, max_workgroups=grid)
+    assert not torch.isnan(y).any()
+    check_exact(host(y), ref, f"split {split} grid {grid}")
+    assert int(ws[:4096].sum()) == 0, "counters not returned to zero"
+    flags = torch.full((R,), EP.e + 1, dtype=torch.int32, device="cuda")
+    y2, _ = run_ag(fo, x, w, R, ws=ws, split=split, max_workgroups=grid, arrived=flags)
+    assert not torch.isnan(y2).any()
+    check_exact(host(y2), ref, f"preset flags, split {split} grid {grid}")
+    assert int(ws[:4096].sum()) == 0, "counters not returned to zero (flags)"
+    xg = wl.bf16_operand((m, k), "gauss", 1.0, 12111)
+    wg = wl.bf16_operand((n, k), "gauss", 0.02, 12112)
+    xd, wd = dev_bf16(xg), dev_bf16(wg)
+    g1, _ = run_ag(fo, xd, wd, R, ws=ws, split=split, max_workgroups=grid)
+    g2, _ = run_ag(fo, xd, wd, R, ws=ws, split=split, max_workgroups=grid)
+    assert torch.equal(g1, g2), "self-reduced split-K not run-to-run deterministic"
+    check_tolerance(host(g1), orc.gemm(xg, wg), what=f"gauss split {split}")
+
+
 def test_ag_gemm_preset_flags_and_epoch_reuse(fo, orc):
     c = wl.CFG1
     xb, wb, x, w = gemm_case(c, "int")
