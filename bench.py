@@ -941,6 +941,12 @@ def profile_kernels(fo, names, launches):
             a2a_rate(fo, wl.CFG6, launches=launches)
         elif nm == "qsa":
             qsa_rate(fo, wl.CFG7, launches=launches)
+        elif nm == "library":
+            # the vendor library's GEMM (torch.matmul) on the shapes of the
+            # step's AG-GEMM, GEMM-RS and the QKV AG-GEMM, as a reference
+            for cfg in (wl.CFG2, wl.CFG3, wl.CFG5):
+                us = library_gemm_us(cfg.m, cfg.n, cfg.k, launches=launches)
+                log(f"library GEMM {cfg.m}x{cfg.n}x{cfg.k}: {us:.1f} us")
         else:
             raise SystemExit(f"unknown workload {nm}")
         torch.cuda.synchronize()
@@ -979,7 +985,8 @@ def main():
     ap.add_argument("--profile-kernels", default="",
                     help="launch only these workloads, --launches times each, for a profiler run: "
                          "comma list of step (AG-GEMM, GEMM-RS, reduce of the TP=8 MLP share), reduce4 "
-                         "(DP gradient reduce), a2a (Ulysses all-to-all GEMM), qsa (TP=4 attention), or all")
+                         "(DP gradient reduce), a2a (Ulysses all-to-all GEMM), qsa (TP=4 attention), or all; "
+                         "library runs the vendor GEMM (torch.matmul) on the GEMM shapes instead")
     ap.add_argument("--launches", type=int, default=5)
     ap.add_argument("--sustain", type=float, default=0.0,
                     help="launch the AG-GEMM of the step back to back for this many seconds (to sample "

@@ -76,7 +76,13 @@ def _gemm_launches(disp, select=None):
     if select is not None:
         sub, label = select
         hits = [(n, v) for n, v in disp if sub in n]
-        return {label: [v for _, v in hits]}, {label: hits[0][0] if hits else None}
+        names = list(dict.fromkeys(n for n, _ in hits))
+        if len(names) <= 1:
+            return {label: [v for _, v in hits]}, {label: hits[0][0] if hits else None}
+        # several kernels hold the substring: one launch per kernel, in the
+        # order they first ran, labelled label_1, label_2, ...
+        res = {f"{label}_{j + 1}": [v for n, v in hits if n == nm] for j, nm in enumerate(names)}
+        return res, {f"{label}_{j + 1}": nm for j, nm in enumerate(names)}
     g = [v for n, v in disp if "gemm_kernel" in n]
     names = [n for n, _ in disp if "gemm_kernel" in n]
     res = {k: [] for k in LAUNCHES}
