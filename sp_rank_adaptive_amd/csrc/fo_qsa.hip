@@ -312,6 +312,14 @@ __device__ __forceinline__ void qsa_block(const QsaArgs &a, char *lds, const Blk
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[qb][ks] = *reinterpret_cast<const bf16x8 *>(qrow + ks * 32);
   }
+  // Opaque to the compiler once loaded: left alone it reloads them from
+  // memory in every tile to free registers, and the waits for those reloads,
+  // counted in order with the next tile's copies issued just before, made
+  // every tile wait for its successor's copies before its first MFMA.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(qf[qb][ks]));
 
   // Copies into LDS by the buffer-load DMA path, both tiles double-buffered
   // (tile kt in buffer kt % 2).  Key tile: thread t fills 16-byte slot t of
@@ -357,16 +365,22 @@ __device__ __forceinline__ void qsa_block(const QsaArgs &a, char *lds, const Blk
     const char *K = lds + (kt & 1) * K_TILE;
     const char *VT = lds + 2 * K_TILE + (kt & 1) * VT_TILE;
     // S^T = K Q^T: st[kb][qb], keys 16 kb + 4 g + v, query 16 qb + li
+    // (the four key fragments of a group of 16 keys are read together, then
+    // its eight MFMAs issued)
     f32x4 st[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
+      bf16x8 kf[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(K + (kb * 16 + li) * K_ROWB + (((ks * 4 + g) ^ li) << 4));
+      for (int ks = 0; ks < 4; ++ks)
+        kf[ks] = *reinterpret_cast<const bf16x8 *>(K + (kb * 16 + li) * K_ROWB + (((ks * 4 + g) ^ li) << 4));
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
-          st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : st[kb][qb], 0, 0, 0);
-      }
+          st[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[qb][ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : st[kb][qb], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
     // Online softmax per query, in log2 units.  The maximum is taken over
     // the raw scores (the scale is positive); the reference m a row's
@@ -421,16 +435,38 @@ __device__ __forceinline__ void qsa_block(const QsaArgs &a, char *lds, const Blk
     }
     // O^T += V^T P^T: value rows 16 db + li, the keys of k-group 4 k2 + g
     // (the same key order as pf)
+    {
+      // two groups of 16 value dims at a time: the next group's four
+      // fragment reads are in flight while this group's eight MFMAs run
+      // (read one at a time, each read's latency stood in front of two MFMAs)
+      auto rdv = [&](int db, int k2) {
+        return *reinterpret_cast<const f16x8 *>(VT + (db * 16 + li) * VT_ROWB + (((k2 * 4 + g) ^ (li & 7)) << 4));
+      };
+      f16x8 vf[2][2][2];
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const char *row = VT + (db * 16 + li) * VT_ROWB;
+      for (int dd = 0; dd < 2; ++dd)
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const f16x8 vf = *reinterpret_cast<const f16x8 *>(row + (((k2 * 4 + g) ^ (li & 7)) << 4));
+        for (int k2 = 0; k2 < 2; ++k2) vf[0][dd][k2] = rdv(dd, k2);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      static_for<4>([&](auto gc) {
+        constexpr int gi = decltype(gc)::value;
+        constexpr int cur = gi & 1;
+        if constexpr (gi + 1 < 4) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[qb][k2], o[db][qb], 0, 0, 0);
-      }
+          for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) vf[cur ^ 1][dd][k2] = rdv(2 * (gi + 1) + dd, k2);
+        }
+#pragma unroll
+        for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+              o[2 * gi + dd][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf[cur][dd][k2], pf[qb][k2], o[2 * gi + dd][qb], 0, 0, 0);
+        if constexpr (gi + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      });
     }
     if (kt + 1 < nkt) {
       wait_vm<0>();                // tile kt + 1 landed
