@@ -706,7 +706,12 @@ fo_status fo_qsa_attention(const void *qkv, void *o, fo_dtype o_dtype, int64_t s
   // are empty and left out.
   int np = 0;
   const int per_pair = heads * a.tiles;
-  a.conv_units = heads * (a.chunk / QSA_BKV);   // (head, key tile) of the chunk
+  // With arrival flags, two groups of 4 waves share each block (one
+  // workgroup per CU): the blocks of the chunk that lands last then use every
+  // CU.  With every chunk present, one group per workgroup and two workgroups
+  // per CU.
+  a.groups = s->arrived != nullptr ? 2 : 1;
+  a.conv_units = heads * (a.chunk / (a.groups * QSA_BKV));   // (head, key tiles of one unit) of the chunk
   for (int sg = 0; sg < R; ++sg) {
     a.stage_pair0[sg] = np;
     const int cs = a.order[sg];
@@ -729,7 +734,7 @@ fo_status fo_qsa_attention(const void *qkv, void *o, fo_dtype o_dtype, int64_t s
   }
   a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)QSA_D));
   const int64_t blocks = (int64_t)np * per_pair;
-  const int full = 2 * I->cus;   // two workgroups per CU
+  const int full = a.groups == 2 ? I->cus : 2 * I->cus;   // 8 waves per CU either way
   const int cap = (s->max_workgroups > 0 && s->max_workgroups < full) ? s->max_workgroups : full;
   a.grid = (int32_t)(blocks < cap ? blocks : cap);
   if (a.grid < 1) a.grid = 1;

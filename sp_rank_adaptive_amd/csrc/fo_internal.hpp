@@ -145,7 +145,8 @@ struct QsaArgs {
   int32_t order[QSA_MAX_CHUNKS];
   int32_t stage_units[QSA_MAX_CHUNKS];          // blocks released by stage s
   int32_t stage_pair0[QSA_MAX_CHUNKS];          // first pair of stage s in pair_q / pair_k
-  int32_t conv_units;                           // conversion units opening each stage (H * key tiles)
+  int32_t groups;                               // groups of 4 waves per workgroup (1 or 2)
+  int32_t conv_units;                           // conversion units opening each stage (H * key tiles / groups)
   int32_t stage_big[QSA_MAX_CHUNKS];            // conversion units plus the blocks of stage s that hold
                                                 // every key tile of their pair; the rest, with the
                                                 // causal mask, are the stage's diagonal pair, by

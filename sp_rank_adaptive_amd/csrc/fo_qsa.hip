@@ -15,11 +15,20 @@
 // times) and writes the output rows.
 //
 // Layout and schedule
-//  - 4 waves per workgroup, 32 queries each; two workgroups per CU.  A key
-//    tile of 64 rows is copied into LDS by the buffer-load DMA path
-//    (16-byte pieces XOR-swizzled by row); the value tile goes through
-//    registers into LDS transposed, as fp16, so each lane reads its value
-//    fragments as two 8-byte pieces.
+//  - 8 waves per CU in either of two forms.  With every chunk present: two
+//    workgroups of 4 waves per CU, each on its own block.  Under arrivals:
+//    one workgroup of two groups of 4 waves per CU, sharing each block, group
+//    g taking key tiles g, g + 2, ... with its own double-buffered LDS tiles,
+//    maxima, sums and weighted sums; at the block's end group 1 hands its
+//    state to group 0 through LDS, which merges the two.  The blocks of the
+//    chunk that lands last then occupy every CU, each in about two thirds of
+//    the time.  (Two independent workgroups overlap one's softmax with the
+//    other's MFMAs; the two groups, in step at every barrier, do not, so the
+//    all-present launch keeps the first form.)  Each wave owns 32 queries.  A key tile of 64 rows is copied into LDS by
+//    the buffer-load DMA path (16-byte pieces XOR-swizzled by row); the
+//    values of a key chunk are converted once to fp16 images, transposed, that
+//    a block copies to LDS as they lie, so each lane reads its value fragments
+//    as 16-byte pieces.
 //  - Scores are computed transposed, S^T = K Q^T (bf16 MFMA, fp32
 //    accumulate), so each lane holds one query's scores for 4 keys of every
 //    16-key block: the softmax needs one cross-lane step per tile, and the
@@ -44,12 +53,12 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int QS_THREADS = 256;
+constexpr int QS_GT = 256;                      // threads of one group of 4 waves
 constexpr int K_ROWB = QSA_D * 2;                  // 256 bytes per key row
 constexpr int K_TILE = QSA_BKV * K_ROWB;           // 16 KiB
 constexpr int VT_ROWB = QSA_BKV * 2;               // 64 fp16 keys per value row
 constexpr int VT_TILE = QSA_D * VT_ROWB;           // 16 KiB
-constexpr int QS_LDS = 2 * K_TILE + 2 * VT_TILE;   // both tiles double-buffered
+constexpr int QS_GLDS = 2 * K_TILE + 2 * VT_TILE;  // one group's tiles, both double-buffered
 constexpr int SLOT_FLOATS = QSA_BQ * QSA_D + 2 * QSA_BQ;   // O [BQ][d], m [BQ], l [BQ]
 constexpr int QS_EXITED = 576, QS_COMBINED = 577, QS_ABORT = 578, QS_EXITED_X = 584;
 constexpr int QS_GROUPS = 8;   // claim groups per stage (one per XCD)
@@ -61,7 +70,7 @@ constexpr float RESCALE_LOG2 = 8.0f;   // lazy rescale threshold (log2 units)
 
 struct Blk {
   int h, qt, qc, kc;   // head, query tile over the whole sequence, query chunk, key chunk; qt < 0: stop
-  int conv;            // 1: conversion unit (chunk qc, head h, key tiles 2 kc and 2 kc + 1)
+  int conv;            // 1: conversion unit (chunk qc, head h, key tiles G kc .. G kc + G - 1, one per group)
 };
 
 __device__ __forceinline__ void store_wt4(float *p, float v) {
@@ -108,8 +117,9 @@ __device__ __forceinline__ Blk decode_unit(const QsaArgs &a, int s, uint32_t u, 
   Blk b;
   b.conv = 0;
   if ((int)u < a.conv_units) {
-    // convert the new chunk's value rows (head u / key tiles, key tile u % key tiles)
-    const int nkt = a.chunk / QSA_BKV;
+    // convert the new chunk's value rows (head u / units per head, key
+    // tiles G (u % units per head) .. + G - 1, one per group)
+    const int nkt = a.chunk / (a.groups * QSA_BKV);
     b.conv = 1;
     b.qc = a.order[s];
     b.h = (int)u / nkt;
@@ -258,10 +268,10 @@ __device__ Blk qsa_claim(const QsaArgs &a, uint32_t &acquired, uint64_t &wait_fr
 // the keys of k-group P = 4 k2 + g, in the order the score fragments hold
 // them (32 k2 + 4 g + 0..3, then 32 k2 + 16 + 4 g + 0..3), and sits at
 // piece P ^ (d % 8), so the fragment reads of 8 rows fall on 8 distinct bank
-// groups.  Thread i: k-group i % 8, head dims 4 (i / 8) .. + 4.  Stores are
-// written through.
+// groups.  Thread i of the group: k-group i % 8, head dims 4 (i / 8) .. + 4.
+// Stores are written through.
 __device__ __forceinline__ void qsa_convert(const QsaArgs &a, int c, int h, int t) {
-  int tid = threadIdx.x;
+  int tid = threadIdx.x & (QS_GT - 1);
   asm volatile("" : "+v"(tid));
   const int kg = tid & 7, dg = tid >> 3;
   const int k2 = kg >> 2, g = kg & 3;
@@ -288,11 +298,18 @@ __device__ __forceinline__ void qsa_convert(const QsaArgs &a, int c, int h, int 
 
 // One block: the 128 queries of tile b.qt against the keys of chunk b.kc, for
 // head b.h; leaves the tile's row maxima m, sums l and unnormalised weighted
-// sums O (fp32, written through) in the block's slot.
-__device__ __forceinline__ void qsa_block(const QsaArgs &a, char *lds, const Blk &b) {
-  int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
+// sums O (fp32, written through) in the block's slot.  With G groups of 4
+// waves, group grp (waves 4 grp .. 4 grp + 3) takes key tiles grp, grp + G,
+// ...; wave w of every group owns queries 32 w .. 32 w + 31 of the tile.
+template <int G>
+__device__ __forceinline__ void qsa_block(const QsaArgs &a, char *lds_all, const Blk &b) {
+  int tid_all = threadIdx.x;
+  asm volatile("" : "+v"(tid_all));
+  const int grp = G == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid_all >> 8);
+  const int tid = tid_all & (QS_GT - 1);
+  char *const lds = lds_all + grp * QS_GLDS;
   const int lane = tid & 63, wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // the same, in a scalar register
   const int g = lane >> 4, li = lane & 15;
   const int HD = a.H * QSA_D;
   const int64_t RS = 3 * (int64_t)HD;                     // qkv row stride (elements)
@@ -332,17 +349,23 @@ __device__ __forceinline__ void qsa_block(const QsaArgs &a, char *lds, const Blk
   const __amdgpu_buffer_rsrc_t rsv =
       uniform_rsrc(a.vt + ((int64_t)b.h * (a.S / QSA_BKV) + (int64_t)b.kc * nkt_all) * (QSA_D * QSA_BKV),
                    nkt_all * VT_TILE);
-  const int k_voff = (int)(((tid >> 4) * RS + (((tid & 15) ^ (tid >> 4)) * 8)) * 2);
-  const uint32_t lds_w = lds_addr(lds) + (uint32_t)(__builtin_amdgcn_readfirstlane(wave) * 1024);
-  auto issue = [&](int kt) {
-    const uint32_t kb = lds_w + (uint32_t)((kt & 1) * K_TILE);
-    const uint32_t vb = lds_w + (uint32_t)(2 * K_TILE + (kt & 1) * VT_TILE);
+  const uint32_t lds_w = lds_addr(lds) + (uint32_t)(wave_s * 1024);
+  auto issue = [&](int kt) {   // the group's tile kt (its iteration kt / G) into buffer (kt / G) % 2
+    const uint32_t kb = lds_w + (uint32_t)(((kt / G) & 1) * K_TILE);
+    const uint32_t vb = lds_w + (uint32_t)(2 * K_TILE + ((kt / G) & 1) * VT_TILE);
+    // the per-lane offsets are rebuilt at each issue from the lane id
+    // (mbcnt, no memory) and the wave index (a scalar): kept live across the
+    // tile loop they were spilled, and the reload's wait, counted in order
+    // with the copies in flight, held back the issue
+    int t = (wave_s << 6) | (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(t));
+    const int k_voff = (int)(((t >> 4) * RS + (((t & 15) ^ (t >> 4)) * 8)) * 2);
 #pragma unroll
     for (int rd = 0; rd < 4; ++rd)
       dma16(kb + (uint32_t)(rd * 4096), k_voff, rsk, (int)((int64_t)(kt * QSA_BKV + rd * 16) * RS * 2));
 #pragma unroll
     for (int rd = 0; rd < 4; ++rd)
-      dma16_coherent(vb + (uint32_t)(rd * 4096), tid * 16, rsv, kt * VT_TILE + rd * 4096);
+      dma16_coherent(vb + (uint32_t)(rd * 4096), t * 16, rsv, kt * VT_TILE + rd * 4096);
   };
 
   f32x4 o[8][2];
@@ -356,14 +379,17 @@ __device__ __forceinline__ void qsa_block(const QsaArgs &a, char *lds, const Blk
   // buffers tile kt - 1 used; one barrier per tile (tile kt + 1 landed, and
   // every wave is done with tile kt's buffers).
   __syncthreads();                 // the previous block's last tile is done with the buffers
-  issue(0);
+  if (grp < nkt) issue(grp);
   wait_vm<0>();
   __syncthreads();
-  auto tile = [&](int kt, auto maskc) {
-    constexpr bool MASK = decltype(maskc)::value;   // the tile crosses the diagonal
-    if (kt + 1 < nkt) issue(kt + 1);
-    const char *K = lds + (kt & 1) * K_TILE;
-    const char *VT = lds + 2 * K_TILE + (kt & 1) * VT_TILE;
+  // The probabilities of the group's current tile (fp16, laid out as the
+  // second operand of O^T = V^T P^T), from score() to pv().
+  f16x8 pf[2][2];
+  // Scores of tile kt, S^T = K Q^T, and its online softmax; MASK: the tile
+  // crosses the diagonal (uniform).
+  auto score = [&](int kt, auto maskc) {
+    const bool MASK = static_cast<bool>(maskc);
+    const char *K = lds + ((kt / G) & 1) * K_TILE;
     // S^T = K Q^T: st[kb][qb], keys 16 kb + 4 g + v, query 16 qb + li
     // (the four key fragments of a group of 16 keys are read together, then
     // its eight MFMAs issued)
@@ -388,7 +414,6 @@ __device__ __forceinline__ void qsa_block(const QsaArgs &a, char *lds, const Blk
     // exceeds it by more than 2^8, so the weighted sums are rescaled only
     // then (any reference gives the same softmax; probabilities stay below
     // 2^8, well inside fp16).  The first tile always sets it.
-    f16x8 pf[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       float mx = NEG_BIG;
@@ -397,7 +422,7 @@ __device__ __forceinline__ void qsa_block(const QsaArgs &a, char *lds, const Blk
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           float sv = st[kb][qb][v];
-          if constexpr (MASK) {
+          if (MASK) {
             const int qrow = q0 + wave * 32 + qb * 16 + li;
             if (kbase + kt * QSA_BKV + kb * 16 + 4 * g + v > qrow) sv = -__builtin_inff();
             st[kb][qb][v] = sv;
@@ -433,8 +458,13 @@ __device__ __forceinline__ void qsa_block(const QsaArgs &a, char *lds, const Blk
         pf[qb][k2] = f16x8{p16[2 * k2][0], p16[2 * k2][1], p16[2 * k2][2], p16[2 * k2][3],
                            p16[2 * k2 + 1][0], p16[2 * k2 + 1][1], p16[2 * k2 + 1][2], p16[2 * k2 + 1][3]};
     }
-    // O^T += V^T P^T: value rows 16 db + li, the keys of k-group 4 k2 + g
+  };
+  // O^T += V^T P^T for tile kt: value rows 16 db + li, the keys of k-group
+  // 4 k2 + g
     // (the same key order as pf)
+  auto pv = [&](int kt) {
+    const char *VT = lds + 2 * K_TILE + ((kt / G) & 1) * VT_TILE;
+
     {
       // two groups of 16 value dims at a time: the next group's four
       // fragment reads are in flight while this group's eight MFMAs run
@@ -468,18 +498,80 @@ __device__ __forceinline__ void qsa_block(const QsaArgs &a, char *lds, const Blk
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       });
     }
-    if (kt + 1 < nkt) {
-      wait_vm<0>();                // tile kt + 1 landed
-      __syncthreads();             // ... for every wave; every wave is done with tile kt
-    }
   };
   // Key tiles that end before the block's first query need no mask; on the
-  // diagonal the last two tiles cross it.
+  // diagonal the last two tiles cross it.  Every tile ends in one barrier of
+  // the whole workgroup (the group's next tile landed, every wave done with
+  // the tile whose buffer is refilled next).
   const int nfree = diag ? (q0 - kbase) / QSA_BKV : nkt;
-  for (int kt = 0; kt < nfree; ++kt) tile(kt, std::false_type{});
-  if (diag) {
-    tile(nfree, std::true_type{});
-    tile(nfree + 1, std::true_type{});
+  if constexpr (G == 1) {
+    // the mask known at compile time: unmasked tiles carry none of it
+    auto step = [&](int kt, auto maskc) {
+      if (kt + 1 < nkt) issue(kt + 1);
+      score(kt, maskc);
+      pv(kt);
+      if (kt + 1 < nkt) {
+        wait_vm<0>();
+        __syncthreads();
+      }
+    };
+    for (int kt = 0; kt < nfree; ++kt) step(kt, std::false_type{});
+    if (diag) {
+      step(nfree, std::true_type{});
+      step(nfree + 1, std::true_type{});
+    }
+  } else {
+    // the groups take the block's tiles in turn, one tile each per
+    // iteration; a group with no tile left sits the last one out.  One tile
+    // body with the mask as a run-time flag: two bodies made the compiler
+    // move the accumulators between register sets at every tile.
+    const int iters = (nkt + G - 1) / G;
+    for (int it = 0; it < iters; ++it) {
+      const int kt = G * it + grp;
+      if (kt < nkt) {
+        if (kt + G < nkt) issue(kt + G);
+        score(kt, kt >= nfree);
+        pv(kt);
+      }
+      if (it + 1 < iters) {
+        wait_vm<0>();
+        __syncthreads();
+      }
+    }
+  }
+
+  // Group 1 hands its maxima, partial sums and weighted sums to group 0,
+  // lane by lane, through LDS (the tile buffers are free after the barrier);
+  // group 0 merges them: M = max, each side scaled by 2^(its m - M).  Group
+  // 0's first tile holds keys at or before every query of the tile, so its
+  // maxima are finite.
+  if constexpr (G == 2) {
+  __syncthreads();
+  float *xo = reinterpret_cast<float *>(lds_all + QS_GLDS) + (wave * 64 + lane) * 64;   // 64 floats per lane
+  float *xm = reinterpret_cast<float *>(lds_all) + (wave * 64 + lane) * 4;              // m[2], l[2] per lane
+  if (grp == 1) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) *reinterpret_cast<f32x4 *>(xo + (db * 2 + qb) * 4) = o[db][qb];
+    *reinterpret_cast<f32x4 *>(xm) = f32x4{m[0], m[1], l[0], l[1]};
+  }
+  __syncthreads();
+  if (grp == 1) return;
+  {
+    const f32x4 ml = *reinterpret_cast<const f32x4 *>(xm);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float m1 = ml[qb], l1 = ml[2 + qb];
+      const float mm = fmaxf(m[qb], m1);
+      const float a0 = __builtin_amdgcn_exp2f(m[qb] - mm), a1 = __builtin_amdgcn_exp2f(m1 - mm);
+      l[qb] = l[qb] * a0 + l1 * a1;
+      m[qb] = mm;
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        o[db][qb] = o[db][qb] * a0 + *reinterpret_cast<const f32x4 *>(xo + (db * 2 + qb) * 4) * a1;
+    }
+  }
   }
 
   // the block's slot: O rows by query (value dims 16 db + 4 g + v in lane
@@ -504,8 +596,9 @@ __device__ __forceinline__ void qsa_block(const QsaArgs &a, char *lds, const Blk
 // Merge of a query tile's blocks (key chunks 0 .. nb-1, in that order): per
 // query, M = max m, L = sum 2^(m - M) l, O = sum (2^(m - M) / L) O.  The
 // maxima and sums go through LDS (the block's buffers are idle here), then
-// each thread merges 16-byte pieces of output rows, all its loads in flight
-// together.
+// each thread merges 16-byte pieces of output rows, the loads of two slots in
+// flight together.
+template <int NTH>
 __device__ __forceinline__ void qsa_combine(const QsaArgs &a, char *lds, int h, int qt, int nb) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
@@ -513,10 +606,25 @@ __device__ __forceinline__ void qsa_combine(const QsaArgs &a, char *lds, int h, 
   const float *slot0 = a.part + (int64_t)(h * QT + qt) * a.R * SLOT_FLOATS;
   float *s_m = reinterpret_cast<float *>(lds);                     // [nb][BQ]
   float *s_l = s_m + QSA_MAX_CHUNKS * QSA_BQ;                      // [nb][BQ]
+  constexpr int PIECES = QSA_BQ * (QSA_D / 4);                     // 16-byte output pieces
+  constexpr int PER = PIECES / NTH;
+  constexpr int SB = NTH >= 512 ? 2 : 1;                           // slots whose loads are in flight together
+                                                                   // (as many as the registers allow)
+  auto slot_rs = [&](int j) { return uniform_rsrc(slot0 + (int64_t)j * SLOT_FLOATS, SLOT_FLOATS * 4); };
+  // the first slots' rows go out before the maxima and sums (they do not
+  // depend on the weights), so those round trips overlap
+  f32x4 t[SB][PER];
+#pragma unroll
+  for (int jj = 0; jj < SB; ++jj)
+    if (jj < nb) {
+      const __amdgpu_buffer_rsrc_t rs = slot_rs(jj);
+#pragma unroll
+      for (int k = 0; k < PER; ++k) t[jj][k] = load_coherent16(rs, (tid + k * NTH) * 16);
+    }
   __syncthreads();   // the block's last tile is done with LDS
-  for (int idx = tid; idx < nb * QSA_BQ; idx += QS_THREADS) {
+  for (int idx = tid; idx < nb * QSA_BQ; idx += NTH) {
     const int j = idx / QSA_BQ, r = idx - (idx / QSA_BQ) * QSA_BQ;
-    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(slot0 + (int64_t)j * SLOT_FLOATS, SLOT_FLOATS * 4);
+    const __amdgpu_buffer_rsrc_t rs = slot_rs(j);
     s_m[idx] = load_coherent4(rs, (QSA_BQ * QSA_D + r) * 4);
     s_l[idx] = load_coherent4(rs, (QSA_BQ * QSA_D + QSA_BQ + r) * 4);
   }
@@ -534,25 +642,33 @@ __device__ __forceinline__ void qsa_combine(const QsaArgs &a, char *lds, int h, 
   }
   __syncthreads();
   const int HD = a.H * QSA_D;
-  constexpr int PIECES = QSA_BQ * (QSA_D / 4);                     // 16-byte output pieces
-  constexpr int PER = PIECES / QS_THREADS;
   f32x4 acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < nb; ++j) {
-    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(slot0 + (int64_t)j * SLOT_FLOATS, SLOT_FLOATS * 4);
-    f32x4 t[PER];
+  // slots in order 0 .. nb-1 (fp32 adds in that order), SB loaded together
+  for (int j0 = 0; j0 < nb; j0 += SB) {
+    if (j0 > 0) {
 #pragma unroll
-    for (int k = 0; k < PER; ++k) t[k] = load_coherent16(rs, (tid + k * QS_THREADS) * 16);
+      for (int jj = 0; jj < SB; ++jj)
+        if (j0 + jj < nb) {
+          const __amdgpu_buffer_rsrc_t rs = slot_rs(j0 + jj);
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int r = (tid + k * QS_THREADS) / (QSA_D / 4);
-      acc[k] += s_m[j * QSA_BQ + r] * t[k];
+          for (int k = 0; k < PER; ++k) t[jj][k] = load_coherent16(rs, (tid + k * NTH) * 16);
+        }
     }
+#pragma unroll
+    for (int jj = 0; jj < SB; ++jj)
+      if (j0 + jj < nb) {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+          const int r = (tid + k * NTH) / (QSA_D / 4);
+          acc[k] += s_m[(j0 + jj) * QSA_BQ + r] * t[jj][k];
+        }
+      }
   }
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int idx = tid + k * QS_THREADS;
+    const int idx = tid + k * NTH;
     const int r = idx / (QSA_D / 4), c4 = idx - r * (QSA_D / 4);
     const int64_t off = (int64_t)(qt * QSA_BQ + r) * HD + h * QSA_D + 4 * c4;
     if (a.o_bf16) {
@@ -569,8 +685,14 @@ __device__ __forceinline__ void qsa_combine(const QsaArgs &a, char *lds, int h, 
 // pairs of the unified register file, so 120 caps each wave at 240 and the
 // two waves of a SIMD leave 32 of each lane's 512 registers free, where the
 // one-wave kernels of a copy-engine emulator still fit beside the grid.
-__global__ void __launch_bounds__(QS_THREADS, 2) __attribute__((amdgpu_num_vgpr(120))) qsa_kernel(QsaArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[QS_LDS];
+// G groups of 4 waves per workgroup: G = 2, one workgroup per CU, when the
+// chunks arrive during the launch (the last chunk's blocks then use every
+// CU, each in half the time); G = 1, two workgroups per CU, when every chunk
+// is present (independent workgroups overlap one's softmax with the other's
+// MFMAs, where two groups of one workgroup, in step at each barrier, do not).
+template <int G>
+__global__ void __launch_bounds__(G * QS_GT, 2 / G) __attribute__((amdgpu_num_vgpr(120))) qsa_kernel(QsaArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[G * QS_GLDS];
   __shared__ Blk s_blk;
   __shared__ int s_last;
   const int tid = threadIdx.x;
@@ -594,8 +716,9 @@ __global__ void __launch_bounds__(QS_THREADS, 2) __attribute__((amdgpu_num_vgpr(
     b.conv = __builtin_amdgcn_readfirstlane(b.conv);
     if (b.qt < 0) break;
     if (b.conv) {
-      // count the unit once its stores are acknowledged
-      qsa_convert(a, b.qc, b.h, b.kc);
+      // group g converts key tile G kc + g; the unit counts once every
+      // group's stores are acknowledged
+      qsa_convert(a, b.qc, b.h, G * b.kc + (G == 1 ? 0 : (tid >> 8)));
       wait_stores();
       __syncthreads();
       if (tid == 0) fetch_add_relaxed(a.ws32 + a.conv_off + b.qc * a.H + b.h, 1u);
@@ -605,7 +728,7 @@ __global__ void __launch_bounds__(QS_THREADS, 2) __attribute__((amdgpu_num_vgpr(
     if (tid == 0) {
       const uint32_t *cc = a.ws32 + a.conv_off + b.kc * a.H + b.h;
       const uint64_t t0 = now_ticks();
-      while (load_relaxed(cc) < (uint32_t)(a.chunk / QSA_BKV)) {
+      while (load_relaxed(cc) < (uint32_t)(a.chunk / (G * QSA_BKV))) {
         if (load_relaxed(a.ws32 + QS_ABORT) != 0u) break;
         if (now_ticks() - t0 > a.timeout_ticks) {
           if (a.status) __hip_atomic_store(a.status, (int32_t)FO_ERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -615,7 +738,7 @@ __global__ void __launch_bounds__(QS_THREADS, 2) __attribute__((amdgpu_num_vgpr(
         __builtin_amdgcn_s_sleep(1);
       }
     }
-    qsa_block(a, lds, b);
+    qsa_block<G>(a, lds, b);
     // count the block once its stores are acknowledged; the block that
     // completes the tile merges it
     wait_stores();
@@ -629,7 +752,7 @@ __global__ void __launch_bounds__(QS_THREADS, 2) __attribute__((amdgpu_num_vgpr(
     }
     __syncthreads();
     if (s_last) {
-      qsa_combine(a, lds, b.h, b.qt, nb);
+      qsa_combine<G * QS_GT>(a, lds, b.h, b.qt, nb);
       if (a.stamps) {
         __syncthreads();
         if (tid == 0) {
@@ -667,7 +790,10 @@ __global__ void __launch_bounds__(QS_THREADS, 2) __attribute__((amdgpu_num_vgpr(
 }  // namespace
 
 hipError_t launch_qsa(const QsaArgs &a, hipStream_t stream) {
-  hipLaunchKernelGGL(qsa_kernel, dim3(a.grid), dim3(QS_THREADS), 0, stream, a);
+  if (a.groups == 2)
+    hipLaunchKernelGGL(qsa_kernel<2>, dim3(a.grid), dim3(2 * QS_GT), 0, stream, a);
+  else
+    hipLaunchKernelGGL(qsa_kernel<1>, dim3(a.grid), dim3(QS_GT), 0, stream, a);
   return hipGetLastError();
 }
 
