@@ -669,10 +669,15 @@ def link_sweep(fo, hz, bws=(50e9, 153e9, 400e9, 1000e9)):
     return out
 
 
-def measure_tail_dp(fo, cfg, hz, schedule="flashoverlap", reps=10, link_bw=wl.LINK_BW, spread=None):
+def measure_tail_dp(fo, cfg, hz, schedule="flashoverlap", reps=10, link_bw=wl.LINK_BW, spread=None, mesh=False):
     """Exposed tail of the DP gradient reduce-add (in place into the local
     shard): the 7 peer chunks land by emulated arrivals in a seeded order; the
-    tail is the time from the last landing to the reduce's completion."""
+    tail is the time from the last landing to the reduce's completion.
+    mesh=False: ring arrivals (chunk s lands at s * B / BW, SDMA copies).
+    mesh=True: mesh-staggered arrivals, one link per peer, chunk s landing at
+    B / BW + (s - 1) * 250 us; the copies of all seven would overlap on one
+    GPU's copy engine, so the data are copied in before the timeline starts
+    and only the flags are released at those times."""
     import torch
     n, R, local = cfg.n, cfg.R, 0
     srcs = [torch.randn(n, device="cuda") * 1e-3 for _ in range(R)]
@@ -688,8 +693,17 @@ def measure_tail_dp(fo, cfg, hz, schedule="flashoverlap", reps=10, link_bw=wl.LI
         e = 300 + rep
         st.zero_()
         torch.cuda.synchronize()
-        _emulate(fo, [srcs[q] for q in order], [staging[q] for q in order], order, n * 4, flags, e, es, side,
-                 link_bw)
+        if mesh:
+            for q in order:
+                srcs[q].copy_(staging[q])
+            torch.cuda.synchronize()
+            rel = wl.mesh_staggered_release_ns(n * 4, len(order), link_bw)
+            with torch.cuda.stream(side):
+                fo.fo_emulate_arrivals([srcs[q] for q in order], [staging[q] for q in order], rel, order, flags, e,
+                                       es, issue_ns=list(rel), nbytes=[0] * len(order), stream=side)
+        else:
+            _emulate(fo, [srcs[q] for q in order], [staging[q] for q in order], order, n * 4, flags, e, es, side,
+                     link_bw)
         if schedule == "naive":
             ev = torch.cuda.Event()
             ev.record(side)
@@ -1218,6 +1232,12 @@ def main():
             row[s_ + "_us"] = round(measure_tail_dp(fo, wl.CFG4, hz, s_, spread=sp), 1)
             row[s_ + "_p10_p90_us"] = [sp["p10"], sp["p90"]]
             row["reps"] = sp["reps"]
+        mesh = {"arrivals": "mesh-staggered, flags only (data copied in before t0)"}
+        for s_ in ("flashoverlap", "naive"):
+            sp = {}
+            mesh[s_ + "_us"] = round(measure_tail_dp(fo, wl.CFG4, hz, s_, spread=sp, mesh=True), 1)
+            mesh[s_ + "_p10_p90_us"] = [sp["p10"], sp["p90"]]
+        row["mesh_staggered"] = mesh
         tails["cfg4_dp_reduce"] = row
         log(f"tail cfg4: {row}")
         out["tails_50GBps_links"] = tails

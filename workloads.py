@@ -199,3 +199,13 @@ def seeded_permutation(values: list[int], seed: int) -> list[int]:
 def ring_release_ns(nbytes: int, count: int, bw: float = LINK_BW) -> list[float]:
     """Release times t_s = s * B / BW (s = 1..count) in nanoseconds."""
     return [s * nbytes / bw * 1e9 for s in range(1, count + 1)]
+
+
+MESH_STAGGER_NS = 250_000.0
+
+
+def mesh_staggered_release_ns(nbytes: int, count: int, bw: float = LINK_BW) -> list[float]:
+    """Mesh-staggered release times t_s = B / BW + (s - 1) * 250 us
+    (s = 1..count) in nanoseconds: one link per peer, the peers starting a
+    little apart."""
+    return [nbytes / bw * 1e9 + (s - 1) * MESH_STAGGER_NS for s in range(1, count + 1)]
