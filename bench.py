@@ -354,7 +354,10 @@ def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LI
         chunks local-2, local-3, ..., local land one per step and each is
         added to this rank's partial of its chunk (in place, to forward; the
         local chunk's sum is the shard);
-      naive: wait for every partial, then GEMM-RS and the reduce."""
+      naive: wait for every partial, then GEMM-RS and the reduce;
+      sliced: GEMM-RS, then one reduce launch per incoming partial, each
+        after a stream wait on its flag, adding it to an fp32 accumulator
+        (the last one writes the bf16 shard)."""
     import torch
     xb, wb = wl.gemm_inputs(cfg, "gauss")
     x, w = dev_bf16(xb), dev_bf16(wb)
@@ -381,6 +384,9 @@ def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LI
     side = side_stream()
     main = torch.cuda.current_stream()
     gs = torch.zeros(2 * cfg.R + 2, dtype=torch.int64, device="cuda")
+    if schedule == "sliced":
+        wait_value = _hip_wait_value()
+        acc = torch.empty((mc, cfg.n), device="cuda")
     tails, spans = [], []
     for rep in range(reps + 1):   # the first repetition is a warm-up
         e = 200 + rep
@@ -406,6 +412,17 @@ def measure_tail_rs(fo, cfg, hz, schedule="flashoverlap", reps=20, link_bw=wl.LI
             fo.fo_gemm_rs_ring(x, w, part, done, shard, inbox,
                                fo.Schedule(nchunks=cfg.R, epoch=e, arrived=flags, stamps=gs,
                                            timeout_ns=5_000_000_000), ws)
+        elif schedule == "sliced":
+            fo.fo_gemm_rs(x, w, part, done, fo.Schedule(nchunks=cfg.R, epoch=e, stamps=gs), ws)
+            running = part[cfg.local * mc:(cfg.local + 1) * mc]
+            for i, q in enumerate(order):
+                st = wait_value(main.cuda_stream, flags[q:q + 1].data_ptr(), e, 0, 0xFFFFFFFF)
+                if st != 0:
+                    raise RuntimeError(f"hipStreamWaitValue32 failed ({st})")
+                last = i == len(order) - 1
+                fo.fo_chunk_reduce(shard if last else acc, [running, inbox[q]],
+                                   fo.Schedule(nchunks=2, epoch=e, stamps=rs_st if last else None))
+                running = acc
         else:
             fo.fo_gemm_rs(x, w, part, done, fo.Schedule(nchunks=cfg.R, epoch=e, stamps=gs), ws)
             srcs = [part[cfg.local * mc:(cfg.local + 1) * mc] if q == cfg.local else inbox[q]
@@ -1138,8 +1155,6 @@ def main():
             row = {"chunk_gemm_us": round(cg, 2), "chunk_gemm_split": cg_split, "chunk_gemm_us_per_split": cg_per,
                    "chunk_gemm_at_70pct_peak_us": round(at70, 2)}
             for sched in ("flashoverlap", "strict", "naive", "sliced"):
-                if cfg is wl.CFG5 and sched in ("strict", "sliced"):
-                    continue
                 sp = {}
                 t, span = measure_tail_ag(fo, cfg, hz, sched, spread=sp)
                 log(f"  {key} {sched}: tail {t:.1f} us")
@@ -1186,7 +1201,7 @@ def main():
             tails[key] = row
             log(f"tail {key}: {row}")
         row = {}
-        for s_ in ("flashoverlap", "fused", "ring", "naive"):
+        for s_ in ("flashoverlap", "fused", "ring", "naive", "sliced"):
             sp = {}
             row[s_ + "_us"] = round(measure_tail_rs(fo, c3, hz, s_, spread=sp), 2)
             row[s_ + "_p10_p90_us"] = [sp["p10"], sp["p90"]]
