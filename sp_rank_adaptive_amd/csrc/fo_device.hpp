@@ -21,12 +21,6 @@ __device__ __forceinline__ bool epoch_reached(uint32_t flag, uint32_t epoch) {
   return (int32_t)(flag - epoch) >= 0;
 }
 
-// Acquire load at system scope: data written before the matching release
-// (by a kernel after a copy-engine transfer) is visible after it returns.
-__device__ __forceinline__ uint32_t load_acquire(const uint32_t *p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-
 __device__ __forceinline__ uint32_t load_relaxed(const uint32_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
@@ -39,11 +33,8 @@ __device__ __forceinline__ void store_u64_relaxed(uint64_t *p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// Device-wide counters (workspace), ordered for cross-XCD hand-offs.
-__device__ __forceinline__ uint32_t fetch_add_acq_rel(uint32_t *p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-
+// Device-wide counters (workspace): relaxed atomics, performed at the
+// coherence point, so every XCD sees one count.
 __device__ __forceinline__ uint32_t fetch_add_relaxed(uint32_t *p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -59,10 +50,6 @@ __device__ __forceinline__ uint32_t load_relaxed_agent(const uint32_t *p) {
 // On gfx950 an agent-scope release fence writes the XCD's L2 back to memory
 // and an acquire fence invalidates it: both are paid by every workgroup on
 // the XCD, so the kernels fence only where data actually changes hands.
-__device__ __forceinline__ void fence_release_agent() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-}
-
 __device__ __forceinline__ void fence_acquire_agent() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
