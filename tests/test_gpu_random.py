@@ -1,0 +1,95 @@
+"""Seeded random parity cases for fo_ag_gemm and fo_gemm_rs: shapes, chunk
+counts, local rank, priority order, STRICT or ready-first, preset flags,
+per-chunk splits, workgroup caps, forced tile layouts and output types drawn
+together, on integer inputs, every element bit-exact against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from helpers import check_exact, dev_bf16, host, log
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+TILES = [None, "256x256", "256x160x3", "128x224", "128x128"]
+SEEDS = list(range(48))
+
+
+@pytest.fixture(scope="module")
+def fo():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sp_rank_adaptive_amd as fo
+    fo.lib()
+    return fo
+
+
+class _Epoch:
+    e = 5000
+
+
+def draw(seed: int) -> dict:
+    g = np.random.Generator(np.random.PCG64(31337 + seed))
+    R = int(g.choice([1, 2, 3, 4, 5, 8, 12]))
+    mc = int(g.integers(1, 600 // R + 2)) * 8 if R > 4 else int(g.integers(8, 520))
+    n = int(g.integers(8, 1100))
+    k = int(g.choice([8, 64, 200, 520, 1024, 2000]))
+    case = {
+        "R": R, "m": R * mc, "n": n, "k": k,
+        "local": int(g.integers(0, R)),
+        "order": [int(v) for v in g.permutation(R)],
+        "strict": bool(g.integers(0, 4) == 0),
+        "flags": bool(g.integers(0, 2)),
+        "split": [int(v) for v in g.choice([1, 1, 2, 3, 4, 8], size=R)] if g.integers(0, 2) else None,
+        "grid": int(g.choice([0, 0, 1, 7, 40, 100, 300])),
+        "tile": TILES[int(g.integers(0, len(TILES)))],
+        "bf16": bool(g.integers(0, 3) == 0),
+    }
+    return case
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_ag_gemm_and_gemm_rs_int_exact(fo, orc, seed, monkeypatch):
+    c = draw(seed)
+    log(f"case: seed {seed} {c}")
+    if c["tile"] is None:
+        monkeypatch.delenv("FO_TILE", raising=False)
+    else:
+        monkeypatch.setenv("FO_TILE", c["tile"])
+    m, n, k, R = c["m"], c["n"], c["k"], c["R"]
+    xb = wl.bf16_operand((m, k), "int", 1.0, 17000 + 2 * seed)
+    wb = wl.bf16_operand((n, k), "int", 1.0, 17001 + 2 * seed)
+    x, w = dev_bf16(xb), dev_bf16(wb)
+    ref = orc.gemm(xb, wb)
+    ws = torch.zeros(4 * fo.fo_workspace_bytes(m, n, k, R), dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    _Epoch.e += 1
+    e = _Epoch.e
+    flags = torch.full((R,), e, dtype=torch.int32, device="cuda") if c["flags"] else None
+    sched = dict(nchunks=R, local=c["local"], order=c["order"], epoch=e, arrived=flags,
+                 mode=fo.FO_SCHED_STRICT if c["strict"] else fo.FO_SCHED_READY_FIRST,
+                 split=c["split"], max_workgroups=c["grid"], status=status, timeout_ns=2_000_000_000)
+    dt = torch.bfloat16 if c["bf16"] else torch.float32
+    y = torch.full((m, n), float("nan"), dtype=dt, device="cuda")
+    fo.fo_ag_gemm(x, w, y, fo.Schedule(**sched), ws)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    if c["bf16"]:
+        assert np.array_equal(host(y), orc.f64_to_bf16(ref)), f"seed {seed} bf16"
+    else:
+        check_exact(host(y), ref, f"seed {seed} ag")
+
+    # GEMM-RS on the same operands: no split, no arrival flags (the local
+    # chunk last is the default order)
+    _Epoch.e += 1
+    e = _Epoch.e
+    part = torch.full((m, n), float("nan"), device="cuda")
+    done = torch.zeros(R, dtype=torch.int32, device="cuda")
+    fo.fo_gemm_rs(x, w, part, done, fo.Schedule(nchunks=R, local=c["local"], epoch=e,
+                                                max_workgroups=c["grid"], status=status), ws)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert (host(done) == e).all()
+    check_exact(host(part), ref, f"seed {seed} gemm_rs")
