@@ -116,7 +116,13 @@ typedef struct fo_schedule {
                                      is one workgroup per CU with `arrived`
                                      (all resident while they wait) and 8
                                      per CU without; it may exceed the value
-                                     so no workgroup owns more than 1 GiB.     */
+                                     so no workgroup owns more than 1 GiB.
+                                     fo_qsa_attention: auto is 8 waves per
+                                     CU; with `arrived` it runs at least 8
+                                     workgroups (one per claim group).
+                                     fo_a2a_gemm runs at least one workgroup
+                                     on every XCD whose tile rectangle is not
+                                     empty (up to 8).                          */
   int32_t         reserved;
 } fo_schedule;
 

@@ -605,6 +605,9 @@ fo_status fo_a2a_gemm(const void *const *pieces, const void *w, void *y, fo_dtyp
     const int use = a.gtiles[g] < wgs_g ? a.gtiles[g] : wgs_g;
     // workgroup b sits on XCD b % 8: the grid must reach rank use - 1 on XCD g
     if (use > 0 && (use - 1) * XCDS + g + 1 > grid) grid = (use - 1) * XCDS + g + 1;
+    // a workgroup computes only its own XCD's rectangle: every rectangle
+    // with tiles needs a workgroup, whatever the cap
+    if (a.gtiles[g] > 0 && grid < g + 1) grid = g + 1;
   }
   a.grid = grid < 1 ? 1 : grid;
   a.arrived = s->arrived;
@@ -738,6 +741,11 @@ fo_status fo_qsa_attention(const void *qkv, void *o, fo_dtype o_dtype, int64_t s
   const int cap = (s->max_workgroups > 0 && s->max_workgroups < full) ? s->max_workgroups : full;
   a.grid = (int32_t)(blocks < cap ? blocks : cap);
   if (a.grid < 1) a.grid = 1;
+  // With arrival flags every claim group needs a workgroup of its own: a
+  // group's workgroups claim its conversion units before any block, and a
+  // block may wait for the conversions dealt to any group.  (Workgroups
+  // with nothing left to claim leave at once.)
+  if (s->arrived != nullptr && a.grid < XCDS) a.grid = XCDS < full ? XCDS : full;
   a.arrived = s->arrived;
   a.epoch = s->epoch;
   a.timeout_ticks = ns_to_ticks(s->timeout_ns ? s->timeout_ns : kDefaultTimeoutNs, I->wall_hz);

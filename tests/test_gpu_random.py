@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import workloads as wl
-from helpers import check_exact, dev_bf16, host, log
+from helpers import bf16_bits_to_f64, check_exact, check_tolerance, dev_bf16, host, log
 
 pytestmark = pytest.mark.gpu
 
@@ -93,3 +93,92 @@ def test_random_ag_gemm_and_gemm_rs_int_exact(fo, orc, seed, monkeypatch):
     assert int(status.item()) == 0
     assert (host(done) == e).all()
     check_exact(host(part), ref, f"seed {seed} gemm_rs")
+
+
+def draw_a2a(seed: int) -> dict:
+    g = np.random.Generator(np.random.PCG64(41000 + seed))
+    P = int(g.choice([1, 2, 3, 4, 8]))
+    return {
+        "P": P, "m": int(g.integers(8, 1200)), "n": int(g.integers(8, 900)),
+        "kp": int(g.choice([8, 64, 120, 256, 520])),
+        "local": int(g.integers(0, P)),
+        "order": [int(v) for v in g.permutation(P)],
+        "flags": bool(g.integers(0, 2)),
+        "grid": int(g.choice([0, 0, 1, 9, 64])),
+        "bf16": bool(g.integers(0, 3) == 0),
+    }
+
+
+@pytest.mark.parametrize("seed", list(range(24)))
+def test_random_a2a_gemm_int_exact(fo, orc, seed):
+    """Flash All-to-All GEMM: random piece count and width, m, n, local
+    rank, piece order, preset flags, workgroup cap and output type; every
+    element bit-exact on integer inputs."""
+    c = draw_a2a(seed)
+    log(f"case: a2a seed {seed} {c}")
+    P, m, n, kp = c["P"], c["m"], c["n"], c["kp"]
+    x = wl.bf16_operand((m, kp * P), "int", 1.0, 42000 + 2 * seed)
+    wb = wl.bf16_operand((n, kp * P), "int", 1.0, 42001 + 2 * seed)
+    pieces_b = [np.ascontiguousarray(x[:, q * kp:(q + 1) * kp]) for q in range(P)]
+    ref = orc.a2a_gemm(pieces_b, wb)
+    _Epoch.e += 1
+    e = _Epoch.e
+    flags = torch.full((P,), e, dtype=torch.int32, device="cuda") if c["flags"] else None
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dt = torch.bfloat16 if c["bf16"] else torch.float32
+    y = torch.full((m, n), float("nan"), dtype=dt, device="cuda")
+    ws = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    fo.fo_a2a_gemm([dev_bf16(p) for p in pieces_b], dev_bf16(wb), y,
+                   fo.Schedule(nchunks=P, local=c["local"], order=c["order"], epoch=e, arrived=flags,
+                               max_workgroups=c["grid"], status=status, timeout_ns=2_000_000_000), ws)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    if c["bf16"]:
+        assert np.array_equal(host(y), orc.f64_to_bf16(ref)), f"seed {seed} bf16"
+    else:
+        check_exact(host(y), ref, f"seed {seed} a2a")
+
+
+def draw_qsa(seed: int) -> dict:
+    g = np.random.Generator(np.random.PCG64(43000 + seed))
+    R = int(g.choice([1, 2, 3, 4, 6]))
+    return {
+        "R": R, "S": R * 128 * int(g.integers(1, 5 if R <= 3 else 3)), "H": int(g.integers(1, 4)),
+        "causal": bool(g.integers(0, 2)),
+        "order": [int(v) for v in g.permutation(R)],
+        "flags": bool(g.integers(0, 2)),
+        "grid": int(g.choice([0, 0, 1, 13, 100])),
+        "bf16": bool(g.integers(0, 3) == 0),
+    }
+
+
+@pytest.mark.parametrize("seed", list(range(16)))
+def test_random_qsa_within_bar(fo, orc, seed):
+    """Query-split attention: random sequence length, chunk count, heads,
+    mask, stage order, preset flags, workgroup cap and output type; within
+    the bar of the fp64 oracle, and the counters back to zero."""
+    from oracle import attention
+    c = draw_qsa(seed)
+    log(f"case: qsa seed {seed} {c}")
+    S, H, R, D = c["S"], c["H"], c["R"], 128
+    qkv = wl.bf16_operand((S, 3 * H * D), "gauss", 1.0, 44000 + seed)
+    ref = attention.attention(qkv, H, D, c["causal"])
+    _Epoch.e += 1
+    e = _Epoch.e
+    flags = torch.full((R,), e, dtype=torch.int32, device="cuda") if c["flags"] else None
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dt = torch.bfloat16 if c["bf16"] else torch.float32
+    o = torch.full((S, H * D), float("nan"), dtype=dt, device="cuda")
+    ws = torch.zeros(fo.fo_qsa_workspace_bytes(S, H, D, R), dtype=torch.uint8, device="cuda")
+    fo.fo_qsa_attention(dev_bf16(qkv), o, H, D, c["causal"],
+                        fo.Schedule(nchunks=R, order=c["order"], epoch=e, arrived=flags,
+                                    max_workgroups=c["grid"], status=status, timeout_ns=2_000_000_000), ws)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    if c["bf16"]:
+        check_tolerance(bf16_bits_to_f64(host(o)), ref, frob_ref=bf16_bits_to_f64(orc.f64_to_bf16(ref)),
+                        what=f"seed {seed} bf16")
+    else:
+        check_tolerance(host(o), ref, what=f"seed {seed}")
+    counters = (1024 + H * (S // 128) + R * H) * 4
+    assert int(ws[:counters].sum()) == 0, "counters not returned to zero"
