@@ -56,7 +56,8 @@ enum {
   FO_ERR_NULL = 1,       /* a required pointer is NULL                        */
   FO_ERR_SHAPE = 2,      /* non-positive size, m % R != 0, R out of range,
                             k > 2^21 (GEMM calls)                             */
-  FO_ERR_ALIGN = 3,      /* pointer not 16-byte aligned, or k % 8 != 0        */
+  FO_ERR_ALIGN = 3,      /* pointer not 16-byte aligned, k % 8 != 0, or n % 4
+                            != 0 where fp32 rows are moved as 16-byte pieces */
   FO_ERR_DTYPE = 4,      /* unknown dtype, or a dtype the call cannot store   */
   FO_ERR_ORDER = 5,      /* order is not a permutation of 0..R-1              */
   FO_ERR_SCHEDULE = 6,   /* local out of range, epoch == 0, bad mode/split    */

@@ -182,3 +182,113 @@ def test_random_qsa_within_bar(fo, orc, seed):
         check_tolerance(host(o), ref, what=f"seed {seed}")
     counters = (1024 + H * (S // 128) + R * H) * 4
     assert int(ws[:counters].sum()) == 0, "counters not returned to zero"
+
+
+def draw_reduce(seed: int) -> dict:
+    g = np.random.Generator(np.random.PCG64(45000 + seed))
+    R = int(g.choice([1, 2, 3, 5, 8, 13, 16]))
+    return {
+        "R": R, "n": 4 * int(g.integers(1, 75000)), "local": int(g.integers(0, R)),   # n % 4 == 0 (16-byte rows)
+        "order": [int(v) for v in g.permutation(R)],
+        "flags": bool(g.integers(0, 2)),
+        "grid": int(g.choice([0, 0, 1, 5, 77])),
+        "out": str(g.choice(["f32", "bf16", "inplace"])),
+    }
+
+
+@pytest.mark.parametrize("seed", list(range(24)))
+def test_random_chunk_reduce_int_exact(fo, orc, seed):
+    """Chunk reduce-add: random source count, length (ragged), local source,
+    order, preset flags, workgroup cap and output (fp32, bf16, in place);
+    integer sources, every element exact."""
+    c = draw_reduce(seed)
+    log(f"case: reduce seed {seed} {c}")
+    R, n, local = c["R"], c["n"], c["local"]
+    srcs = [wl.f32_operand((n,), "int", 1.0, 46000 + 64 * seed + q) for q in range(R)]
+    ref = orc.reduce(srcs)
+    d = [torch.from_numpy(a).cuda() for a in srcs]
+    _Epoch.e += 1
+    e = _Epoch.e
+    flags = torch.full((R,), e, dtype=torch.int32, device="cuda") if c["flags"] else None
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    if c["out"] == "inplace":
+        dst = d[local]
+    else:
+        dst = torch.full((n,), float("nan"), dtype=torch.bfloat16 if c["out"] == "bf16" else torch.float32,
+                         device="cuda")
+    fo.fo_chunk_reduce(dst, d, fo.Schedule(nchunks=R, local=local, order=c["order"], epoch=e, arrived=flags,
+                                           max_workgroups=c["grid"], status=status, timeout_ns=2_000_000_000))
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    if c["out"] == "bf16":
+        assert np.array_equal(host(dst), orc.f64_to_bf16(ref)), f"seed {seed} bf16"
+    else:
+        check_exact(host(dst), ref, f"seed {seed} reduce")
+
+
+def draw_fused(seed: int) -> dict:
+    g = np.random.Generator(np.random.PCG64(47000 + seed))
+    R = int(g.choice([1, 2, 3, 4, 5, 8]))
+    return {
+        "R": R, "mc": int(g.integers(1, 80)) * 8, "n": 4 * int(g.integers(2, 225)),   # n % 4 == 0
+        "k": int(g.choice([8, 64, 200, 1024])), "local": int(g.integers(0, R)),
+        "flags": bool(g.integers(0, 2)), "grid": int(g.choice([0, 0, 3, 40])),
+        "bf16": bool(g.integers(0, 2)), "ring": bool(g.integers(0, 2)),
+    }
+
+
+@pytest.mark.parametrize("seed", list(range(24)))
+def test_random_fused_and_ring_rs_int_exact(fo, orc, seed):
+    """GEMM-RS with the reduce in the same launch, direct or ring form:
+    random shape, chunks, local rank, preset incoming flags, workgroup cap
+    and shard type; partials, shard (and the ring's forwarded sums) exact
+    on integer inputs, done flags all released."""
+    c = draw_fused(seed)
+    log(f"case: fused seed {seed} {c}")
+    R, mc, n, k, local = c["R"], c["mc"], c["n"], c["k"], c["local"]
+    m = R * mc
+    xb = wl.bf16_operand((m, k), "int", 1.0, 48000 + 2 * seed)
+    wb = wl.bf16_operand((n, k), "int", 1.0, 48001 + 2 * seed)
+    inc = [wl.f32_operand((mc, n), "int", 1.0, 48100 + 16 * seed + q) for q in range(R)]
+    prod = orc.gemm(xb, wb)
+    x, w = dev_bf16(xb), dev_bf16(wb)
+    part = torch.full((m, n), float("nan"), device="cuda")
+    sdt = torch.bfloat16 if c["bf16"] else torch.float32
+    shard = torch.full((mc, n), float("nan"), dtype=sdt, device="cuda")
+    done = torch.zeros(R, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(fo.fo_workspace_bytes(m, n, k, R), dtype=torch.uint8, device="cuda")
+    _Epoch.e += 1
+    e = _Epoch.e
+    flags = torch.full((R,), e, dtype=torch.int32, device="cuda") if c["flags"] else None
+    s = fo.Schedule(nchunks=R, local=local, epoch=e, arrived=flags, status=status, max_workgroups=c["grid"],
+                    timeout_ns=2_000_000_000)
+    if c["ring"]:
+        # ring form: every chunk but local - 1 receives an accumulated partial
+        start = (local - 1) % R
+        incoming = [None if (q == start and R > 1) else torch.from_numpy(inc[q]).cuda() for q in range(R)]
+        fo.fo_gemm_rs_ring(x, w, part, done, shard, incoming, s, ws)
+    else:
+        incoming = [None if q == local else torch.from_numpy(inc[q]).cuda() for q in range(R)]
+        fo.fo_gemm_rs_reduce(x, w, part, done, shard, incoming, s, ws)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert (host(done) == e).all()
+    loc = slice(local * mc, (local + 1) * mc)
+    if c["ring"]:
+        want = prod.copy()
+        for q in range(R):
+            if incoming[q] is not None and q != local:
+                want[q * mc:(q + 1) * mc] += inc[q]
+        if R > 1:
+            peers = np.r_[0:local * mc, (local + 1) * mc:m]
+            check_exact(host(part)[peers], want[peers], f"seed {seed} forwarded sums")
+        check_exact(host(part)[loc], prod[loc], f"seed {seed} local partial")
+        ref = prod[loc] + (inc[local] if incoming[local] is not None else 0.0)
+    else:
+        check_exact(host(part), prod, f"seed {seed} partials")
+        ref = orc.gemm_rs_shard(xb, wb, R, local, [None if q == local else inc[q] for q in range(R)])
+    if c["bf16"]:
+        assert np.array_equal(host(shard), orc.f64_to_bf16(ref)), f"seed {seed} bf16 shard"
+    else:
+        check_exact(host(shard), ref, f"seed {seed} shard")
