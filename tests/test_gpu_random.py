@@ -292,3 +292,132 @@ def test_random_fused_and_ring_rs_int_exact(fo, orc, seed):
         assert np.array_equal(host(shard), orc.f64_to_bf16(ref)), f"seed {seed} bf16 shard"
     else:
         check_exact(host(shard), ref, f"seed {seed} shard")
+
+
+def draw_emulated(seed: int) -> dict:
+    g = np.random.Generator(np.random.PCG64(49000 + seed))
+    R = int(g.choice([2, 3, 4, 6, 8, 12]))
+    local = int(g.integers(0, R))
+    peers = [q for q in range(R) if q != local]
+    return {
+        "R": R, "mc": int(g.integers(1, 64)) * 8, "n": int(g.integers(8, 700)),
+        "k": int(g.choice([64, 512, 1024, 2048])), "local": local,
+        "arrival": [int(v) for v in g.permutation(peers)],
+        "gap_ns": int(g.choice([0, 3000, 20000, 60000])),
+        "strict": bool(g.integers(0, 4) == 0),
+        "split": [int(v) for v in g.choice([1, 1, 2, 4, 8], size=R)] if g.integers(0, 3) == 0 else None,
+        "grid": int(g.choice([0, 0, 0, 16, 64])),
+        "tile": TILES[int(g.integers(0, len(TILES)))],
+    }
+
+
+@pytest.mark.parametrize("seed", list(range(24)))
+def test_random_ag_gemm_emulated_arrivals_int_exact(fo, orc, seed, monkeypatch):
+    """AG-GEMM with the peers' chunks copied by the copy engine into
+    NaN-poisoned rows and released at modelled times, in a random landing
+    order: random shape, chunks, local rank, gap between landings, STRICT or
+    ready-first, splits (explicit or the automatic split of the last peer),
+    workgroup cap and tile layout; every element exact."""
+    from test_gpu_emulated import side_stream
+    c = draw_emulated(seed)
+    log(f"case: emulated seed {seed} {c}")
+    if c["tile"] is None:
+        monkeypatch.delenv("FO_TILE", raising=False)
+    else:
+        monkeypatch.setenv("FO_TILE", c["tile"])
+    R, mc, n, k, local = c["R"], c["mc"], c["n"], c["k"], c["local"]
+    m = R * mc
+    xb = wl.bf16_operand((m, k), "int", 1.0, 50000 + 2 * seed)
+    wb = wl.bf16_operand((n, k), "int", 1.0, 50001 + 2 * seed)
+    ref = orc.gemm(xb, wb)
+    staging = dev_bf16(xb)
+    w = dev_bf16(wb)
+    x = staging.clone()
+    for q in c["arrival"]:
+        x[q * mc:(q + 1) * mc].fill_(float("nan"))
+    flags = torch.zeros(R, dtype=torch.int32, device="cuda")
+    es = torch.zeros(R + 2, dtype=torch.int64, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(4 * fo.fo_workspace_bytes(m, n, k, R), dtype=torch.uint8, device="cuda")
+    y = torch.full((m, n), float("nan"), device="cuda")
+    _Epoch.e += 1
+    e = _Epoch.e
+    side = side_stream()
+    torch.cuda.synchronize()
+    rel = [c["gap_ns"] * (i + 1) for i in range(len(c["arrival"]))]
+    with torch.cuda.stream(side):
+        fo.fo_emulate_arrivals([x[q * mc:(q + 1) * mc] for q in c["arrival"]],
+                               [staging[q * mc:(q + 1) * mc] for q in c["arrival"]],
+                               rel, c["arrival"], flags, e, es, stream=side)
+    fo.fo_ag_gemm(x, w, y, fo.Schedule(nchunks=R, local=local, arrived=flags, epoch=e, status=status,
+                                       mode=fo.FO_SCHED_STRICT if c["strict"] else fo.FO_SCHED_READY_FIRST,
+                                       split=c["split"], max_workgroups=c["grid"], timeout_ns=5_000_000_000), ws)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "flag wait timed out"
+    check_exact(host(y), ref, f"seed {seed} emulated")
+
+
+def draw_qsa_emulated(seed: int) -> dict:
+    g = np.random.Generator(np.random.PCG64(51000 + seed))
+    R = int(g.choice([2, 3, 4, 6]))
+    local = int(g.integers(0, R))
+    peers = [q for q in range(R) if q != local]
+    return {
+        "R": R, "S": R * 128 * int(g.integers(1, 4 if R <= 3 else 3)), "H": int(g.integers(1, 4)),
+        "causal": bool(g.integers(0, 2)), "local": local,
+        "arrival": [int(v) for v in g.permutation(peers)],
+        "order": [int(v) for v in g.permutation(R)] if g.integers(0, 2) else None,
+        "gap_ns": int(g.choice([0, 5000, 30000])),
+        "grid": int(g.choice([0, 0, 16, 64])),
+    }
+
+
+@pytest.mark.parametrize("seed", list(range(16)))
+def test_random_qsa_emulated_arrivals_same_bits(fo, orc, seed):
+    """Query-split attention with the peers' QKV rows copied into NaN-poisoned
+    rows and released in a random order: random length, chunks, heads, mask,
+    stage order, gap and workgroup cap.  The output equals, bit for bit, the
+    run with every flag preset, and is within the bar of the oracle."""
+    from oracle import attention
+    from test_gpu_emulated import side_stream
+    c = draw_qsa_emulated(seed)
+    log(f"case: qsa emulated seed {seed} {c}")
+    S, H, R, D, local = c["S"], c["H"], c["R"], 128, c["local"]
+    cs = S // R
+    qkv_b = wl.bf16_operand((S, 3 * H * D), "gauss", 1.0, 52000 + seed)
+    ref = attention.attention(qkv_b, H, D, c["causal"])
+    staging = dev_bf16(qkv_b)
+    ws = torch.zeros(fo.fo_qsa_workspace_bytes(S, H, D, R), dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def sched(flags, e):
+        return fo.Schedule(nchunks=R, local=local, order=c["order"], arrived=flags, epoch=e, status=status,
+                           max_workgroups=c["grid"], timeout_ns=5_000_000_000)
+
+    _Epoch.e += 1
+    base = torch.full((S, H * D), float("nan"), device="cuda")
+    fo.fo_qsa_attention(staging, base, H, D, c["causal"],
+                        sched(torch.full((R,), _Epoch.e, dtype=torch.int32, device="cuda"), _Epoch.e), ws)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    qkv = staging.clone()
+    for q in c["arrival"]:
+        qkv[q * cs:(q + 1) * cs].fill_(float("nan"))
+    flags = torch.zeros(R, dtype=torch.int32, device="cuda")
+    es = torch.zeros(R + 2, dtype=torch.int64, device="cuda")
+    o = torch.full((S, H * D), float("nan"), device="cuda")
+    _Epoch.e += 1
+    e = _Epoch.e
+    side = side_stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        fo.fo_emulate_arrivals([qkv[q * cs:(q + 1) * cs] for q in c["arrival"]],
+                               [staging[q * cs:(q + 1) * cs] for q in c["arrival"]],
+                               [c["gap_ns"] * (i + 1) for i in range(R - 1)], c["arrival"], flags, e, es,
+                               stream=side)
+    fo.fo_qsa_attention(qkv, o, H, D, c["causal"], sched(flags, e), ws)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "flag wait timed out"
+    got = host(o)
+    assert np.array_equal(got.view(np.uint32), host(base).view(np.uint32)), f"seed {seed}: landings changed the bits"
+    check_tolerance(got, ref, what=f"seed {seed} emulated")
