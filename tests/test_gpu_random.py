@@ -421,3 +421,58 @@ def test_random_qsa_emulated_arrivals_same_bits(fo, orc, seed):
     got = host(o)
     assert np.array_equal(got.view(np.uint32), host(base).view(np.uint32)), f"seed {seed}: landings changed the bits"
     check_tolerance(got, ref, what=f"seed {seed} emulated")
+
+
+@pytest.mark.parametrize("seed", list(range(8)))
+def test_random_ag_gemm_bits_independent_of_landings(fo, orc, seed, monkeypatch):
+    """Gaussian inputs, a fixed split vector: the output bits do not depend
+    on when or in which order the chunks land (two emulated landing orders
+    and gaps, and every flag preset, give the same bits), and are within the
+    bar of the oracle."""
+    from test_gpu_emulated import side_stream
+    monkeypatch.delenv("FO_TILE", raising=False)
+    g = np.random.Generator(np.random.PCG64(53000 + seed))
+    R = int(g.choice([3, 4, 8]))
+    local = int(g.integers(0, R))
+    mc, n, k = int(g.integers(4, 40)) * 16, int(g.integers(64, 900)), int(g.choice([512, 1024, 2048]))
+    m = R * mc
+    split = [int(v) for v in g.choice([1, 2, 4, 8], size=R)]
+    log(f"case: determinism seed {seed} R={R} local={local} {m}x{n}x{k} split {split}")
+    xb = wl.bf16_operand((m, k), "gauss", 1.0, 54000 + 2 * seed)
+    wb = wl.bf16_operand((n, k), "gauss", 0.02, 54001 + 2 * seed)
+    staging = dev_bf16(xb)
+    w = dev_bf16(wb)
+    ws = torch.zeros(4 * fo.fo_workspace_bytes(m, n, k, R), dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    peers = [q for q in range(R) if q != local]
+    outs = []
+    for run in range(3):
+        x = staging.clone()
+        y = torch.full((m, n), float("nan"), device="cuda")
+        _Epoch.e += 1
+        e = _Epoch.e
+        if run == 0:
+            flags = torch.full((R,), e, dtype=torch.int32, device="cuda")
+        else:
+            arrival = [int(v) for v in g.permutation(peers)]
+            for q in arrival:
+                x[q * mc:(q + 1) * mc].fill_(float("nan"))
+            flags = torch.zeros(R, dtype=torch.int32, device="cuda")
+            es = torch.zeros(R + 2, dtype=torch.int64, device="cuda")
+            side = side_stream()
+            torch.cuda.synchronize()
+            gap = int(g.choice([0, 4000, 25000]))
+            with torch.cuda.stream(side):
+                fo.fo_emulate_arrivals([x[q * mc:(q + 1) * mc] for q in arrival],
+                                       [staging[q * mc:(q + 1) * mc] for q in arrival],
+                                       [gap * (i + 1) for i in range(len(arrival))], arrival, flags, e, es,
+                                       stream=side)
+        fo.fo_ag_gemm(x, w, y, fo.Schedule(nchunks=R, local=local, arrived=flags, epoch=e, status=status,
+                                           split=split, timeout_ns=5_000_000_000), ws)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, "flag wait timed out"
+        outs.append(host(y))
+    for i in (1, 2):
+        assert np.array_equal(outs[i].view(np.uint32), outs[0].view(np.uint32)), f"seed {seed} run {i}"
+    rows = np.arange(0, m, 7)
+    check_tolerance(outs[0][rows], orc.gemm(xb[rows], wb), what=f"seed {seed}")
