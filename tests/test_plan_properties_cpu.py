@@ -1,8 +1,9 @@
 """Property tests of the host-only schedule model over random valid inputs
 (hypothesis): whatever the shape, chunk count, local rank and landing
-times, the plans are valid schedules, the predictions are consistent with
-the landings, and later landings never predict an earlier completion
-(beyond the modelled cost of claims that fall on one instant)."""
+times, the plans are valid schedules and the predictions are consistent
+with the landings.  (Later landings do not always predict a later
+completion: the model replays greedy ready-first claims, and a greedy list
+schedule can finish earlier when a job is released later.)"""
 import pytest
 
 hyp = pytest.importorskip("hypothesis")
@@ -40,22 +41,6 @@ def test_ag_schedule_is_valid_and_consistent(p):
     assert all(v > max(arr) for v in pred if v > 0)            # nothing completes before the last landing
     chosen = pred[SPLITS.index(split[last])]
     assert chosen > 0 and chosen <= min(v for v in pred if v > 0) + 500   # the earliest, up to the 0.5 us margin
-
-
-@settings(max_examples=200, deadline=None)
-@given(problems(), st.integers(1, 2_000_000))
-def test_later_landings_never_predict_earlier(p, delay):
-    m, n, k, R, local, arr, grid = p
-    if R == 1:
-        return
-    _, _, p0 = fo.fo_plan_ag_schedule(m, n, k, R, local, arr, num_workgroups=grid)
-    later = [t if q == local else t + delay for q, t in enumerate(arr)]
-    _, _, p1 = fo.fo_plan_ag_schedule(m, n, k, R, local, later, num_workgroups=grid)
-    # (claims that fall on one instant queue, 10 ns per workgroup in the
-    # model, so landings that no longer coincide may save up to that much)
-    for a, b in zip(p0, p1):
-        if a > 0 and b > 0:
-            assert b >= a - 10 * grid
 
 
 @settings(max_examples=150, deadline=None)
