@@ -2,6 +2,8 @@
 counts, local rank, priority order, STRICT or ready-first, preset flags,
 per-chunk splits, workgroup caps, forced tile layouts and output types drawn
 together, on integer inputs, every element bit-exact against the fp64 oracle."""
+import os
+
 import numpy as np
 import pytest
 
@@ -13,7 +15,14 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 TILES = [None, "256x256", "256x160x3", "128x224", "128x128"]
-SEEDS = list(range(48))
+# FO_RANDOM_SCALE multiplies the number of cases of every random test
+# (default 1: a few seconds in all)
+SCALE = int(os.environ.get("FO_RANDOM_SCALE", "1"))
+SEEDS = list(range(48 * SCALE))
+
+
+def seeds(n):
+    return list(range(n * SCALE))
 
 
 @pytest.fixture(scope="module")
@@ -27,6 +36,13 @@ def fo():
 
 class _Epoch:
     e = 5000
+
+
+def ws_bytes(fo, m, n, k, R, split):
+    """fo_workspace_bytes covers the automatic split (one chunk split up to 8
+    ways); an explicit vector needs partial slots for every split chunk."""
+    extra = 0 if split is None else sum(s_ for s_ in split if s_ > 1) // 8
+    return (2 + extra) * fo.fo_workspace_bytes(m, n, k, R)
 
 
 def draw(seed: int) -> dict:
@@ -62,7 +78,7 @@ def test_random_ag_gemm_and_gemm_rs_int_exact(fo, orc, seed, monkeypatch):
     wb = wl.bf16_operand((n, k), "int", 1.0, 17001 + 2 * seed)
     x, w = dev_bf16(xb), dev_bf16(wb)
     ref = orc.gemm(xb, wb)
-    ws = torch.zeros(4 * fo.fo_workspace_bytes(m, n, k, R), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(ws_bytes(fo, m, n, k, R, c["split"]), dtype=torch.uint8, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
 
     _Epoch.e += 1
@@ -109,7 +125,7 @@ def draw_a2a(seed: int) -> dict:
     }
 
 
-@pytest.mark.parametrize("seed", list(range(24)))
+@pytest.mark.parametrize("seed", seeds(24))
 def test_random_a2a_gemm_int_exact(fo, orc, seed):
     """Flash All-to-All GEMM: random piece count and width, m, n, local
     rank, piece order, preset flags, workgroup cap and output type; every
@@ -152,7 +168,7 @@ def draw_qsa(seed: int) -> dict:
     }
 
 
-@pytest.mark.parametrize("seed", list(range(16)))
+@pytest.mark.parametrize("seed", seeds(16))
 def test_random_qsa_within_bar(fo, orc, seed):
     """Query-split attention: random sequence length, chunk count, heads,
     mask, stage order, preset flags, workgroup cap and output type; within
@@ -196,7 +212,7 @@ def draw_reduce(seed: int) -> dict:
     }
 
 
-@pytest.mark.parametrize("seed", list(range(24)))
+@pytest.mark.parametrize("seed", seeds(24))
 def test_random_chunk_reduce_int_exact(fo, orc, seed):
     """Chunk reduce-add: random source count, length (ragged), local source,
     order, preset flags, workgroup cap and output (fp32, bf16, in place);
@@ -237,7 +253,7 @@ def draw_fused(seed: int) -> dict:
     }
 
 
-@pytest.mark.parametrize("seed", list(range(24)))
+@pytest.mark.parametrize("seed", seeds(24))
 def test_random_fused_and_ring_rs_int_exact(fo, orc, seed):
     """GEMM-RS with the reduce in the same launch, direct or ring form:
     random shape, chunks, local rank, preset incoming flags, workgroup cap
@@ -311,7 +327,7 @@ def draw_emulated(seed: int) -> dict:
     }
 
 
-@pytest.mark.parametrize("seed", list(range(24)))
+@pytest.mark.parametrize("seed", seeds(24))
 def test_random_ag_gemm_emulated_arrivals_int_exact(fo, orc, seed, monkeypatch):
     """AG-GEMM with the peers' chunks copied by the copy engine into
     NaN-poisoned rows and released at modelled times, in a random landing
@@ -338,7 +354,7 @@ def test_random_ag_gemm_emulated_arrivals_int_exact(fo, orc, seed, monkeypatch):
     flags = torch.zeros(R, dtype=torch.int32, device="cuda")
     es = torch.zeros(R + 2, dtype=torch.int64, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    ws = torch.zeros(4 * fo.fo_workspace_bytes(m, n, k, R), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(ws_bytes(fo, m, n, k, R, c["split"]), dtype=torch.uint8, device="cuda")
     y = torch.full((m, n), float("nan"), device="cuda")
     _Epoch.e += 1
     e = _Epoch.e
@@ -372,7 +388,7 @@ def draw_qsa_emulated(seed: int) -> dict:
     }
 
 
-@pytest.mark.parametrize("seed", list(range(16)))
+@pytest.mark.parametrize("seed", seeds(16))
 def test_random_qsa_emulated_arrivals_same_bits(fo, orc, seed):
     """Query-split attention with the peers' QKV rows copied into NaN-poisoned
     rows and released in a random order: random length, chunks, heads, mask,
@@ -423,7 +439,7 @@ def test_random_qsa_emulated_arrivals_same_bits(fo, orc, seed):
     check_tolerance(got, ref, what=f"seed {seed} emulated")
 
 
-@pytest.mark.parametrize("seed", list(range(8)))
+@pytest.mark.parametrize("seed", seeds(8))
 def test_random_ag_gemm_bits_independent_of_landings(fo, orc, seed, monkeypatch):
     """Gaussian inputs, a fixed split vector: the output bits do not depend
     on when or in which order the chunks land (two emulated landing orders
@@ -442,7 +458,7 @@ def test_random_ag_gemm_bits_independent_of_landings(fo, orc, seed, monkeypatch)
     wb = wl.bf16_operand((n, k), "gauss", 0.02, 54001 + 2 * seed)
     staging = dev_bf16(xb)
     w = dev_bf16(wb)
-    ws = torch.zeros(4 * fo.fo_workspace_bytes(m, n, k, R), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(ws_bytes(fo, m, n, k, R, split), dtype=torch.uint8, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     peers = [q for q in range(R) if q != local]
     outs = []
