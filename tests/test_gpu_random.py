@@ -492,3 +492,79 @@ def test_random_ag_gemm_bits_independent_of_landings(fo, orc, seed, monkeypatch)
         assert np.array_equal(outs[i].view(np.uint32), outs[0].view(np.uint32)), f"seed {seed} run {i}"
     rows = np.arange(0, m, 7)
     check_tolerance(outs[0][rows], orc.gemm(xb[rows], wb), what=f"seed {seed}")
+
+
+def draw_fused_emulated(seed: int) -> dict:
+    g = np.random.Generator(np.random.PCG64(55000 + seed))
+    R = int(g.choice([2, 3, 4, 8]))
+    local = int(g.integers(0, R))
+    return {
+        "R": R, "mc": int(g.integers(1, 48)) * 8, "n": 4 * int(g.integers(2, 200)),
+        "k": int(g.choice([64, 512, 1024])), "local": local,
+        "gap_ns": int(g.choice([0, 5000, 30000])), "grid": int(g.choice([0, 0, 40])),
+        "ring": bool(g.integers(0, 2)), "perm_seed": int(g.integers(0, 1 << 30)),
+    }
+
+
+@pytest.mark.parametrize("seed", seeds(16))
+def test_random_fused_and_ring_rs_emulated_incoming_int_exact(fo, orc, seed):
+    """GEMM-RS with the reduce in the same launch (direct or ring form), the
+    incoming partials copied by the copy engine into NaN-poisoned inboxes in
+    a random order at a random gap: the shard (and the ring's forwarded sums)
+    exact on integer inputs, the same bits as with every partial present."""
+    from test_gpu_emulated import side_stream
+    c = draw_fused_emulated(seed)
+    log(f"case: fused emulated seed {seed} {c}")
+    R, mc, n, k, local = c["R"], c["mc"], c["n"], c["k"], c["local"]
+    m = R * mc
+    xb = wl.bf16_operand((m, k), "int", 1.0, 56000 + 2 * seed)
+    wb = wl.bf16_operand((n, k), "int", 1.0, 56001 + 2 * seed)
+    inc = [wl.f32_operand((mc, n), "int", 1.0, 56100 + 16 * seed + q) for q in range(R)]
+    x, w = dev_bf16(xb), dev_bf16(wb)
+    if c["ring"]:
+        start = (local - 1) % R
+        has = [not (q == start and R > 1) for q in range(R)]
+    else:
+        has = [q != local for q in range(R)]
+    staging = [torch.from_numpy(inc[q]).cuda() if has[q] else None for q in range(R)]
+    senders = [q for q in range(R) if has[q]]
+    arrival = [senders[i] for i in np.random.Generator(np.random.PCG64(c["perm_seed"])).permutation(len(senders))]
+    ws = torch.zeros(fo.fo_workspace_bytes(m, n, k, R), dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    outs = []
+    for emulated in (False, True):
+        inbox = [None if a is None else (torch.full_like(a, float("nan")) if emulated else a.clone()) for a in staging]
+        part = torch.full((m, n), float("nan"), device="cuda")
+        shard = torch.full((mc, n), float("nan"), device="cuda")
+        done = torch.zeros(R, dtype=torch.int32, device="cuda")
+        _Epoch.e += 1
+        e = _Epoch.e
+        flags = torch.zeros(R, dtype=torch.int32, device="cuda") if emulated else \
+            torch.full((R,), e, dtype=torch.int32, device="cuda")
+        if emulated:
+            es = torch.zeros(R + 2, dtype=torch.int64, device="cuda")
+            side = side_stream()
+            torch.cuda.synchronize()
+            with torch.cuda.stream(side):
+                fo.fo_emulate_arrivals([inbox[q] for q in arrival], [staging[q] for q in arrival],
+                                       [c["gap_ns"] * (i + 1) for i in range(len(arrival))], arrival, flags, e, es,
+                                       stream=side)
+        s = fo.Schedule(nchunks=R, local=local, epoch=e, arrived=flags, status=status, max_workgroups=c["grid"],
+                        timeout_ns=5_000_000_000)
+        if c["ring"]:
+            fo.fo_gemm_rs_ring(x, w, part, done, shard, inbox, s, ws)
+        else:
+            fo.fo_gemm_rs_reduce(x, w, part, done, shard, inbox, s, ws)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, "flag wait timed out"
+        assert (host(done) == e).all()
+        outs.append((host(part), host(shard)))
+    assert np.array_equal(outs[0][0].view(np.uint32), outs[1][0].view(np.uint32)), f"seed {seed} partials"
+    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32)), f"seed {seed} shard"
+    prod = orc.gemm(xb, wb)
+    loc = slice(local * mc, (local + 1) * mc)
+    if c["ring"]:
+        ref = prod[loc] + (inc[local] if has[local] else 0.0)
+    else:
+        ref = orc.gemm_rs_shard(xb, wb, R, local, [None if q == local else inc[q] for q in range(R)])
+    check_exact(outs[1][1], ref, f"seed {seed} shard")
