@@ -568,3 +568,60 @@ def test_random_fused_and_ring_rs_emulated_incoming_int_exact(fo, orc, seed):
     else:
         ref = orc.gemm_rs_shard(xb, wb, R, local, [None if q == local else inc[q] for q in range(R)])
     check_exact(outs[1][1], ref, f"seed {seed} shard")
+
+
+@pytest.mark.parametrize("seed", seeds(16))
+def test_random_a2a_and_reduce_emulated_int_exact(fo, orc, seed):
+    """All-to-all GEMM pieces and reduce sources copied into NaN-poisoned
+    buffers by the copy engine in a random order at a random gap: every
+    element exact on integer inputs."""
+    from test_gpu_emulated import side_stream
+    g = np.random.Generator(np.random.PCG64(57000 + seed))
+    P = int(g.choice([2, 3, 4, 8]))
+    local = int(g.integers(0, P))
+    m, n, kp = int(g.integers(8, 900)), int(g.integers(8, 700)), int(g.choice([8, 64, 200, 520]))
+    gap = int(g.choice([0, 4000, 30000]))
+    peers = [q for q in range(P) if q != local]
+    arrival = [int(v) for v in g.permutation(peers)]
+    log(f"case: a2a/reduce emulated seed {seed} P={P} local={local} m={m} n={n} kp={kp} gap={gap} {arrival}")
+    side = side_stream()
+    # all-to-all GEMM
+    x = wl.bf16_operand((m, kp * P), "int", 1.0, 58000 + 2 * seed)
+    wb = wl.bf16_operand((n, kp * P), "int", 1.0, 58001 + 2 * seed)
+    pieces_b = [np.ascontiguousarray(x[:, q * kp:(q + 1) * kp]) for q in range(P)]
+    staging = [dev_bf16(p_) for p_ in pieces_b]
+    inbox = [staging[q].clone() if q == local else torch.full_like(staging[q], float("nan")) for q in range(P)]
+    flags = torch.zeros(P, dtype=torch.int32, device="cuda")
+    es = torch.zeros(P + 2, dtype=torch.int64, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _Epoch.e += 1
+    e = _Epoch.e
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        fo.fo_emulate_arrivals([inbox[q] for q in arrival], [staging[q] for q in arrival],
+                               [gap * (i + 1) for i in range(len(arrival))], arrival, flags, e, es, stream=side)
+    y = torch.full((m, n), float("nan"), device="cuda")
+    fo.fo_a2a_gemm(inbox, dev_bf16(wb), y, fo.Schedule(nchunks=P, local=local, arrived=flags, epoch=e, status=status,
+                                                       timeout_ns=5_000_000_000),
+                   torch.zeros(4096, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "flag wait timed out"
+    check_exact(host(y), orc.a2a_gemm(pieces_b, wb), f"seed {seed} a2a")
+    # reduce-add of the same peers' sources into the local one
+    nn = 4 * int(g.integers(1, 40000))
+    srcs = [wl.f32_operand((nn,), "int", 1.0, 59000 + 16 * seed + q) for q in range(P)]
+    src_st = [torch.from_numpy(a).cuda() for a in srcs]
+    dsts = [src_st[q].clone() if q == local else torch.full_like(src_st[q], float("nan")) for q in range(P)]
+    flags.zero_()
+    _Epoch.e += 1
+    e = _Epoch.e
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        fo.fo_emulate_arrivals([dsts[q] for q in arrival], [src_st[q] for q in arrival],
+                               [gap * (i + 1) for i in range(len(arrival))], arrival, flags, e, es, stream=side)
+    out = torch.full((nn,), float("nan"), device="cuda")
+    fo.fo_chunk_reduce(out, dsts, fo.Schedule(nchunks=P, local=local, arrived=flags, epoch=e, status=status,
+                                              timeout_ns=5_000_000_000))
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "flag wait timed out"
+    check_exact(host(out), orc.reduce(srcs), f"seed {seed} reduce")
