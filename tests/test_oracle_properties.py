@@ -51,15 +51,19 @@ def test_gemm_integer_inputs_equal_int64(orc, m, n, k, seed):
 @settings(max_examples=60, deadline=None)
 @given(st.integers(1, 4), st.integers(1, 4), st.integers(1, 6), st.integers(0, 2 ** 31 - 1))
 def test_gemm_fractional_inputs_equal_fraction_sum(orc, m, n, k, seed):
-    """Arbitrary bf16 operands on tiny shapes: the oracle's fp64 result
-    equals the exact rational dot product rounded to double (k <= 6 bf16
-    products fit in a double without rounding)."""
+    """bf16 operands with random signs and mantissas and exponents within
+    2^-4 .. 2^4, on tiny shapes: every product (16 significant bits) and
+    every partial sum then fits a double exactly, so the oracle's fp64
+    result equals the exact rational dot product."""
     g = np.random.Generator(np.random.PCG64(seed))
-    xb = g.integers(0, 1 << 16, size=(m, k), dtype=np.uint16)
-    wb = g.integers(0, 1 << 16, size=(n, k), dtype=np.uint16)
-    # finite values only
-    xb[(xb & 0x7F80) == 0x7F80] = 0x3F80
-    wb[(wb & 0x7F80) == 0x7F80] = 0x3F80
+
+    def operand(shape):
+        sign = g.integers(0, 2, size=shape) << 15
+        expo = g.integers(127 - 4, 127 + 5, size=shape) << 7
+        mant = g.integers(0, 128, size=shape)
+        return (sign | expo | mant).astype(np.uint16)
+
+    xb, wb = operand((m, k)), operand((n, k))
     dec = lambda b: float(np.array([int(b) << 16], dtype=np.uint32).view(np.float32)[0])
     got = orc.gemm(xb, wb)
     for i in range(m):
